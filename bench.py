@@ -1,0 +1,219 @@
+"""Benchmark of the fused contraction + bias + activation on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one fused gemm_bias_act call over the resident inputs of the
+workload (default: M = N = K = 4096, bf16 operands, fp32 bias, ReLU, bf16
+output).  W untimed steps, then exactly K timed steps between two
+synchronisations; rank 0 prints one JSON line.
+
+Besides the headline, the line carries:
+  roofline      the dominant kernel's achieved TFLOP/s (algorithmic flops per
+                launch / mean launch time from HIP events on the launch stream)
+                against the dense bf16 MFMA peak;
+  cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
+                workload (a subset of output rows), on this host's cores;
+  others        the other workloads (fused and two-kernel), same protocol.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}   # dense MFMA, MI355X datasheet
+PEAK_HBM_GBS = 8000.0
+
+
+def _parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="gemm_relu_4096_bf16")
+    ap.add_argument("--no-others", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle sample time")
+    ap.add_argument("--tile", type=int, default=-1, help="force a tile config (tuning)")
+    return ap.parse_args()
+
+
+def to_device(words, dt):
+    import torch
+    if dt == "f32":
+        return torch.from_numpy(np.ascontiguousarray(words).view(np.float32)).cuda()
+    t = torch.from_numpy(np.ascontiguousarray(words).view(np.int16))
+    return t.view({"f16": torch.float16, "bf16": torch.bfloat16}[dt]).cuda()
+
+
+def make_step(case, seed=0, path="fused"):
+    """Returns (step_fn, n_kernel_launches) for one workload with resident inputs."""
+    import torch
+    import conv_bias_activation_amd as ba
+    import workloads as wl
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+    if isinstance(case, wl.GemmCase):
+        inp = wl.gen_gemm(case, seed)
+        A = to_device(inp["A"].reshape(case.M, case.K), case.in_dtype)
+        B = to_device(inp["B"].reshape(case.K, case.N), case.in_dtype)
+        bias = None if inp["bias"] is None else to_device(inp["bias"], case.bias_dtype)
+        C = torch.empty((case.M, case.N), dtype=tdt[case.out_dtype], device="cuda")
+        alpha = float(np.float32(case.alpha))
+        if path == "fused":
+            return (lambda: ba.gemm_bias_act(A, B, bias, C, case.act, alpha)), 1
+        ws = torch.empty(ba.gemm_bias_act_workspace_size(case.M, case.N) // 4, dtype=torch.float32,
+                         device="cuda")
+        return (lambda: ba.gemm_bias_act_2k(A, B, bias, C, case.act, alpha, workspace=ws)), 2
+    inp = wl.gen_conv(case, seed)
+    x = to_device(inp["x"].reshape(case.N, case.C, case.H, case.W), case.in_dtype)
+    w = to_device(inp["w"].reshape(case.Co, case.C, case.kh, case.kw), case.in_dtype)
+    bias = None if inp["bias"] is None else to_device(inp["bias"], case.bias_dtype)
+    Ho, Wo = case.out_hw()
+    y = torch.empty((case.N, case.Co, Ho, Wo), dtype=tdt[case.out_dtype], device="cuda")
+    args = (case.strides, case.pads, case.dilations, case.act)
+    if path == "fused":
+        return (lambda: ba.conv2d_bias_act(x, w, bias, y, *args)), 1
+    n = ba.conv2d_bias_act_workspace_size(case.N, case.C, case.H, case.W, case.Co, case.kh, case.kw,
+                                          case.strides, case.pads, case.dilations)
+    ws = torch.empty(n // 4, dtype=torch.float32, device="cuda")
+    return (lambda: ba.conv2d_bias_act_2k(x, w, bias, y, *args, workspace=ws)), 2
+
+
+def time_steps(step, steps, warmup):
+    """Mean ms per step over `steps` back-to-back steps, measured with HIP
+    events recorded on the stream the library launches on (torch's current
+    stream), between two device synchronisations."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(s)
+    for _ in range(steps):
+        step()
+    e1.record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def measure_case(case, path, min_ms=200.0):
+    step, nk = make_step(case, 0, path)
+    ms1, _ = time_steps(step, 5, 3)
+    reps = int(max(10, min(2000, min_ms / max(ms1, 1e-3))))
+    ms, _ = time_steps(step, reps, 5)
+    tf = case.flops / (ms * 1e-3) / 1e12
+    gbs = case.alg_bytes / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 5), "tflops": round(tf, 2),
+            "frac_mfma": round(tf / PEAK_TFLOPS[case.in_dtype], 4),
+            "alg_GBs": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "kernels": nk}
+
+
+def cpu_baseline(case, target_s):
+    """The oracle as it stands, on a subset of the workload's output rows."""
+    import oracle as orc
+    import workloads as wl
+    O = orc.Oracle()
+    if not isinstance(case, wl.GemmCase):
+        return None
+    inp = wl.gen_gemm(case, 0)
+    A = O.decode(inp["A"], case.in_dtype).reshape(case.M, case.K)
+    B = O.decode(inp["B"], case.in_dtype).reshape(case.K, case.N)
+    bias = O.decode(inp["bias"], case.bias_dtype) if inp["bias"] is not None else None
+    rows = max(1, O.num_threads())
+    t0 = time.perf_counter()
+    O.gemm(A[:rows], B, bias, case.act, orc.f32(case.alpha))
+    t1 = time.perf_counter() - t0
+    rows = int(min(case.M, max(rows, rows * target_s / max(t1, 1e-6))))
+    rows -= rows % max(1, O.num_threads()) if rows > O.num_threads() else 0
+    t0 = time.perf_counter()
+    O.gemm(A[:rows], B, bias, case.act, orc.f32(case.alpha))
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * case.N * case.K
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": O.num_threads(),
+            "kind": "oracle",
+            "sample": f"{rows} of {case.M} output rows of {case.name} (full K and N), fp64, "
+                      f"{dt:.1f} s wall; inputs decoded beforehand",
+            "host_cpus": os.cpu_count()}
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": f"--gpus {args.gpus}: this benchmark runs on exactly one GPU; "
+                                   "the fused kernel shards by rows/columns with no exchange, so "
+                                   "N GPUs would each run this same step on 1/N of the rows"}))
+        sys.exit(2)
+    import torch
+    import conv_bias_activation_amd as ba
+    import workloads as wl
+
+    case = wl.CASES[args.workload]
+    if args.tile >= 0:
+        ba.force_tile_config(args.tile)
+    step, _ = make_step(case, 0, "fused")
+    ms, wall = time_steps(step, args.steps, args.warmup)
+    tflops = case.flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[case.in_dtype]
+    if isinstance(case, wl.GemmCase):
+        tile = ba.gemm_tile_config(case.M, case.N, case.K, ba.dtypes_code(case.in_dtype, case.in_dtype,
+                                                                           case.bias_dtype, case.out_dtype))
+        cfg = {"workload": case.name, "M": case.M, "N": case.N, "K": case.K,
+               "in": case.in_dtype, "bias": case.bias_dtype, "out": case.out_dtype, "act": case.act}
+    else:
+        Ho, Wo = case.out_hw()
+        tile = ba.conv_tile_config(case.N, case.Co, Ho, Wo, case.C * case.kh * case.kw,
+                                   ba.dtypes_code(case.in_dtype, case.in_dtype, case.bias_dtype,
+                                                  case.out_dtype))
+        cfg = {"workload": case.name, "in": case.in_dtype, "out": case.out_dtype, "act": case.act}
+    cfg["tile"] = ba.tile_config_name(tile)
+    line = {
+        "metric": "TFLOP/s of fused act(A.B+bias) (gemm_relu_4096_bf16: M=N=K=4096, bf16 in/out, "
+                  "fp32 bias, ReLU)",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": case.in_dtype,
+        "data": "synthetic (seeded PCG64 inputs of the workload's shape and distribution)",
+        "config": cfg,
+        "frac_of_peak": round(tflops / peak, 4),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4), "traffic": None,
+                     "kernel": "gemm_bias_act_kernel", "per_launch_flops": case.flops,
+                     "mean_launch_ms": round(ms, 5)},
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_others:
+        others = {}
+        for name, c in wl.CASES.items():
+            entry = {}
+            for path in ("fused", "2k"):
+                try:
+                    entry[path] = measure_case(c, path)
+                except Exception as e:  # report, never hide
+                    entry[path] = {"error": repr(e)}
+            others[name] = entry
+            torch.cuda.empty_cache()
+        line["others"] = others
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

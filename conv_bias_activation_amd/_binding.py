@@ -1,0 +1,252 @@
+"""ctypes marshalling for libbiasact.so (see include/biasact.h for the
+contract of every entry point).  No arithmetic of the method happens here."""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libbiasact.so")
+
+DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
+ACT_CODES = {"none": 0, "relu": 1, "leaky_relu": 2, "tanh": 3}
+BA_OK, BA_ERR_INVALID, BA_ERR_UNSUPPORTED, BA_ERR_HIP = 0, 1, 2, 3
+
+
+class BiasActError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(lib_path):
+        raise ImportError(f"{lib_path} is not built; run `python -m conv_bias_activation_amd.build` "
+                          "(or __graft_entry__.build()) first")
+    l = ctypes.CDLL(lib_path)
+    vp, i64, u32, i32p = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.POINTER(ctypes.c_int32)
+    l.gemm_bias_act.argtypes = [vp, vp, vp, vp, i64, i64, i64, u32, ctypes.c_int, ctypes.c_float, vp]
+    l.gemm_bias_act.restype = ctypes.c_int
+    l.gemm_bias_act_2k.argtypes = [vp, vp, vp, vp, i64, i64, i64, u32, ctypes.c_int, ctypes.c_float,
+                                   vp, ctypes.c_size_t, vp]
+    l.gemm_bias_act_2k.restype = ctypes.c_int
+    l.gemm_bias_act_workspace_size.argtypes = [i64, i64]
+    l.gemm_bias_act_workspace_size.restype = ctypes.c_size_t
+    conv = [vp, vp, vp, vp] + [i64] * 7 + [i32p, i32p, i32p, u32, ctypes.c_int]
+    l.conv2d_bias_act.argtypes = conv + [vp]
+    l.conv2d_bias_act.restype = ctypes.c_int
+    l.conv2d_bias_act_2k.argtypes = conv + [vp, ctypes.c_size_t, vp]
+    l.conv2d_bias_act_2k.restype = ctypes.c_int
+    l.conv2d_bias_act_workspace_size.argtypes = [i64] * 7 + [i32p, i32p, i32p]
+    l.conv2d_bias_act_workspace_size.restype = ctypes.c_size_t
+    l.biasact_status_string.argtypes = [ctypes.c_int]
+    l.biasact_status_string.restype = ctypes.c_char_p
+    l.biasact_num_tile_configs.argtypes = []
+    l.biasact_num_tile_configs.restype = ctypes.c_int
+    l.biasact_tile_config_name.argtypes = [ctypes.c_int, ctypes.c_char_p, ctypes.c_size_t]
+    l.biasact_tile_config_name.restype = ctypes.c_int
+    l.biasact_gemm_tile_config.argtypes = [i64, i64, i64, u32]
+    l.biasact_gemm_tile_config.restype = ctypes.c_int
+    l.biasact_conv_tile_config.argtypes = [i64] * 5 + [u32]
+    l.biasact_conv_tile_config.restype = ctypes.c_int
+    l.biasact_force_tile_config.argtypes = [ctypes.c_int]
+    l.biasact_force_tile_config.restype = ctypes.c_int
+    return l
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.biasact_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status == BA_OK:
+        return
+    msg = f"{what}: {status_string(status)}"
+    if status in (BA_ERR_INVALID, BA_ERR_UNSUPPORTED):
+        raise ValueError(msg)
+    raise BiasActError(status, msg)
+
+
+def dtypes_code(a: str, b: str, bias: Optional[str], out: str) -> int:
+    try:
+        codes = [DTYPE_CODES[a], DTYPE_CODES[b], DTYPE_CODES[bias or "f32"], DTYPE_CODES[out]]
+    except KeyError as e:
+        raise ValueError(f"unknown element type {e}; supported: {sorted(DTYPE_CODES)}") from None
+    return codes[0] | (codes[1] << 8) | (codes[2] << 16) | (codes[3] << 24)
+
+
+def _act(act) -> int:
+    if isinstance(act, int):
+        return act
+    if act not in ACT_CODES:
+        raise ValueError(f"unknown activation {act!r}; supported: {sorted(ACT_CODES)}")
+    return ACT_CODES[act]
+
+
+# -- torch marshalling ------------------------------------------------------
+
+def _torch():
+    import torch  # device memory and streams only
+    return torch
+
+
+def _tname(t) -> str:
+    torch = _torch()
+    m = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
+    if t.dtype not in m:
+        raise ValueError(f"unsupported tensor dtype {t.dtype}; supported: float32, float16, bfloat16")
+    return m[t.dtype]
+
+
+def _dev(t, name):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (packed, row-major)")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _i32x(vals: Sequence[int], n: int, name: str):
+    vals = [int(v) for v in vals]
+    if len(vals) != n:
+        raise ValueError(f"{name} needs {n} values")
+    return (ctypes.c_int32 * n)(*vals)
+
+
+# -- GEMM ------------------------------------------------------------------
+
+def _gemm_args(A, B, bias, C):
+    if A.dim() != 2 or B.dim() != 2 or C.dim() != 2:
+        raise ValueError("A, B, C must be 2-D")
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K or tuple(C.shape) != (M, N):
+        raise ValueError(f"shape mismatch: A{tuple(A.shape)} B{tuple(B.shape)} C{tuple(C.shape)}")
+    if bias is not None and bias.numel() != N:
+        raise ValueError(f"bias must have N = {N} elements")
+    dt = dtypes_code(_tname(A), _tname(B), _tname(bias) if bias is not None else None, _tname(C))
+    return M, N, K, dt
+
+
+def gemm_bias_act(A, B, bias, C, act="none", alpha: float = 0.0, stream=None):
+    """C = act(A @ B + bias) on the GPU, C written in place."""
+    M, N, K, dt = _gemm_args(A, B, bias, C)
+    rc = lib.gemm_bias_act(_dev(A, "A"), _dev(B, "B"), _dev(bias, "bias"), _dev(C, "C"),
+                           M, N, K, dt, _act(act), float(alpha), _stream(stream))
+    _check(rc, "gemm_bias_act")
+    return C
+
+
+def gemm_bias_act_workspace_size(M: int, N: int) -> int:
+    return int(lib.gemm_bias_act_workspace_size(M, N))
+
+
+def gemm_bias_act_2k(A, B, bias, C, act="none", alpha: float = 0.0, workspace=None, stream=None):
+    M, N, K, dt = _gemm_args(A, B, bias, C)
+    if workspace is None:
+        raise ValueError("workspace (device buffer of gemm_bias_act_workspace_size bytes) is required")
+    nbytes = workspace.numel() * workspace.element_size()
+    rc = lib.gemm_bias_act_2k(_dev(A, "A"), _dev(B, "B"), _dev(bias, "bias"), _dev(C, "C"),
+                              M, N, K, dt, _act(act), float(alpha), _dev(workspace, "workspace"),
+                              nbytes, _stream(stream))
+    _check(rc, "gemm_bias_act_2k")
+    return C
+
+
+# -- conv2d ----------------------------------------------------------------
+
+def conv_out_hw(H, W, kh, kw, strides, pads, dilations):
+    """Output size with zero padding, floor rounding (None when empty)."""
+    sh, sw = strides
+    pt, pb, pl, pr = pads
+    dh, dw = dilations
+    span_h = H + pt + pb - dh * (kh - 1) - 1
+    span_w = W + pl + pr - dw * (kw - 1) - 1
+    if span_h < 0 or span_w < 0:
+        return None
+    return span_h // sh + 1, span_w // sw + 1
+
+
+def _conv_args(x, w, bias, y, strides, pads, dilations):
+    if x.dim() != 4 or w.dim() != 4 or y.dim() != 4:
+        raise ValueError("x, w, y must be 4-D (NCHW, OIHW, NCHW)")
+    N, C, H, W = x.shape
+    Co, C2, kh, kw = w.shape
+    if C2 != C:
+        raise ValueError("x and w disagree on the channel count")
+    hw = conv_out_hw(H, W, kh, kw, strides, pads, dilations)
+    if hw is not None and tuple(y.shape) != (N, Co, hw[0], hw[1]):
+        raise ValueError(f"y must be {(N, Co, hw[0], hw[1])}, got {tuple(y.shape)}")
+    if bias is not None and bias.numel() != Co:
+        raise ValueError(f"bias must have Co = {Co} elements")
+    dt = dtypes_code(_tname(x), _tname(w), _tname(bias) if bias is not None else None, _tname(y))
+    return (N, C, H, W, Co, kh, kw), dt
+
+
+def conv2d_bias_act(x, w, bias, y, strides=(1, 1), pads=(0, 0, 0, 0), dilations=(1, 1),
+                    act="tanh", stream=None):
+    """y = act(conv2d(x, w) + bias); pads = (top, bottom, left, right)."""
+    dims, dt = _conv_args(x, w, bias, y, strides, pads, dilations)
+    rc = lib.conv2d_bias_act(_dev(x, "x"), _dev(w, "w"), _dev(bias, "bias"), _dev(y, "y"), *dims,
+                             _i32x(strides, 2, "strides"), _i32x(pads, 4, "pads"),
+                             _i32x(dilations, 2, "dilations"), dt, _act(act), _stream(stream))
+    _check(rc, "conv2d_bias_act")
+    return y
+
+
+def conv2d_bias_act_workspace_size(N, C, H, W, Co, kh, kw, strides, pads, dilations) -> int:
+    return int(lib.conv2d_bias_act_workspace_size(N, C, H, W, Co, kh, kw,
+                                                  _i32x(strides, 2, "strides"), _i32x(pads, 4, "pads"),
+                                                  _i32x(dilations, 2, "dilations")))
+
+
+def conv2d_bias_act_2k(x, w, bias, y, strides=(1, 1), pads=(0, 0, 0, 0), dilations=(1, 1),
+                       act="tanh", workspace=None, stream=None):
+    dims, dt = _conv_args(x, w, bias, y, strides, pads, dilations)
+    if workspace is None:
+        raise ValueError("workspace (device buffer of conv2d_bias_act_workspace_size bytes) is required")
+    nbytes = workspace.numel() * workspace.element_size()
+    rc = lib.conv2d_bias_act_2k(_dev(x, "x"), _dev(w, "w"), _dev(bias, "bias"), _dev(y, "y"), *dims,
+                                _i32x(strides, 2, "strides"), _i32x(pads, 4, "pads"),
+                                _i32x(dilations, 2, "dilations"), dt, _act(act),
+                                _dev(workspace, "workspace"), nbytes, _stream(stream))
+    _check(rc, "conv2d_bias_act_2k")
+    return y
+
+
+# -- tile configs ------------------------------------------------------------
+
+def num_tile_configs() -> int:
+    return int(lib.biasact_num_tile_configs())
+
+
+def tile_config_name(i: int) -> str:
+    buf = ctypes.create_string_buffer(64)
+    _check(lib.biasact_tile_config_name(i, buf, 64), "tile_config_name")
+    return buf.value.decode()
+
+
+def gemm_tile_config(M, N, K, dtypes: int) -> int:
+    return int(lib.biasact_gemm_tile_config(M, N, K, dtypes))
+
+
+def conv_tile_config(N, Co, Ho, Wo, K, dtypes: int) -> int:
+    return int(lib.biasact_conv_tile_config(N, Co, Ho, Wo, K, dtypes))
+
+
+def force_tile_config(i: int):
+    _check(lib.biasact_force_tile_config(int(i)), "force_tile_config")

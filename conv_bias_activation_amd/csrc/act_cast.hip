@@ -1,0 +1,25 @@
+// act_cast.hip — second kernel of the two-kernel path (activation + cast).
+#include "kernels_impl.hpp"
+
+namespace biasact {
+int launch_act_cast(int dto, const float* ws, void* out, uint32_t n, int act, float alpha,
+                    hipStream_t s) {
+  if (n == 0) return 0;
+  const uint32_t threads = 256;
+  uint32_t blocks = (n + threads * 8 - 1) / (threads * 8);
+  if (blocks > 256u * 32u) blocks = 256u * 32u;     // grid-stride beyond 32 waves of workgroups per CU
+  switch (dto) {
+    case DT_F32:
+      hipLaunchKernelGGL(act_cast_kernel<DT_F32>, dim3(blocks), dim3(threads), 0, s, ws, out, n, act, alpha);
+      return 0;
+    case DT_F16:
+      hipLaunchKernelGGL(act_cast_kernel<DT_F16>, dim3(blocks), dim3(threads), 0, s, ws, out, n, act, alpha);
+      return 0;
+    case DT_BF16:
+      hipLaunchKernelGGL(act_cast_kernel<DT_BF16>, dim3(blocks), dim3(threads), 0, s, ws, out, n, act, alpha);
+      return 0;
+    default:
+      return -1;
+  }
+}
+}  // namespace biasact

@@ -1,0 +1,196 @@
+// api.hip — the extern "C" entry points declared in include/biasact.h.
+// Each call checks its arguments (plan.cpp), then queues one kernel (fused
+// path) or two kernels (two-kernel path) on the caller's stream.  Nothing is
+// allocated and nothing is synchronised here.
+#include <stdio.h>
+#include <string.h>
+
+#include "biasact.h"
+#include "launch.hpp"
+#include "plan.hpp"
+
+using namespace biasact;
+
+namespace {
+
+int launch_gemm_plan(const GemmPlan& p, const void* A, const void* B, const void* bias, void* C,
+                     int dto, int act, float alpha, hipStream_t s) {
+  GemmArgs a;
+  a.A = A;
+  a.B = B;
+  a.bias = bias;
+  a.C = C;
+  a.M = p.M;
+  a.N = p.N;
+  a.K = p.K;
+  a.a_bytes = p.a_bytes;
+  a.b_bytes = p.b_bytes;
+  a.bias_bytes = p.bias_bytes;
+  a.c_bytes = p.M * p.N * (dto == DT_F32 ? 4u : 2u);
+  a.bias_dt = p.bias_dt;
+  a.act = act;
+  a.alpha = alpha;
+  a.tiles_m = p.tiles_m;
+  a.tiles_n = p.tiles_n;
+  a.vec_a = p.vec_a;
+  a.vec_b = p.vec_b;
+  a.vec_c = p.N % 4 == 0 && ((uintptr_t)C % (dto == DT_F32 ? 16u : 8u)) == 0;
+  int rc;
+  switch (p.dti) {
+    case DT_F32: rc = launch_gemm_f32(dto, p.tile, a, s); break;
+    case DT_F16: rc = launch_gemm_f16(dto, p.tile, a, s); break;
+    case DT_BF16: rc = launch_gemm_bf16(dto, p.tile, a, s); break;
+    default: return kErrUnsupported;
+  }
+  if (rc) return kErrUnsupported;
+  return hipGetLastError() == hipSuccess ? kOk : kErrHip;
+}
+
+int launch_conv_plan(const ConvPlan& p, const void* x, const void* w, const void* bias, void* y,
+                     int dto, int act, hipStream_t s) {
+  ConvArgs a;
+  a.x = x;
+  a.w = w;
+  a.bias = bias;
+  a.y = y;
+  ConvGeom& g = a.geom;
+  g.N = p.N; g.C = p.C; g.H = p.H; g.W = p.W; g.Co = p.Co; g.kh = p.kh; g.kw = p.kw;
+  g.Ho = p.Ho; g.Wo = p.Wo;
+  g.sh = p.sh; g.sw = p.sw; g.pt = p.pt; g.pl = p.pl; g.dh = p.dh; g.dw = p.dw;
+  g.K = p.K;
+  g.P = p.P;
+  g.div_wo = make_fastdiv(p.Wo);
+  g.div_howo = make_fastdiv(p.Ho * p.Wo);
+  a.x_bytes = p.x_bytes;
+  a.w_bytes = p.w_bytes;
+  a.bias_bytes = p.bias_bytes;
+  a.y_bytes = p.N * p.Co * p.Ho * p.Wo * (dto == DT_F32 ? 4u : 2u);
+  a.bias_dt = p.bias_dt;
+  a.act = act;
+  a.alpha = 0.0f;
+  a.tiles_m = p.tiles_m;
+  a.tiles_n = p.tiles_n;
+  a.vec_w = p.vec_w;
+  a.vec_y = (p.Ho * p.Wo) % 4 == 0 && ((uintptr_t)y % (dto == DT_F32 ? 16u : 8u)) == 0;
+  int rc;
+  switch (p.dti) {
+    case DT_F32: rc = launch_conv_f32(dto, p.tile, a, s); break;
+    case DT_F16: rc = launch_conv_f16(dto, p.tile, a, s); break;
+    case DT_BF16: rc = launch_conv_bf16(dto, p.tile, a, s); break;
+    default: return kErrUnsupported;
+  }
+  if (rc) return kErrUnsupported;
+  return hipGetLastError() == hipSuccess ? kOk : kErrHip;
+}
+
+int launch_second_kernel(int dto, const void* ws, void* out, uint64_t n, int act, float alpha,
+                         hipStream_t s) {
+  if (launch_act_cast(dto, static_cast<const float*>(ws), out, (uint32_t)n, act, alpha, s))
+    return kErrUnsupported;
+  return hipGetLastError() == hipSuccess ? kOk : kErrHip;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_bias_act(const void* A, const void* B, const void* bias, void* C, int64_t M, int64_t N,
+                  int64_t K, uint32_t dtypes, int act, float alpha, hipStream_t stream) {
+  GemmPlan p;
+  int rc = plan_gemm(A, B, bias, C, M, N, K, dtypes, act, &p);
+  if (rc || p.empty) return rc;
+  return launch_gemm_plan(p, A, B, bias, C, p.dto, act, alpha, stream);
+}
+
+size_t gemm_bias_act_workspace_size(int64_t M, int64_t N) {
+  if (M < 0 || N < 0) return 0;
+  return (size_t)M * (size_t)N * 4u;
+}
+
+int gemm_bias_act_2k(const void* A, const void* B, const void* bias, void* C, int64_t M, int64_t N,
+                     int64_t K, uint32_t dtypes, int act, float alpha, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  GemmPlan p;
+  int rc = plan_gemm(A, B, bias, C, M, N, K, dtypes, act, &p);
+  if (rc || p.empty) return rc;
+  const uint64_t need = (uint64_t)M * (uint64_t)N * 4u;
+  if (need >= (1ull << 31)) return kErrUnsupported;
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % 16) != 0) return kErrInvalid;
+  // kernel 1: same main loop, fp32 pre-activation to the workspace
+  rc = launch_gemm_plan(p, A, B, bias, workspace, DT_F32, BA_ACT_NONE, 0.0f, stream);
+  if (rc) return rc;
+  // kernel 2: activation + cast
+  return launch_second_kernel(p.dto, workspace, C, need / 4u, act, alpha, stream);
+}
+
+int conv2d_bias_act(const void* x, const void* w, const void* bias, void* y, int64_t N, int64_t C,
+                    int64_t H, int64_t W, int64_t Co, int64_t kh, int64_t kw,
+                    const int32_t strides[2], const int32_t pads[4], const int32_t dilations[2],
+                    uint32_t dtypes, int act, hipStream_t stream) {
+  ConvPlan p;
+  int rc = plan_conv(x, w, bias, y, N, C, H, W, Co, kh, kw, strides, pads, dilations, dtypes, act,
+                     &p);
+  if (rc || p.empty) return rc;
+  return launch_conv_plan(p, x, w, bias, y, p.dto, act, stream);
+}
+
+size_t conv2d_bias_act_workspace_size(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Co,
+                                      int64_t kh, int64_t kw, const int32_t strides[2],
+                                      const int32_t pads[4], const int32_t dilations[2]) {
+  ConvPlan p;
+  // geometry only: any valid element types and non-null placeholders
+  static const char dummy[16] __attribute__((aligned(16))) = {0};
+  if (plan_conv(dummy, dummy, nullptr, dummy, N, C, H, W, Co, kh, kw, strides, pads, dilations,
+                BA_DTYPES(BA_F32, BA_F32, BA_F32, BA_F32), BA_ACT_NONE, &p))
+    return 0;
+  return (size_t)p.N * p.Co * p.Ho * p.Wo * 4u;
+}
+
+int conv2d_bias_act_2k(const void* x, const void* w, const void* bias, void* y, int64_t N,
+                       int64_t C, int64_t H, int64_t W, int64_t Co, int64_t kh, int64_t kw,
+                       const int32_t strides[2], const int32_t pads[4],
+                       const int32_t dilations[2], uint32_t dtypes, int act, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  ConvPlan p;
+  int rc = plan_conv(x, w, bias, y, N, C, H, W, Co, kh, kw, strides, pads, dilations, dtypes, act,
+                     &p);
+  if (rc || p.empty) return rc;
+  const uint64_t need = (uint64_t)p.N * p.Co * p.Ho * p.Wo * 4u;
+  if (need >= (1ull << 31)) return kErrUnsupported;
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % 16) != 0) return kErrInvalid;
+  rc = launch_conv_plan(p, x, w, bias, workspace, DT_F32, BA_ACT_NONE, stream);
+  if (rc) return rc;
+  return launch_second_kernel(p.dto, workspace, y, need / 4u, act, 0.0f, stream);
+}
+
+const char* biasact_status_string(int status) { return status_string(status); }
+
+int biasact_num_tile_configs(void) { return kNumTileConfigs; }
+
+int biasact_tile_config_name(int id, char* buf, size_t n) {
+  if (id < 0 || id >= kNumTileConfigs || !buf || n == 0) return kErrInvalid;
+  const TileShapeDesc& t = kTiles[id];
+  snprintf(buf, n, "%dx%d/%dx%d", t.bm, t.bn, t.waves_m, t.waves_n);
+  return kOk;
+}
+
+int biasact_gemm_tile_config(int64_t M, int64_t N, int64_t K, uint32_t dtypes) {
+  const int f = forced_tile();
+  if (f >= 0) return f;
+  return select_gemm_tile(M, N, K, (int)(dtypes & 0xffu));
+}
+
+int biasact_conv_tile_config(int64_t N, int64_t Co, int64_t Ho, int64_t Wo, int64_t K_total,
+                             uint32_t dtypes) {
+  const int f = forced_tile();
+  if (f >= 0) return f;
+  return select_conv_tile(N, Co, Ho, Wo, K_total, (int)(dtypes & 0xffu));
+}
+
+int biasact_force_tile_config(int id) {
+  if (id < -1 || id >= kNumTileConfigs) return kErrInvalid;
+  set_forced_tile(id);
+  return kOk;
+}
+
+}  // extern "C"

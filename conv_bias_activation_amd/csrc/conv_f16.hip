@@ -1,0 +1,8 @@
+// conv_f16.hip — fused implicit-GEMM conv2d + bias + activation kernels for f16 inputs.
+#include "kernels_impl.hpp"
+
+namespace biasact {
+int launch_conv_f16(int dto, int tile, const ConvArgs& a, hipStream_t s) {
+  return launch_conv_in<DT_F16>(dto, tile, a, s);
+}
+}  // namespace biasact

@@ -1,0 +1,147 @@
+// device_common.hpp — gfx950 device helpers shared by the biasact kernels:
+// element traits, buffer-resource loads/stores (out-of-range reads return 0,
+// out-of-range writes are dropped), activation, output casts and the
+// 32x32 MFMA step.
+//
+// Page legend used in comments:
+//   [MLR] "CANN pyasc MatmulLeakyRelu 融合算子实战" (lshu.cn/news/76032)
+//   [FMR] ops-nn fused_matmul_relu article (mlqm.cn/news/1824)
+//   [FCT] multimodal-ops "Fused ConvTanh" article (wmrh.cn/news/81139)
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace biasact {
+
+enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+enum : int { ACT_NONE = 0, ACT_RELU = 1, ACT_LEAKY = 2, ACT_TANH = 3 };
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// Offset used for a masked-off access: beyond every num_records the library
+// creates (all tensors are < 2^31 bytes), so the hardware range check turns
+// the load into 0 and the store into a no-op.
+constexpr uint32_t kOOB = 0x80000000u;
+
+// Element traits.  A "chunk" is 16 bytes of consecutive reduction-index (k)
+// values: 8 for 16-bit inputs, 4 for fp32.
+template <int DT> struct Elem;
+template <> struct Elem<DT_F32>  { static constexpr int bytes = 4, epc = 4; };
+template <> struct Elem<DT_F16>  { static constexpr int bytes = 2, epc = 8; };
+template <> struct Elem<DT_BF16> { static constexpr int bytes = 2, epc = 8; };
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t nbytes) {
+  // dword3 0x00020000: raw (untyped) 32-bit data format for gfx9-family buffers.
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)nbytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 ld_b128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t ld_b32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ uint16_t ld_b16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ void st_b128(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
+__device__ __forceinline__ void st_b64(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+}
+__device__ __forceinline__ void st_b32(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
+}
+__device__ __forceinline__ void st_b16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint16_t v) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, 0);
+}
+
+// ---- scalar conversions --------------------------------------------------
+
+// Exact widening of one stored element to fp32.
+template <int DT> __device__ __forceinline__ float widen(uint32_t w);
+template <> __device__ __forceinline__ float widen<DT_F32>(uint32_t w) { return __uint_as_float(w); }
+template <> __device__ __forceinline__ float widen<DT_F16>(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)w);
+}
+template <> __device__ __forceinline__ float widen<DT_BF16>(uint32_t w) {
+  return __uint_as_float(w << 16);   // bf16 is the upper half of a binary32
+}
+
+// Narrowing fp32 -> output element bits, round to nearest even (the hardware
+// conversions v_cvt_f16_f32 / v_cvt_pk_bf16_f32 round to nearest even).
+template <int DT> __device__ __forceinline__ uint32_t narrow(float v);
+template <> __device__ __forceinline__ uint32_t narrow<DT_F32>(float v) { return __float_as_uint(v); }
+template <> __device__ __forceinline__ uint32_t narrow<DT_F16>(float v) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v);
+}
+template <> __device__ __forceinline__ uint32_t narrow<DT_BF16>(float v) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
+// ---- activation ----------------------------------------------------------
+// LeakyReLU keeps non-negative values and scales negative ones by alpha
+// ([MLR] 概述); ReLU maps non-positive values to +0 ([FMR] host loop); tanh
+// is the hyperbolic tangent of [FCT] (K2 chain), evaluated with the device
+// math library's tanhf, which stays finite where the page's quotient of
+// exponentials overflows.
+__device__ __forceinline__ float apply_act(int act, float z, float alpha) {
+  switch (act) {
+    case ACT_RELU:  return z > 0.0f ? z : 0.0f;
+    case ACT_LEAKY: return z >= 0.0f ? z : alpha * z;
+    case ACT_TANH:  return tanhf(z);
+    default:        return z;
+  }
+}
+
+// ---- MFMA ----------------------------------------------------------------
+// One 16-byte chunk per lane of each operand.  For 16-bit inputs that is one
+// v_mfma_f32_32x32x16 (8 k-values per lane); for fp32 it is four
+// v_mfma_f32_32x32x2_f32, element e of the chunk feeding the e-th one.  The
+// two operands always use the same (lane, element) -> k assignment, so the
+// instruction sums every k of the chunk pair exactly once.
+template <int DT> __device__ __forceinline__ void mfma_chunk(f32x16& acc, u32x4 a, u32x4 b);
+template <> __device__ __forceinline__ void mfma_chunk<DT_BF16>(f32x16& acc, u32x4 a, u32x4 b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+}
+template <> __device__ __forceinline__ void mfma_chunk<DT_F16>(f32x16& acc, u32x4 a, u32x4 b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                               __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
+}
+template <> __device__ __forceinline__ void mfma_chunk<DT_F32>(f32x16& acc, u32x4 a, u32x4 b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+}
+
+// Unsigned division by a runtime-invariant divisor via a precomputed
+// multiplier (round-up method of Granlund & Montgomery, "Division by
+// Invariant Integers using Multiplication", 1994): q = (umulhi(n, mul) + n) >> shift
+// for 0 <= n < 2^31.
+struct FastDiv {
+  uint32_t div, mul, shift;
+};
+__host__ __device__ inline FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f;
+  f.div = d;
+  uint32_t s = 0;
+  while ((1ull << s) < d) ++s;     // s = ceil(log2 d)
+  f.shift = s;
+  // mul = floor(2^32 * (2^s - d) / d) + 1
+  f.mul = (uint32_t)(((1ull << 32) * ((1ull << s) - d)) / d + 1);
+  return f;
+}
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
+  return (__umulhi(n, f.mul) + n) >> f.shift;
+}
+
+}  // namespace biasact

@@ -1,0 +1,291 @@
+// kernels_impl.hpp — __global__ kernels built on the main loop of
+// mfma_core.hpp: the fused GEMM + bias + activation, the fused implicit-GEMM
+// conv2d + bias + activation, and the elementwise activation/cast pass of the
+// two-kernel path.  Each translation unit instantiates them for one input
+// element type.
+#pragma once
+
+#include "launch.hpp"
+#include "mfma_core.hpp"
+
+namespace biasact {
+
+// Per-element bias fetch (fp32, fp16 or bf16 storage), exact widening.
+__device__ __forceinline__ float load_bias(__amdgpu_buffer_rsrc_t r, int dt, uint32_t idx) {
+  if (dt == DT_F32) return __uint_as_float(ld_b32(r, idx * 4));
+  const uint32_t w = ld_b16(r, idx * 2);
+  return dt == DT_F16 ? widen<DT_F16>(w) : widen<DT_BF16>(w);
+}
+
+// Store four consecutive outputs (one accumulator register group).
+template <int DTO>
+__device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t r, uint32_t off_elems, bool ok,
+                                       float v0, float v1, float v2, float v3) {
+  const uint32_t off = ok ? off_elems * Elem<DTO>::bytes : kOOB;
+  if constexpr (DTO == DT_F32) {
+    u32x4 o;
+    o.x = __float_as_uint(v0); o.y = __float_as_uint(v1);
+    o.z = __float_as_uint(v2); o.w = __float_as_uint(v3);
+    st_b128(r, off, o);
+  } else {
+    u32x2 o;
+    o.x = narrow<DTO>(v0) | (narrow<DTO>(v1) << 16);
+    o.y = narrow<DTO>(v2) | (narrow<DTO>(v3) << 16);
+    st_b64(r, off, o);
+  }
+}
+
+template <int DTO>
+__device__ __forceinline__ void store1(__amdgpu_buffer_rsrc_t r, uint32_t off_elems, bool ok, float v) {
+  const uint32_t off = ok ? off_elems * Elem<DTO>::bytes : kOOB;
+  if constexpr (DTO == DT_F32) st_b32(r, off, __float_as_uint(v));
+  else st_b16(r, off, (uint16_t)narrow<DTO>(v));
+}
+
+// ---------------------------------------------------------------------------
+// C[M,N] = act(A[M,K] . B[K,N] + bias[N])   ([MLR] 概述 / 样例规格;
+// [FMR] fused_matmul_relu).  One workgroup per BM x BN output tile.
+// ---------------------------------------------------------------------------
+template <int DTI, int DTO, class TL>
+__global__ __launch_bounds__(TL::threads, 1) void gemm_bias_act_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TL::stage_bytes];
+  constexpr int BK = kChunks * Elem<DTI>::epc;
+
+  uint32_t tm, tn;
+  map_tile(blockIdx.x, gridDim.x, a.tiles_m, a.tiles_n, tm, tn);
+  const uint32_t m0 = tm * TL::BM, n0 = tn * TL::BN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wave_m = wave / TL::WAVES_N, wave_n = wave % TL::WAVES_N;
+  const int half = lane >> 5, lrow = lane & 31;
+
+  // accumulator starts at the bias (the extra reduction term)
+  f32x16 acc[TL::SN][TL::SM];
+  {
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.bias, a.bias_bytes);
+#pragma unroll
+    for (int si = 0; si < TL::SN; ++si) {
+      f32x16 b;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t n = n0 + wave_n * TL::WTN + si * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        b[r] = (a.bias_dt >= 0 && n < a.N) ? load_bias(rb, a.bias_dt, n) : 0.0f;
+      }
+#pragma unroll
+      for (int sj = 0; sj < TL::SM; ++sj) acc[si][sj] = b;
+    }
+  }
+
+  DenseRowLoader<DTI, TL> la;
+  DenseColLoader<DTI, TL> lb;
+  la.init(a.A, a.a_bytes, a.M, a.K, m0, a.vec_a);
+  lb.init(a.B, a.b_bytes, a.K, a.N, n0, a.vec_b);
+  const int ktiles = (int)((a.K + BK - 1) / BK);
+  main_loop<DTI, TL>(acc, la, lb, smem, ktiles);
+
+  // epilogue: activation, cast, one store per element
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.C, a.c_bytes);
+#pragma unroll
+  for (int si = 0; si < TL::SN; ++si)
+#pragma unroll
+    for (int sj = 0; sj < TL::SM; ++sj) {
+      const uint32_t m = m0 + wave_m * TL::WTM + sj * 32 + lrow;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t n = n0 + wave_n * TL::WTN + si * 32 + 8 * g + 4 * half;
+        const float y0 = apply_act(a.act, acc[si][sj][4 * g + 0], a.alpha);
+        const float y1 = apply_act(a.act, acc[si][sj][4 * g + 1], a.alpha);
+        const float y2 = apply_act(a.act, acc[si][sj][4 * g + 2], a.alpha);
+        const float y3 = apply_act(a.act, acc[si][sj][4 * g + 3], a.alpha);
+        if (a.vec_c) {
+          store4<DTO>(rc, m * a.N + n, m < a.M && n < a.N, y0, y1, y2, y3);
+        } else {
+          const bool mok = m < a.M;
+          store1<DTO>(rc, m * a.N + n + 0, mok && n + 0 < a.N, y0);
+          store1<DTO>(rc, m * a.N + n + 1, mok && n + 1 < a.N, y1);
+          store1<DTO>(rc, m * a.N + n + 2, mok && n + 2 < a.N, y2);
+          store1<DTO>(rc, m * a.N + n + 3, mok && n + 3 < a.N, y3);
+        }
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// y[N,Co,Ho,Wo] = act(conv2d(x, w) + bias[Co]) as an implicit GEMM:
+// j = co (weights [Co, C*kh*kw]), i = p = (n, oh, ow) gathered from x
+// ([FCT] "这个算子到底在算什么" and "双 Kernel 是怎么分工的").
+// ---------------------------------------------------------------------------
+template <int DTI, int DTO, class TL>
+__global__ __launch_bounds__(TL::threads, 1) void conv_bias_act_kernel(ConvArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TL::stage_bytes];
+  constexpr int BK = kChunks * Elem<DTI>::epc;
+  const ConvGeom& G = a.geom;
+
+  uint32_t tm, tn;
+  map_tile(blockIdx.x, gridDim.x, a.tiles_m, a.tiles_n, tm, tn);
+  const uint32_t m0 = tm * TL::BM, p0 = tn * TL::BN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wave_m = wave / TL::WAVES_N, wave_n = wave % TL::WAVES_N;
+  const int half = lane >> 5, lrow = lane & 31;
+
+  f32x16 acc[TL::SN][TL::SM];
+  {
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.bias, a.bias_bytes);
+#pragma unroll
+    for (int sj = 0; sj < TL::SM; ++sj) {
+      const uint32_t co = m0 + wave_m * TL::WTM + sj * 32 + lrow;
+      const float bv = (a.bias_dt >= 0 && co < G.Co) ? load_bias(rb, a.bias_dt, co) : 0.0f;
+#pragma unroll
+      for (int si = 0; si < TL::SN; ++si)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[si][sj][r] = bv;
+    }
+  }
+
+  DenseRowLoader<DTI, TL> la;
+  ConvGatherLoader<DTI, TL> lb;
+  la.init(a.w, a.w_bytes, G.Co, G.K, m0, a.vec_w);
+  lb.init(a.x, a.x_bytes, G, p0);
+  const int ktiles = (int)((G.K + BK - 1) / BK);
+  main_loop<DTI, TL>(acc, la, lb, smem, ktiles);
+
+  const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.y, a.y_bytes);
+  const uint32_t howo = G.Ho * G.Wo;
+#pragma unroll
+  for (int si = 0; si < TL::SN; ++si)
+#pragma unroll
+    for (int sj = 0; sj < TL::SM; ++sj) {
+      const uint32_t co = m0 + wave_m * TL::WTM + sj * 32 + lrow;
+      const bool cok = co < G.Co;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t p = p0 + wave_n * TL::WTN + si * 32 + 8 * g + 4 * half;
+        const float y0 = apply_act(a.act, acc[si][sj][4 * g + 0], a.alpha);
+        const float y1 = apply_act(a.act, acc[si][sj][4 * g + 1], a.alpha);
+        const float y2 = apply_act(a.act, acc[si][sj][4 * g + 2], a.alpha);
+        const float y3 = apply_act(a.act, acc[si][sj][4 * g + 3], a.alpha);
+        if (a.vec_y) {
+          // Ho*Wo % 4 == 0: the four positions lie in one image
+          const uint32_t img = fdiv(p, G.div_howo);
+          const uint32_t q = p - img * howo;
+          store4<DTO>(ry, (img * G.Co + co) * howo + q, cok && p < G.P, y0, y1, y2, y3);
+        } else {
+          const float yv[4] = {y0, y1, y2, y3};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t pe = p + e;
+            const uint32_t img = fdiv(pe, G.div_howo);
+            const uint32_t q = pe - img * howo;
+            store1<DTO>(ry, (img * G.Co + co) * howo + q, cok && pe < G.P, yv[e]);
+          }
+        }
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Second kernel of the two-kernel path: out[i] = cast(act(ws[i])) over a
+// packed fp32 workspace that already holds A.B + bias (GEMM, [M,N]) or
+// conv + bias (conv, NCHW).  Each thread handles 8 consecutive elements with
+// two 16-byte loads; grid-stride over the array.
+// ---------------------------------------------------------------------------
+template <int DTO>
+__global__ __launch_bounds__(256) void act_cast_kernel(const float* ws, void* out, uint32_t n,
+                                                       int act, float alpha) {
+  const __amdgpu_buffer_rsrc_t ri = make_rsrc(ws, n * 4u);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(out, n * (uint32_t)Elem<DTO>::bytes);
+  const uint32_t stride = gridDim.x * blockDim.x * 8u;
+  for (uint32_t base = (blockIdx.x * blockDim.x + threadIdx.x) * 8u; base < n; base += stride) {
+    const bool full = base + 8u <= n;
+    u32x4 v0 = ld_b128(ri, full ? base * 4u : kOOB);
+    u32x4 v1 = ld_b128(ri, full ? base * 4u + 16u : kOOB);
+    float z[8] = {__uint_as_float(v0.x), __uint_as_float(v0.y), __uint_as_float(v0.z),
+                  __uint_as_float(v0.w), __uint_as_float(v1.x), __uint_as_float(v1.y),
+                  __uint_as_float(v1.z), __uint_as_float(v1.w)};
+    if (!full) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        z[e] = __uint_as_float(ld_b32(ri, base + e < n ? (base + e) * 4u : kOOB));
+    }
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = apply_act(act, z[e], alpha);
+    if (full) {
+      store4<DTO>(ro, base, true, y[0], y[1], y[2], y[3]);
+      store4<DTO>(ro, base + 4, true, y[4], y[5], y[6], y[7]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) store1<DTO>(ro, base + e, base + e < n, y[e]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launch helpers (instantiated per input type in its own TU).
+// ---------------------------------------------------------------------------
+template <int DTI, int DTO, class TL>
+inline void launch_gemm_t(const GemmArgs& a, hipStream_t s) {
+  const uint32_t nblk = a.tiles_m * a.tiles_n;
+  hipLaunchKernelGGL((gemm_bias_act_kernel<DTI, DTO, TL>), dim3(nblk), dim3(TL::threads), 0, s, a);
+}
+
+template <int DTI, int DTO, class TL>
+inline void launch_conv_t(const ConvArgs& a, hipStream_t s) {
+  const uint32_t nblk = a.tiles_m * a.tiles_n;
+  hipLaunchKernelGGL((conv_bias_act_kernel<DTI, DTO, TL>), dim3(nblk), dim3(TL::threads), 0, s, a);
+}
+
+// The tile table (same ids and order as kTiles in plan.hpp).
+using T0 = Tile<256, 256, 2, 2>;
+using T1 = Tile<128, 256, 2, 2>;
+using T2 = Tile<128, 128, 2, 2>;
+using T3 = Tile<64, 128, 2, 2>;
+using T4 = Tile<64, 256, 1, 4>;
+using T5 = Tile<64, 64, 2, 2>;
+
+template <int DTI, int DTO>
+inline int launch_gemm_tile(int tile, const GemmArgs& a, hipStream_t s) {
+  switch (tile) {
+    case 0: launch_gemm_t<DTI, DTO, T0>(a, s); return 0;
+    case 1: launch_gemm_t<DTI, DTO, T1>(a, s); return 0;
+    case 2: launch_gemm_t<DTI, DTO, T2>(a, s); return 0;
+    case 3: launch_gemm_t<DTI, DTO, T3>(a, s); return 0;
+    case 4: launch_gemm_t<DTI, DTO, T4>(a, s); return 0;
+    case 5: launch_gemm_t<DTI, DTO, T5>(a, s); return 0;
+    default: return -1;
+  }
+}
+
+template <int DTI, int DTO>
+inline int launch_conv_tile(int tile, const ConvArgs& a, hipStream_t s) {
+  switch (tile) {
+    case 0: launch_conv_t<DTI, DTO, T0>(a, s); return 0;
+    case 1: launch_conv_t<DTI, DTO, T1>(a, s); return 0;
+    case 2: launch_conv_t<DTI, DTO, T2>(a, s); return 0;
+    case 3: launch_conv_t<DTI, DTO, T3>(a, s); return 0;
+    case 4: launch_conv_t<DTI, DTO, T4>(a, s); return 0;
+    case 5: launch_conv_t<DTI, DTO, T5>(a, s); return 0;
+    default: return -1;
+  }
+}
+
+template <int DTI>
+inline int launch_gemm_in(int dto, int tile, const GemmArgs& a, hipStream_t s) {
+  switch (dto) {
+    case DT_F32: return launch_gemm_tile<DTI, DT_F32>(tile, a, s);
+    case DT_F16: return launch_gemm_tile<DTI, DT_F16>(tile, a, s);
+    case DT_BF16: return launch_gemm_tile<DTI, DT_BF16>(tile, a, s);
+    default: return -1;
+  }
+}
+
+template <int DTI>
+inline int launch_conv_in(int dto, int tile, const ConvArgs& a, hipStream_t s) {
+  switch (dto) {
+    case DT_F32: return launch_conv_tile<DTI, DT_F32>(tile, a, s);
+    case DT_F16: return launch_conv_tile<DTI, DT_F16>(tile, a, s);
+    case DT_BF16: return launch_conv_tile<DTI, DT_BF16>(tile, a, s);
+    default: return -1;
+  }
+}
+
+}  // namespace biasact

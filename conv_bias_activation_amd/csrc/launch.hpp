@@ -1,0 +1,52 @@
+// launch.hpp — host <-> kernel argument blocks, the tile-config table and
+// the per-input-type launch entry points of the biasact library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mfma_core.hpp"
+
+namespace biasact {
+
+// Kernel argument block of the fused GEMM (passed by value).
+struct GemmArgs {
+  const void* A;
+  const void* B;
+  const void* bias;
+  void* C;
+  uint32_t M, N, K;
+  uint32_t a_bytes, b_bytes, bias_bytes, c_bytes;
+  int bias_dt;             // DT_* of bias, or -1 without bias
+  int act;
+  float alpha;
+  uint32_t tiles_m, tiles_n;
+  bool vec_a, vec_b, vec_c;   // 16-byte loads / 4-wide stores allowed
+};
+
+struct ConvArgs {
+  const void* x;
+  const void* w;
+  const void* bias;
+  void* y;
+  ConvGeom geom;
+  uint32_t x_bytes, w_bytes, bias_bytes, y_bytes;
+  int bias_dt;
+  int act;
+  float alpha;
+  uint32_t tiles_m, tiles_n;
+  bool vec_w, vec_y;
+};
+
+// Per-input-type launchers (one translation unit each).  Return 0, or -1 for
+// an unknown output type / tile id.
+int launch_gemm_f32(int dto, int tile, const GemmArgs& a, hipStream_t s);
+int launch_gemm_f16(int dto, int tile, const GemmArgs& a, hipStream_t s);
+int launch_gemm_bf16(int dto, int tile, const GemmArgs& a, hipStream_t s);
+int launch_conv_f32(int dto, int tile, const ConvArgs& a, hipStream_t s);
+int launch_conv_f16(int dto, int tile, const ConvArgs& a, hipStream_t s);
+int launch_conv_bf16(int dto, int tile, const ConvArgs& a, hipStream_t s);
+int launch_act_cast(int dto, const float* ws, void* out, uint32_t n, int act, float alpha,
+                    hipStream_t s);
+
+}  // namespace biasact

@@ -1,0 +1,179 @@
+// plan.cpp — argument checking, tile selection and launch planning for the
+// biasact C ABI.  Plain C++: no HIP call happens here, so every error path is
+// reachable on a machine without a GPU.
+#include "plan.hpp"
+
+#include <atomic>
+
+namespace biasact {
+
+namespace {
+
+constexpr int kF32 = 0, kF16 = 1, kBF16 = 2;
+constexpr int64_t kMaxBytes = (int64_t)1 << 31;   // every tensor < 2 GiB (32-bit buffer offsets)
+
+int elem_bytes(int dt) { return dt == kF32 ? 4 : 2; }
+int chunk_elems(int dt) { return dt == kF32 ? 4 : 8; }   // 16 bytes of one type
+bool valid_dt(int dt) { return dt == kF32 || dt == kF16 || dt == kBF16; }
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+std::atomic<int> g_forced_tile{-1};
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Shared dtype decoding: A/x and B/w share one type; bias is fp32 or that
+// type; the output is any of the three.
+int decode_dtypes(uint32_t dtypes, bool has_bias, int* dti, int* dto, int* dtb) {
+  const int a = (int)(dtypes & 0xffu), b = (int)((dtypes >> 8) & 0xffu);
+  const int bias = (int)((dtypes >> 16) & 0xffu), out = (int)((dtypes >> 24) & 0xffu);
+  if (!valid_dt(a) || b != a || !valid_dt(out)) return kErrUnsupported;
+  if (has_bias && !(bias == kF32 || bias == a)) return kErrUnsupported;
+  *dti = a;
+  *dto = out;
+  *dtb = has_bias ? bias : -1;
+  return kOk;
+}
+
+// Pick the first tile (in preference order) that yields at least `want`
+// workgroups; otherwise the one with the most workgroups.
+int pick_tile(const int* order, int n_order, int64_t rows_j, int64_t rows_i, int64_t want) {
+  int best = order[n_order - 1];
+  int64_t best_tiles = -1;
+  for (int k = 0; k < n_order; ++k) {
+    const TileShapeDesc& t = kTiles[order[k]];
+    const int64_t tiles = ceil_div(rows_j, t.bm) * ceil_div(rows_i, t.bn);
+    if (tiles >= want) return order[k];
+    if (tiles > best_tiles) {
+      best_tiles = tiles;
+      best = order[k];
+    }
+  }
+  return best;
+}
+
+}  // namespace
+
+int forced_tile() { return g_forced_tile.load(std::memory_order_relaxed); }
+void set_forced_tile(int id) { g_forced_tile.store(id, std::memory_order_relaxed); }
+
+int select_gemm_tile(int64_t M, int64_t N, int64_t /*K*/, int /*dti*/) {
+  // Largest tiles first while the grid still covers all 256 compute units.
+  static const int order[] = {0, 1, 2, 3, 5};
+  return pick_tile(order, 5, M, N, 256);
+}
+
+int select_conv_tile(int64_t N, int64_t Co, int64_t Ho, int64_t Wo, int64_t /*K*/, int /*dti*/) {
+  const int64_t P = N * Ho * Wo;
+  if (Co <= 64) {
+    static const int order[] = {4, 3, 5};
+    return pick_tile(order, 3, Co, P, 256);
+  }
+  static const int order[] = {0, 1, 2, 3, 5};
+  return pick_tile(order, 5, Co, P, 256);
+}
+
+int plan_gemm(const void* A, const void* B, const void* bias, const void* C, int64_t M, int64_t N,
+              int64_t K, uint32_t dtypes, int act, GemmPlan* p) {
+  if (!p) return kErrInvalid;
+  if (M < 0 || N < 0 || K < 0) return kErrInvalid;
+  if (act < 0 || act > 3) return kErrInvalid;
+  int dti, dto, dtb;
+  int rc = decode_dtypes(dtypes, bias != nullptr, &dti, &dto, &dtb);
+  if (rc) return rc;
+  const int64_t es = elem_bytes(dti);
+  const int64_t a_bytes = M * K * es, b_bytes = K * N * es, c_bytes = M * N * elem_bytes(dto);
+  const int64_t bias_bytes = bias ? N * elem_bytes(dtb) : 0;
+  if (M >= kMaxBytes || N >= kMaxBytes || K >= kMaxBytes) return kErrUnsupported;
+  if (a_bytes >= kMaxBytes || b_bytes >= kMaxBytes || c_bytes >= kMaxBytes) return kErrUnsupported;
+  if ((a_bytes > 0 && !A) || (b_bytes > 0 && !B) || (c_bytes > 0 && !C)) return kErrInvalid;
+  p->dti = dti;
+  p->dto = dto;
+  p->bias_dt = dtb;
+  p->M = (uint32_t)M;
+  p->N = (uint32_t)N;
+  p->K = (uint32_t)K;
+  p->a_bytes = (uint32_t)a_bytes;
+  p->b_bytes = (uint32_t)b_bytes;
+  p->bias_bytes = (uint32_t)bias_bytes;
+  p->c_bytes = (uint32_t)c_bytes;
+  const int epc = chunk_elems(dti);
+  p->vec_a = K % epc == 0 && aligned(A, 16);
+  p->vec_b = N % epc == 0 && aligned(B, 16);
+  p->vec_c = N % 4 == 0 && aligned(C, 4 * (uintptr_t)elem_bytes(dto));
+  p->empty = M == 0 || N == 0;
+  int tile = forced_tile();
+  if (tile < 0 || tile >= kNumTileConfigs) tile = select_gemm_tile(M, N, K, dti);
+  p->tile = tile;
+  p->tiles_m = (uint32_t)ceil_div(M, kTiles[tile].bm);
+  p->tiles_n = (uint32_t)ceil_div(N, kTiles[tile].bn);
+  return kOk;
+}
+
+int plan_conv(const void* x, const void* w, const void* bias, const void* y, int64_t N, int64_t C,
+              int64_t H, int64_t W, int64_t Co, int64_t kh, int64_t kw, const int32_t* strides,
+              const int32_t* pads, const int32_t* dilations, uint32_t dtypes, int act,
+              ConvPlan* p) {
+  if (!p || !strides || !pads || !dilations) return kErrInvalid;
+  if (N < 0 || C <= 0 || H <= 0 || W <= 0 || Co <= 0 || kh <= 0 || kw <= 0) return kErrInvalid;
+  if (act < 0 || act > 3) return kErrInvalid;
+  if (act == 2) return kErrUnsupported;                 // no alpha argument on this entry point
+  const int32_t sh = strides[0], sw = strides[1], dh = dilations[0], dw = dilations[1];
+  const int32_t pt = pads[0], pb = pads[1], pl = pads[2], pr = pads[3];
+  if (sh < 1 || sw < 1 || dh < 1 || dw < 1) return kErrInvalid;
+  if (pt < 0 || pb < 0 || pl < 0 || pr < 0) return kErrInvalid;
+  const int64_t span_h = H + pt + pb - (int64_t)dh * (kh - 1) - 1;
+  const int64_t span_w = W + pl + pr - (int64_t)dw * (kw - 1) - 1;
+  if (span_h < 0 || span_w < 0) return kErrInvalid;  // empty output
+  const int64_t Ho = span_h / sh + 1, Wo = span_w / sw + 1;
+  int dti, dto, dtb;
+  int rc = decode_dtypes(dtypes, bias != nullptr, &dti, &dto, &dtb);
+  if (rc) return rc;
+  const int64_t es = elem_bytes(dti);
+  const int64_t K = C * kh * kw, P = N * Ho * Wo;
+  const int64_t x_bytes = N * C * H * W * es, w_bytes = Co * K * es;
+  const int64_t y_bytes = N * Co * Ho * Wo * elem_bytes(dto);
+  const int64_t bias_bytes = bias ? Co * elem_bytes(dtb) : 0;
+  if (C >= kMaxBytes || H >= kMaxBytes || W >= kMaxBytes || Co >= kMaxBytes || K >= kMaxBytes ||
+      P >= kMaxBytes || Ho * Wo >= kMaxBytes || H + pt + pb >= kMaxBytes || W + pl + pr >= kMaxBytes)
+    return kErrUnsupported;
+  if (x_bytes >= kMaxBytes || w_bytes >= kMaxBytes || y_bytes >= kMaxBytes) return kErrUnsupported;
+  if ((x_bytes > 0 && !x) || !w || (y_bytes > 0 && !y)) return kErrInvalid;
+  p->dti = dti;
+  p->dto = dto;
+  p->bias_dt = dtb;
+  p->N = (uint32_t)N; p->C = (uint32_t)C; p->H = (uint32_t)H; p->W = (uint32_t)W;
+  p->Co = (uint32_t)Co; p->kh = (uint32_t)kh; p->kw = (uint32_t)kw;
+  p->Ho = (uint32_t)Ho; p->Wo = (uint32_t)Wo;
+  p->sh = sh; p->sw = sw; p->pt = pt; p->pb = pb; p->pl = pl; p->pr = pr; p->dh = dh; p->dw = dw;
+  p->K = (uint32_t)K;
+  p->P = (uint32_t)P;
+  p->x_bytes = (uint32_t)x_bytes;
+  p->w_bytes = (uint32_t)w_bytes;
+  p->bias_bytes = (uint32_t)bias_bytes;
+  p->y_bytes = (uint32_t)y_bytes;
+  p->vec_w = K % chunk_elems(dti) == 0 && aligned(w, 16);
+  p->vec_y = (Ho * Wo) % 4 == 0 && aligned(y, 4 * (uintptr_t)elem_bytes(dto));
+  p->empty = N == 0;
+  int tile = forced_tile();
+  if (tile < 0 || tile >= kNumTileConfigs) tile = select_conv_tile(N, Co, Ho, Wo, K, dti);
+  p->tile = tile;
+  p->tiles_m = (uint32_t)ceil_div(Co, kTiles[tile].bm);
+  p->tiles_n = (uint32_t)ceil_div(P, kTiles[tile].bn);
+  return kOk;
+}
+
+const char* status_string(int s) {
+  switch (s) {
+    case kOk: return "ok";
+    case kErrInvalid:
+      return "invalid argument (null pointer, negative or empty dimension, bad activation, "
+             "stride/dilation < 1, pad < 0, empty conv output, or workspace too small)";
+    case kErrUnsupported:
+      return "unsupported (element types: A = B in {f32, f16, bf16}, bias in {f32, input type}, "
+             "output in {f32, f16, bf16}; conv has no LeakyReLU; every tensor < 2^31 bytes)";
+    case kErrHip: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+}  // namespace biasact

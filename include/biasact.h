@@ -1,0 +1,142 @@
+/*
+ * biasact.h — C ABI of the MI355X (gfx950) fused contraction + bias +
+ * activation library (libbiasact.so).
+ *
+ * Computes, in one kernel and one store per output element,
+ *     C = act(A . B + bias)                       (GEMM)
+ *     y = act(conv2d(x, w) + bias)                (conv2d as an implicit GEMM)
+ * with act in {identity, ReLU, LeakyReLU(alpha), tanh}.  Sources (web pages,
+ * cited by title and section):
+ *   - "CANN pyasc MatmulLeakyRelu 融合算子实战" (lshu.cn/news/76032): section
+ *     概述 (C = A x B + Bias, then LeakyReLU: non-negative values unchanged,
+ *     negative values times alpha), section 样例规格 (operand shapes and types:
+ *     fp16 A/B, fp32 bias [1,N], fp32 alpha, fp32 C), section 补充说明 (bias
+ *     may be fp16 or fp32 for fp16 operands).
+ *   - ops-nn fused_matmul_relu article (mlqm.cn/news/1824): sections
+ *     "fused_matmul_relu底层到底做了什么" (fused matmul + ReLU on caller-owned
+ *     device buffers, one HBM read of the operands and one write of C; the
+ *     two-step matmul-then-activation fallback through a device temporary).
+ *   - multimodal-ops "Fused ConvTanh" article (wmrh.cn/news/81139): sections
+ *     这个算子到底在算什么 (y = tanh(conv2d(x, filter, bias)) with strides,
+ *     pads and dilations), 双 Kernel 是怎么分工的 (implicit GEMM with the
+ *     weights as the co x k operand; bias as one extra k column; the two-kernel
+ *     split through an fp32 workspace), 快速上手 (the Python entry point
+ *     fused_conv_tanh(x, conv_filter, bias, strides, pads, dilations)).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees, or synchronises.  Work is enqueued on `stream`
+ *     (0 = the null stream) and runs asynchronously; the call returns once the
+ *     kernels are queued.
+ *   - Tensors are packed and contiguous: A[M,K], B[K,N], C[M,N] row-major;
+ *     x[N,C,H,W], w[Co,C,kh,kw], y[N,Co,Ho,Wo] (NCHW / OIHW); bias is a vector
+ *     of N (GEMM) or Co (conv) elements added to every row / every spatial
+ *     position.  bias == NULL means no bias.
+ *   - Every tensor must be smaller than 2^31 bytes.
+ *   - Accumulation is fp32.  The bias is the first term of the sum (the
+ *     contribution of an extra k column of bias against a row of ones), the
+ *     activation runs in fp32, and the result is rounded once to the output
+ *     type (round to nearest, ties to even).
+ *   - Return value: BA_OK, or an error code below; nothing is launched when an
+ *     error is returned.  No exception crosses the ABI.
+ */
+#ifndef BIASACT_H
+#define BIASACT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element type codes (storage size: 4, 2, 2 bytes) */
+#define BA_F32 0u
+#define BA_F16 1u
+#define BA_BF16 2u
+
+/* dtypes argument: one 8-bit code per operand.
+ *   a   : A (GEMM) or x (conv)
+ *   b   : B (GEMM) or w (conv)      — must equal a
+ *   bias: bias element type         — fp32, or the same type as a (ignored when bias == NULL)
+ *   out : C (GEMM) or y (conv)      — fp32, fp16 or bf16 */
+#define BA_DTYPES(a, b, bias, out) \
+  ((uint32_t)(a) | ((uint32_t)(b) << 8) | ((uint32_t)(bias) << 16) | ((uint32_t)(out) << 24))
+
+/* activation codes */
+#define BA_ACT_NONE 0
+#define BA_ACT_RELU 1       /* z > 0 ? z : +0 */
+#define BA_ACT_LEAKY_RELU 2 /* z >= 0 ? z : alpha * z */
+#define BA_ACT_TANH 3       /* tanh(z) */
+
+/* status codes */
+#define BA_OK 0
+#define BA_ERR_INVALID 1     /* null pointer, negative dimension, bad act, stride/dilation < 1,
+                                pad < 0, empty conv output, workspace too small */
+#define BA_ERR_UNSUPPORTED 2 /* dtype combination, act for this op, tensor >= 2^31 bytes */
+#define BA_ERR_HIP 3         /* the HIP runtime refused the launch */
+
+/* C[M,N] = act(A[M,K] . B[K,N] + bias[N]).
+ * M, N, K >= 0 (M or N == 0: nothing to do; K == 0: C = act(bias)).
+ * alpha is read only for BA_ACT_LEAKY_RELU (fp32, as in the MatmulLeakyRelu
+ * spec).  Fast path: K and N multiples of 8 (fp16/bf16) or 4 (fp32) and
+ * 16-byte aligned pointers; other shapes are correct but slower. */
+int gemm_bias_act(const void* A, const void* B, const void* bias, void* C,
+                  int64_t M, int64_t N, int64_t K, uint32_t dtypes,
+                  int act, float alpha, hipStream_t stream);
+
+/* y = act(conv2d(x, w) + bias): cross-correlation, zero padding, groups = 1.
+ * strides = {sh, sw} >= 1, pads = {top, bottom, left, right} >= 0,
+ * dilations = {dh, dw} >= 1, all HOST pointers to int32.
+ *   Ho = floor((H + top + bottom - dh*(kh-1) - 1) / sh) + 1, likewise Wo;
+ * both must be >= 1.  N >= 0 (N == 0: nothing to do).  This entry point has
+ * no alpha, so BA_ACT_LEAKY_RELU returns BA_ERR_UNSUPPORTED. */
+int conv2d_bias_act(const void* x, const void* w, const void* bias, void* y,
+                    int64_t N, int64_t C, int64_t H, int64_t W, int64_t Co,
+                    int64_t kh, int64_t kw, const int32_t strides[2],
+                    const int32_t pads[4], const int32_t dilations[2],
+                    uint32_t dtypes, int act, hipStream_t stream);
+
+/* Two-kernel variants (the ablation of the fused path): kernel 1 runs the same
+ * main loop and stores the fp32 pre-activation (A.B + bias, or conv + bias) to
+ * `workspace` ([M,N], or NCHW for conv); kernel 2 reads it back and applies the
+ * activation and the output cast.  Results are bitwise identical to the fused
+ * entry points.  `workspace` is a caller-owned device buffer of at least
+ * *_workspace_size() bytes (BA_ERR_INVALID otherwise). */
+size_t gemm_bias_act_workspace_size(int64_t M, int64_t N);
+int gemm_bias_act_2k(const void* A, const void* B, const void* bias, void* C,
+                     int64_t M, int64_t N, int64_t K, uint32_t dtypes,
+                     int act, float alpha, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+size_t conv2d_bias_act_workspace_size(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Co,
+                                      int64_t kh, int64_t kw, const int32_t strides[2],
+                                      const int32_t pads[4], const int32_t dilations[2]);
+int conv2d_bias_act_2k(const void* x, const void* w, const void* bias, void* y,
+                       int64_t N, int64_t C, int64_t H, int64_t W, int64_t Co,
+                       int64_t kh, int64_t kw, const int32_t strides[2],
+                       const int32_t pads[4], const int32_t dilations[2],
+                       uint32_t dtypes, int act, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/* Introspection and tuning. */
+const char* biasact_status_string(int status);  /* static string, never NULL */
+int biasact_num_tile_configs(void);
+/* Describe tile config `id` ("BMxBN/waves_mxwaves_n") into buf (NUL-terminated,
+ * truncated to n bytes); BA_ERR_INVALID for an unknown id. */
+int biasact_tile_config_name(int id, char* buf, size_t n);
+/* Tile config the library picks for a GEMM / conv problem (no launch). */
+int biasact_gemm_tile_config(int64_t M, int64_t N, int64_t K, uint32_t dtypes);
+int biasact_conv_tile_config(int64_t N, int64_t Co, int64_t Ho, int64_t Wo, int64_t K_total,
+                             uint32_t dtypes);
+/* Process-wide override of the tile choice for tuning (-1 restores the
+ * automatic choice).  Not synchronised: set it before launching from other
+ * threads.  Returns BA_ERR_INVALID for an unknown id. */
+int biasact_force_tile_config(int id);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BIASACT_H */

@@ -1,0 +1,155 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+that include/biasact.h declares, and rejects invalid arguments before any HIP
+call (so every error path is reachable here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "biasact.h")
+
+ba = pytest.importorskip("conv_bias_activation_amd")
+L = ba.lib
+
+F32, F16, BF16 = 0, 1, 2
+
+
+def _dt(a, b, bias, out):
+    return a | (b << 8) | (bias << 16) | (out << 24)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for must in ("gemm_bias_act", "conv2d_bias_act", "gemm_bias_act_2k", "conv2d_bias_act_2k",
+                 "gemm_bias_act_workspace_size", "conv2d_bias_act_workspace_size",
+                 "biasact_status_string", "biasact_force_tile_config"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    for name in declared_functions():
+        assert hasattr(L, name), f"libbiasact.so does not export {name}"
+
+
+def test_status_strings():
+    assert L.biasact_status_string(0) == b"ok"
+    for s in (1, 2, 3, 99):
+        assert len(L.biasact_status_string(s)) > 0
+
+
+def test_tile_table_introspection():
+    n = ba.num_tile_configs()
+    assert n >= 5
+    names = [ba.tile_config_name(i) for i in range(n)]
+    assert names[0] == "256x256/2x2"
+    assert len(set(names)) == n
+    with pytest.raises(ValueError):
+        ba.tile_config_name(n)
+    assert 0 <= ba.gemm_tile_config(4096, 4096, 4096, _dt(BF16, BF16, F32, BF16)) < n
+    assert ba.gemm_tile_config(4096, 4096, 4096, _dt(BF16, BF16, F32, BF16)) == 0
+    ba.force_tile_config(3)
+    try:
+        assert ba.gemm_tile_config(4096, 4096, 4096, 0) == 3
+    finally:
+        ba.force_tile_config(-1)
+    with pytest.raises(ValueError):
+        ba.force_tile_config(n)
+
+
+def test_workspace_sizes():
+    assert L.gemm_bias_act_workspace_size(4096, 4096) == 4096 * 4096 * 4
+    assert L.gemm_bias_act_workspace_size(-1, 3) == 0
+    i32 = lambda *v: (ctypes.c_int32 * len(v))(*v)
+    n = L.conv2d_bias_act_workspace_size(8, 64, 56, 56, 64, 3, 3, i32(1, 1), i32(1, 1, 1, 1), i32(1, 1))
+    assert n == 8 * 64 * 56 * 56 * 4
+    assert L.conv2d_bias_act_workspace_size(1, 1, 2, 2, 1, 5, 5, i32(1, 1), i32(0, 0, 0, 0), i32(1, 1)) == 0
+
+
+# Fake (never dereferenced) device pointers: every call below fails validation
+# before anything is launched.
+P = ctypes.c_void_p(0x1000)
+NUL = ctypes.c_void_p(0)
+
+
+def gemm(A=P, B=P, bias=P, C=P, M=4, N=4, K=4, dt=_dt(F16, F16, F32, F32), act=2, alpha=0.1):
+    return L.gemm_bias_act(A, B, bias, C, M, N, K, dt, act, alpha, NUL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(A=NUL), 1), (dict(B=NUL), 1), (dict(C=NUL), 1),
+    (dict(M=-1), 1), (dict(N=-2), 1), (dict(K=-3), 1),
+    (dict(act=4), 1), (dict(act=-1), 1),
+    (dict(dt=_dt(F16, BF16, F32, F32)), 2),           # A and B differ
+    (dict(dt=_dt(3, 3, F32, F32)), 2),                # unknown type
+    (dict(dt=_dt(F16, F16, BF16, F32)), 2),           # bias neither f32 nor the input type
+    (dict(dt=_dt(F16, F16, F32, 7)), 2),              # unknown output type
+    (dict(M=1 << 20, K=1 << 11, dt=_dt(F32, F32, F32, F32)), 2),   # A is 2^33 bytes
+])
+def test_gemm_rejects(kw, code):
+    assert gemm(**kw) == code
+
+
+def test_gemm_empty_problem_is_ok_without_launch():
+    assert gemm(M=0) == 0 and gemm(N=0) == 0
+
+
+def test_gemm_2k_workspace_checks():
+    dt = _dt(BF16, BF16, F32, BF16)
+    assert L.gemm_bias_act_2k(P, P, P, P, 4, 4, 4, dt, 1, 0.0, NUL, 64, NUL) == 1
+    assert L.gemm_bias_act_2k(P, P, P, P, 4, 4, 4, dt, 1, 0.0, P, 63, NUL) == 1
+    assert L.gemm_bias_act_2k(P, P, P, P, 4, 4, 4, dt, 9, 0.0, P, 64, NUL) == 1
+
+
+def _i32(*v):
+    return (ctypes.c_int32 * len(v))(*v)
+
+
+def conv(x=P, w=P, bias=P, y=P, N=1, C=3, H=8, W=8, Co=4, kh=3, kw=3, st=(1, 1), pd=(1, 1, 1, 1),
+         dl=(1, 1), dt=_dt(F16, F16, F16, F16), act=3):
+    return L.conv2d_bias_act(x, w, bias, y, N, C, H, W, Co, kh, kw, _i32(*st), _i32(*pd), _i32(*dl),
+                             dt, act, NUL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=NUL), 1), (dict(w=NUL), 1), (dict(y=NUL), 1),
+    (dict(N=-1), 1), (dict(C=0), 1), (dict(H=0), 1), (dict(Co=0), 1), (dict(kh=0), 1),
+    (dict(st=(0, 1)), 1), (dict(st=(1, -2)), 1), (dict(dl=(0, 1)), 1),
+    (dict(pd=(-1, 0, 0, 0)), 1), (dict(pd=(0, 0, 0, -1)), 1),
+    (dict(H=2, W=2, pd=(0, 0, 0, 0)), 1),             # 3x3 filter on a 2x2 image: empty output
+    (dict(act=7), 1),
+    (dict(act=2), 2),                                 # no alpha on the conv entry point
+    (dict(dt=_dt(F16, F32, F16, F16)), 2),
+    (dict(N=64, C=1024, H=256, W=256, dt=_dt(F32, F32, F32, F32)), 2),   # x >= 2^31 bytes
+])
+def test_conv_rejects(kw, code):
+    assert conv(**kw) == code
+
+
+def test_conv_empty_batch_is_ok_without_launch():
+    assert conv(N=0) == 0
+
+
+def test_null_attribute_arrays_rejected():
+    c_null = ctypes.POINTER(ctypes.c_int32)()
+    rc = L.conv2d_bias_act(P, P, P, P, 1, 3, 8, 8, 4, 3, 3, c_null, _i32(1, 1, 1, 1), _i32(1, 1),
+                           _dt(F16, F16, F16, F16), 3, NUL)
+    assert rc == 1
+
+
+def test_python_binding_raises_value_error_on_bad_names():
+    with pytest.raises(ValueError):
+        ba.dtypes_code("f64", "f64", None, "f32")
+    with pytest.raises(ValueError):
+        ba._binding._act("gelu")
+    assert ba.conv_out_hw(224, 224, 7, 7, (2, 2), (3, 3, 3, 3), (1, 1)) == (112, 112)
+    assert ba.conv_out_hw(2, 2, 3, 3, (1, 1), (0, 0, 0, 0), (1, 1)) is None

@@ -1,0 +1,361 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle, on
+the same seeded input bits, element by element.
+
+Acceptance (oracle/compare.py): fp32 output with fp16/bf16 inputs within
+1e-3*(1+|ref|); fp32 inputs within 1e-5*(1+|ref|); fp16/bf16 output within one
+output ulp (taken at max(|ref|, fp32 accumulation-error bound)).  Where the
+result is exact in fp32 (small-integer operands, identity B) the test demands
+bit equality; fused vs two-kernel and run-to-run must be bitwise equal.
+"""
+import numpy as np
+import pytest
+
+import workloads as wl
+from gpu_helpers import (check, conv_reference, empty_out, gemm_reference, guard_intact, run_conv,
+                         run_gemm, to_dev, values_of, words_of)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def ba():
+    import conv_bias_activation_amd as m
+    m.force_tile_config(-1)
+    return m
+
+
+def _gcase(M, N, K, ti, to, tb, act, alpha=0.01, dist=("uniform", -1.0, 1.0)):
+    return wl.GemmCase(f"g{M}x{N}x{K}", M, N, K, ti, tb, to, act, alpha, dist, dist, dist)
+
+
+def _ccase(N, C, H, W, Co, kh, kw, st, pd, dl, ti, to, tb, act, dist=("uniform", -0.5, 0.5)):
+    return wl.ConvCase(f"c{N}x{C}x{H}x{W}", N, C, H, W, Co, kh, kw, st, pd, dl, ti, tb, to, act, 0.0,
+                       dist, dist, dist)
+
+
+def _report(tag, rep):
+    print(f"[{tag}] n={rep['n']} bad={rep['n_bad']} max_err/tol={rep['max_err_over_tol']:.3g}", flush=True)
+
+
+# ---------------------------------------------------------------------------
+# GEMM: small and ragged shapes, every element against the oracle
+# ---------------------------------------------------------------------------
+
+GEMM_SHAPES = [(1, 1, 1), (3, 5, 7), (64, 64, 64), (127, 129, 65), (200, 136, 72),
+               (256, 256, 64), (300, 520, 200), (33, 260, 1000), (520, 8, 24), (16, 1024, 40)]
+GEMM_TYPES = [("bf16", "bf16", "f32"), ("f16", "f32", "f32"), ("f16", "f16", "f16"),
+              ("bf16", "f32", "bf16"), ("f32", "f32", "f32"), ("f32", "bf16", "f32")]
+ACTS = ["none", "relu", "leaky_relu", "tanh"]
+
+
+@pytest.mark.parametrize("shape", GEMM_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("types", GEMM_TYPES, ids=lambda t: "-".join(t))
+def test_gemm_small_vs_oracle(ba, shape, types):
+    M, N, K = shape
+    ti, to, tb = types
+    s0 = sum(shape) + len(ti)
+    for j, act in enumerate((ACTS[s0 % 4], ACTS[(s0 + 1) % 4])):
+        case = _gcase(M, N, K, ti, to, tb, act, alpha=0.1)
+        inp = wl.gen_gemm(case, seed=11 + j)
+        y = values_of(run_gemm(case, inp), to)
+        ref, floor = gemm_reference(case, inp)
+        rep = check(y, ref, floor, case)
+        _report(f"gemm {shape} {types} {act}", rep)
+        assert rep["ok"], rep
+
+
+@pytest.mark.parametrize("tile", range(6))
+def test_gemm_every_tile_config(ba, tile):
+    ba.force_tile_config(tile)
+    try:
+        for ti, to in (("bf16", "bf16"), ("f16", "f32"), ("f32", "f32")):
+            case = _gcase(300, 520, 200, ti, to, "f32", "leaky_relu", 0.05)
+            inp = wl.gen_gemm(case, seed=3)
+            y = values_of(run_gemm(case, inp), to)
+            ref, floor = gemm_reference(case, inp)
+            rep = check(y, ref, floor, case)
+            _report(f"tile {tile} {ti}->{to}", rep)
+            assert rep["ok"], rep
+    finally:
+        ba.force_tile_config(-1)
+
+
+def test_gemm_no_bias_and_k_zero(ba):
+    case = wl.GemmCase("nobias", 70, 90, 130, "bf16", None, "f32", "relu")
+    inp = wl.gen_gemm(case, seed=5)
+    y = values_of(run_gemm(case, inp), "f32")
+    ref, _ = gemm_reference(case, inp)
+    assert check(y, ref, None, case)["ok"]
+    # K = 0: the sum is empty, C = act(bias)
+    case0 = _gcase(9, 40, 0, "f16", "f32", "f32", "leaky_relu", 0.25)
+    inp0 = wl.gen_gemm(case0, seed=6)
+    y0 = values_of(run_gemm(case0, inp0), "f32")
+    ref0, _ = gemm_reference(case0, inp0)
+    assert np.array_equal(y0, ref0.astype(np.float32).astype(np.float64))
+
+
+def test_gemm_empty_is_a_no_op(ba):
+    A = torch.zeros((0, 8), dtype=torch.bfloat16, device="cuda")
+    B = torch.zeros((8, 16), dtype=torch.bfloat16, device="cuda")
+    C = torch.zeros((0, 16), dtype=torch.bfloat16, device="cuda")
+    ba.gemm_bias_act(A, B, None, C, "relu")
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# exact cases: bit equality where fp32 arithmetic is exact
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("ti", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("shape", [(5, 7, 3), (64, 96, 128), (130, 70, 257)])
+def test_gemm_small_integers_bitwise(ba, ti, shape):
+    M, N, K = shape
+    for act, alpha in (("none", 0), ("relu", 0), ("leaky_relu", 0.25)):
+        case = wl.GemmCase("ints", M, N, K, ti, "f32", "f32", act, alpha,
+                           ("ints", -2, 2), ("ints", -2, 2), ("ints", -2, 2))
+        inp = wl.gen_gemm(case, seed=21)
+        y = values_of(run_gemm(case, inp), "f32")
+        ref, _ = gemm_reference(case, inp)
+        assert np.array_equal(y, ref), (act, np.abs(y - ref).max())
+
+
+def test_gemm_identity_b_bitwise(ba):
+    M, K = 96, 128
+    rng = np.random.default_rng(0)
+    a = rng.uniform(-4, 4, (M, K)).astype(np.float32)
+    bias = rng.uniform(-1, 1, K).astype(np.float32)
+    inp = {"A": wl.encode(a, "bf16"), "B": wl.encode(np.eye(K, dtype=np.float32), "bf16"),
+           "bias": wl.encode(bias, "f32")}
+    case = wl.GemmCase("eye", M, K, K, "bf16", "f32", "f32", "none")
+    y = values_of(run_gemm(case, inp), "f32")
+    a_bf = (inp["A"].astype(np.uint32) << 16).view(np.float32)
+    want = (bias.reshape(1, K) + a_bf).astype(np.float64)      # one fp32 rounding of bias + a
+    assert np.array_equal(y.reshape(M, K), want)
+
+
+def test_leaky_and_relu_invariants_bitwise(ba):
+    base = _gcase(130, 264, 96, "bf16", "f32", "f32", "none")
+    inp = wl.gen_gemm(base, seed=9)
+    y_none = values_of(run_gemm(base, inp), "f32").astype(np.float32)
+    for alpha in (0.001, 0.01, 0.25):
+        lk = _gcase(130, 264, 96, "bf16", "f32", "f32", "leaky_relu", alpha)
+        y = values_of(run_gemm(lk, inp), "f32").astype(np.float32)
+        want = np.where(y_none >= 0, y_none, np.float32(alpha) * y_none)
+        assert np.array_equal(y, want)
+    rl = _gcase(130, 264, 96, "bf16", "f32", "f32", "relu")
+    y = values_of(run_gemm(rl, inp), "f32").astype(np.float32)
+    assert np.array_equal(y, np.maximum(y_none, np.float32(0)))
+
+
+def test_tanh_sweep_through_k1_gemm(ba):
+    z = np.array([0.0, 1e-8, 1e-6, 1e-3, 0.1, 0.5, 1.0, 2.0, 5.0, 9.0, 10.0, 15.0, 20.0,
+                  88.0, 89.0, 1e4, 3.4e38], dtype=np.float32)
+    z = np.concatenate([z, -z, np.linspace(-12, 12, 4047, dtype=np.float32)])
+    M = z.size
+    inp = {"A": wl.encode(z.reshape(M, 1), "f32"), "B": wl.encode(np.ones((1, 1), np.float32), "f32"),
+           "bias": None}
+    case = wl.GemmCase("tanh", M, 1, 1, "f32", None, "f32", "tanh")
+    y = values_of(run_gemm(case, inp), "f32")
+    ref = np.tanh(z.astype(np.float64))
+    assert np.all(np.isfinite(y))
+    ulp32 = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(y - ref) <= np.maximum(4 * ulp32, 1e-30))
+    assert np.all(y[np.abs(z) >= 10] == np.sign(z[np.abs(z) >= 10]))
+    yf = y.astype(np.float32)
+    pos, neg = yf[:17], yf[17:34]
+    assert np.array_equal(neg, -pos)
+
+
+# ---------------------------------------------------------------------------
+# conv2d
+# ---------------------------------------------------------------------------
+
+CONV_SHAPES = [
+    # N, C, H, W, Co, kh, kw, strides, pads(t,b,l,r), dilations
+    (1, 1, 5, 6, 1, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1)),
+    (2, 3, 9, 7, 4, 3, 2, (2, 1), (1, 0, 2, 1), (1, 2)),
+    (1, 5, 11, 13, 3, 5, 5, (3, 2), (2, 2, 0, 3), (1, 1)),
+    (3, 16, 8, 8, 70, 1, 1, (2, 2), (0, 0, 0, 0), (1, 1)),
+    (2, 12, 12, 10, 33, 3, 3, (1, 1), (2, 2, 2, 2), (2, 3)),
+    (1, 3, 31, 29, 64, 7, 7, (2, 2), (3, 3, 3, 3), (1, 1)),
+    (2, 64, 14, 14, 64, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1)),
+    (1, 40, 9, 9, 136, 3, 3, (1, 1), (2, 2, 2, 2), (2, 2)),
+]
+CONV_TYPES = [("f16", "f16", "f16"), ("bf16", "bf16", "bf16"), ("f32", "f32", "f32"),
+              ("f16", "f32", "f32"), ("bf16", "bf16", "f32")]
+
+
+@pytest.mark.parametrize("shape", CONV_SHAPES, ids=lambda s: "x".join(map(str, s[:7])))
+@pytest.mark.parametrize("types", CONV_TYPES, ids=lambda t: "-".join(t))
+def test_conv_small_vs_oracle(ba, shape, types):
+    N, C, H, W, Co, kh, kw, st, pd, dl = shape
+    ti, to, tb = types
+    for j, act in enumerate(("tanh", "none", "relu")):
+        case = _ccase(N, C, H, W, Co, kh, kw, st, pd, dl, ti, to, tb, act)
+        inp = wl.gen_conv(case, seed=31 + j)
+        y = values_of(run_conv(case, inp), to)
+        ref, floor = conv_reference(case, inp)
+        rep = check(y, ref, floor, case)
+        _report(f"conv {shape} {types} {act}", rep)
+        assert rep["ok"], rep
+
+
+@pytest.mark.parametrize("tile", range(6))
+def test_conv_every_tile_config(ba, tile):
+    ba.force_tile_config(tile)
+    try:
+        for ti, to in (("f16", "f16"), ("f32", "f32")):
+            case = _ccase(2, 20, 15, 17, 75, 3, 3, (1, 2), (1, 0, 1, 2), (2, 1), ti, to, ti, "tanh")
+            inp = wl.gen_conv(case, seed=4)
+            y = values_of(run_conv(case, inp), to)
+            ref, floor = conv_reference(case, inp)
+            rep = check(y, ref, floor, case)
+            _report(f"conv tile {tile} {ti}", rep)
+            assert rep["ok"], rep
+    finally:
+        ba.force_tile_config(-1)
+
+
+def test_conv_no_bias(ba):
+    case = _ccase(2, 8, 10, 10, 16, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1), "bf16", "f32", None, "none")
+    inp = wl.gen_conv(case, seed=2)
+    y = values_of(run_conv(case, inp), "f32")
+    ref, _ = conv_reference(case, inp)
+    assert check(y, ref, None, case)["ok"]
+
+
+def test_conv_1x1_identity_weights_bitwise(ba):
+    N, C, H, W = 2, 32, 6, 10
+    rng = np.random.default_rng(1)
+    x = rng.uniform(-2, 2, (N, C, H, W)).astype(np.float32)
+    bias = rng.uniform(-1, 1, C).astype(np.float32)
+    inp = {"x": wl.encode(x, "f16"), "w": wl.encode(np.eye(C, dtype=np.float32).reshape(C, C, 1, 1), "f16"),
+           "bias": wl.encode(bias, "f32")}
+    case = wl.ConvCase("eye", N, C, H, W, C, 1, 1, (1, 1), (0, 0, 0, 0), (1, 1), "f16", "f32", "f32", "none")
+    y = values_of(run_conv(case, inp), "f32")
+    xf = inp["x"].view(np.float16).astype(np.float32)
+    want = (xf + bias.reshape(1, C, 1, 1)).astype(np.float64)
+    assert np.array_equal(y.reshape(N, C, H, W), want)
+
+
+# ---------------------------------------------------------------------------
+# two-kernel path, determinism, guard bands
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("types", GEMM_TYPES, ids=lambda t: "-".join(t))
+def test_gemm_two_kernel_bitwise_equal_fused(ba, types):
+    ti, to, tb = types
+    for act in ACTS:
+        case = _gcase(257, 264, 136, ti, to, tb, act, 0.02)
+        inp = wl.gen_gemm(case, seed=8)
+        a = words_of(run_gemm(case, inp, "fused"), to)
+        b = words_of(run_gemm(case, inp, "2k"), to)
+        assert np.array_equal(a, b), act
+
+
+@pytest.mark.parametrize("types", CONV_TYPES, ids=lambda t: "-".join(t))
+def test_conv_two_kernel_bitwise_equal_fused(ba, types):
+    ti, to, tb = types
+    for act in ("tanh", "relu", "none"):
+        case = _ccase(2, 24, 13, 11, 40, 3, 3, (2, 1), (1, 1, 0, 2), (1, 2), ti, to, tb, act)
+        inp = wl.gen_conv(case, seed=12)
+        a = words_of(run_conv(case, inp, "fused"), to)
+        b = words_of(run_conv(case, inp, "2k"), to)
+        assert np.array_equal(a, b), act
+
+
+def test_run_to_run_bitwise_determinism(ba):
+    case = _gcase(520, 384, 640, "bf16", "bf16", "f32", "tanh")
+    inp = wl.gen_gemm(case, seed=1)
+    first = words_of(run_gemm(case, inp), "bf16")
+    for _ in range(3):
+        assert np.array_equal(words_of(run_gemm(case, inp), "bf16"), first)
+    cc = _ccase(2, 16, 20, 20, 48, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1), "f16", "f16", "f16", "tanh")
+    cinp = wl.gen_conv(cc, seed=1)
+    cfirst = words_of(run_conv(cc, cinp), "f16")
+    for _ in range(3):
+        assert np.array_equal(words_of(run_conv(cc, cinp), "f16"), cfirst)
+
+
+@pytest.mark.parametrize("to", ["f32", "bf16"])
+def test_guard_bands_untouched(ba, to):
+    canary = 0x7FC01234 if to == "f32" else 0x7FC1
+    guard = 256
+    for M, N, K in ((131, 77, 50), (300, 260, 72), (64, 128, 64)):
+        case = _gcase(M, N, K, "bf16", to, "f32", "relu")
+        inp = wl.gen_gemm(case, seed=2)
+        C, buf = empty_out((M, N), to, guard, canary)
+        run_gemm(case, inp, out=C)
+        assert guard_intact(buf, guard, to, canary), (M, N, K)
+        ref, floor = gemm_reference(case, inp)
+        assert check(values_of(C, to), ref, floor, case)["ok"]
+    cc = _ccase(3, 5, 9, 11, 70, 3, 3, (2, 2), (1, 1, 1, 1), (1, 1), "bf16", to, "bf16", "tanh")
+    cinp = wl.gen_conv(cc, seed=3)
+    Ho, Wo = cc.out_hw()
+    y, buf = empty_out((3, 70, Ho, Wo), to, guard, canary)
+    run_conv(cc, cinp, out=y)
+    assert guard_intact(buf, guard, to, canary)
+
+
+def test_python_binding_rejects_bad_tensors(ba):
+    A = torch.zeros((4, 8), dtype=torch.bfloat16, device="cuda")
+    B = torch.zeros((8, 4), dtype=torch.float16, device="cuda")
+    C = torch.zeros((4, 4), dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError):
+        ba.gemm_bias_act(A, B, None, C, "relu")             # A and B types differ
+    with pytest.raises(ValueError):
+        ba.gemm_bias_act(A, A.t(), None, C, "relu")          # non-contiguous
+    x = torch.zeros((1, 2, 5, 5), dtype=torch.float16, device="cuda")
+    w = torch.zeros((3, 2, 3, 3), dtype=torch.float16, device="cuda")
+    y = torch.zeros((1, 3, 3, 3), dtype=torch.float16, device="cuda")
+    with pytest.raises(ValueError):
+        ba.conv2d_bias_act(x, w, None, y, act="leaky_relu")
+
+
+# ---------------------------------------------------------------------------
+# the named workloads at full size (sampled outputs; full output for the
+# small MatmulLeakyRelu spec case)
+# ---------------------------------------------------------------------------
+
+NAMED = list(wl.CASES)
+
+
+@pytest.mark.parametrize("name", NAMED)
+def test_named_workload_full_size(ba, name):
+    case = wl.CASES[name]
+    is_gemm = isinstance(case, wl.GemmCase)
+    for seed in (0, 1):
+        inp = wl.gen_gemm(case, seed) if is_gemm else wl.gen_conv(case, seed)
+        y_t = run_gemm(case, inp) if is_gemm else run_conv(case, inp)
+        total = y_t.numel()
+        small = name == "gemm_leaky_1024x640x256_f16"
+        idx = None if small else wl.sample_indices(total, 6000, seed)
+        ref, floor = (gemm_reference if is_gemm else conv_reference)(case, inp, idx)
+        vals = values_of(y_t, case.out_dtype)
+        got = vals if idx is None else vals[idx]
+        rep = check(got, ref, floor, case)
+        _report(f"{name} seed {seed}", rep)
+        assert rep["ok"], rep
+        assert np.all(np.isfinite(vals))
+        # the two-kernel path gives the same bits at full size
+        if seed == 0:
+            y2 = run_gemm(case, inp, "2k") if is_gemm else run_conv(case, inp, "2k")
+            assert np.array_equal(words_of(y2, case.out_dtype), words_of(y_t, case.out_dtype))
+        del y_t
+        torch.cuda.empty_cache()
+
+
+def test_matmul_leakyrelu_sample_acceptance_rule(ba):
+    """The sample's own check: fp32 matmul of the fp16 operands plus bias,
+    LeakyReLU by torch.where, allclose with rtol = atol = 1e-3."""
+    case = wl.CASES["gemm_leaky_1024x640x256_f16"]
+    inp = wl.gen_gemm(case, 0)
+    c = run_gemm(case, inp).float().cpu()
+    a = torch.from_numpy(inp["A"].view(np.float16).astype(np.float32))
+    b = torch.from_numpy(inp["B"].view(np.float16).astype(np.float32))
+    bias = torch.from_numpy(inp["bias"].view(np.float32))
+    alpha = float(np.float32(case.alpha))
+    mm = a @ b + bias
+    assert torch.allclose(c, torch.where(mm >= 0, mm, mm * alpha), rtol=1e-3, atol=1e-3)
