@@ -8,12 +8,16 @@ The rule:
     MatmulLeakyRelu sample of "CANN pyasc MatmulLeakyRelu 融合算子实战" runs
     in its 编译执行 section);
   * fp32 output, fp32 inputs:        |y - ref| <= 1e-5 * (1 + |ref|);
-  * fp16 / bf16 output:              |y - ref| <= 1 ulp of the output format,
-    the ulp taken at max(|ref|, E) where E bounds the fp32 accumulation error
-    of the device (Higham: gamma_K * (sum_k |a_k b_k| + |bias|), with
-    gamma_K = K u / (1 - K u), u = 2^-24).  Without E a value whose exact
-    result is ~1e-9 would demand an fp32 sum exact to far below fp32's own
-    rounding error.
+  * fp16 / bf16 output:              |y - ref| <= ulp_out(ref) + E, one ulp
+    of the output format at |ref| plus E, a bound on the device's fp32
+    accumulation error (Higham: gamma_n * (sum_k |a_k b_k| + |bias|) with
+    n = K + 1 terms, gamma_n = n u / (1 - n u), u = 2^-24).  The device
+    result is round(z) with |z - ref| <= E, so |y - ref| <= ulp/2 + E; without
+    E an output whose exact value is tiny next to sum |a_k b_k| would demand
+    an fp32 sum far more accurate than fp32 itself.
+  * fp32 output with an error bound E given (used only for shapes outside
+    the named workloads, e.g. fp32 inputs with K > 512, where fp32 summation
+    error alone exceeds 1e-5 * (1 + |ref|)): max(rule, E).
 """
 from __future__ import annotations
 
@@ -46,13 +50,11 @@ def gamma(K: int, u: float = 2.0 ** -24) -> float:
 def tolerance(ref: np.ndarray, in_dtype: str, out_dtype: str,
               err_floor: Optional[np.ndarray] = None) -> np.ndarray:
     ref = np.asarray(ref, dtype=np.float64)
+    e = 0.0 if err_floor is None else np.asarray(err_floor, dtype=np.float64)
     if out_dtype == "f32":
         rel = 1e-5 if in_dtype == "f32" else 1e-3
-        return rel * (1.0 + np.abs(ref))
-    mag = np.abs(ref)
-    if err_floor is not None:
-        mag = np.maximum(mag, np.asarray(err_floor, dtype=np.float64))
-    return ulp(mag, out_dtype)
+        return np.maximum(rel * (1.0 + np.abs(ref)), e)
+    return ulp(np.abs(ref), out_dtype) + e
 
 
 def decode_out(words: np.ndarray, out_dtype: str) -> np.ndarray:
@@ -87,7 +89,7 @@ def compare(y: np.ndarray, ref: np.ndarray, in_dtype: str, out_dtype: str,
         "n_nonfinite": int((~np.isfinite(y)).sum()),
     }
     if floor is not None:
-        rep["n_floor_used"] = int((floor > np.abs(ref)).sum())
+        rep["max_floor"] = float(floor.max()) if floor.size else 0.0
     if n_bad:
         k = int(np.argmax(np.where(bad, err / np.where(tol > 0, tol, 1e-300), -1)))
         rep["worst"] = {"index": k, "y": float(y[k]), "ref": float(ref[k]), "tol": float(tol[k])}

@@ -371,7 +371,10 @@ def test_compare_flags_errors():
     # 16-bit output: one ulp passes, two fail
     assert compare(np.array([1.0 + 2 ** -7]), np.array([1.0]), "bf16", "bf16")["ok"]
     assert not compare(np.array([1.0 + 2 ** -6]), np.array([1.0]), "bf16", "bf16")["ok"]
-    assert (tolerance(np.array([0.0]), "bf16", "bf16", np.array([1.0])) == 2.0 ** -7).all()
+    # 16-bit output: one ulp at |ref| plus the accumulation-error bound
+    assert tolerance(np.array([1.0]), "bf16", "bf16", np.array([0.5]))[0] == 2.0 ** -7 + 0.5
+    assert tolerance(np.array([2.0]), "f32", "f32", np.array([1.0]))[0] == 1.0
+    assert abs(tolerance(np.array([2.0]), "f32", "f32")[0] - 3e-5) < 1e-18
 
 
 def test_generator_rounding_and_determinism():
