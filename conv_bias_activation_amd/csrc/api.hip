@@ -175,16 +175,18 @@ int biasact_tile_config_name(int id, char* buf, size_t n) {
 }
 
 int biasact_gemm_tile_config(int64_t M, int64_t N, int64_t K, uint32_t dtypes) {
-  const int f = forced_tile();
-  if (f >= 0) return f;
-  return select_gemm_tile(M, N, K, (int)(dtypes & 0xffu));
+  // the choice gemm_bias_act makes for 16-byte aligned operands
+  GemmPlan p;
+  static const char dummy[16] __attribute__((aligned(16))) = {0};
+  if (plan_gemm(dummy, dummy, nullptr, dummy, M, N, K, dtypes, BA_ACT_NONE, &p)) return -1;
+  return p.tile;
 }
 
 int biasact_conv_tile_config(int64_t N, int64_t Co, int64_t Ho, int64_t Wo, int64_t K_total,
                              uint32_t dtypes) {
-  const int f = forced_tile();
-  if (f >= 0) return f;
-  return select_conv_tile(N, Co, Ho, Wo, K_total, (int)(dtypes & 0xffu));
+  int f = forced_tile();
+  if (f < 0) f = select_conv_tile(N, Co, Ho, Wo, K_total, (int)(dtypes & 0xffu));
+  return f == 6 ? 0 : f;
 }
 
 int biasact_force_tile_config(int id) {

@@ -1,0 +1,62 @@
+// epilogue.hpp — bias fetch and output stores shared by the biasact kernels.
+#pragma once
+
+#include "device_common.hpp"
+
+namespace biasact {
+
+// Per-element bias fetch (fp32, fp16 or bf16 storage), exact widening.
+__device__ __forceinline__ float load_bias(__amdgpu_buffer_rsrc_t r, int dt, uint32_t idx) {
+  if (dt == DT_F32) return __uint_as_float(ld_b32(r, idx * 4));
+  const uint32_t w = ld_b16(r, idx * 2);
+  return dt == DT_F16 ? widen<DT_F16>(w) : widen<DT_BF16>(w);
+}
+
+// NV bias values bias[idx[v]] (0 where idx[v] >= lim or without bias), all
+// loads issued before the first use; the element-type branch is uniform.
+template <int NV>
+__device__ __forceinline__ void load_bias_vec(const void* bias, uint32_t nbytes, int dt,
+                                              const uint32_t (&idx)[NV], uint32_t lim,
+                                              float (&out)[NV]) {
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(bias, nbytes);
+  if (dt == DT_F32) {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) out[v] = __uint_as_float(ld_b32(r, idx[v] < lim ? idx[v] * 4u : kOOB));
+  } else if (dt == DT_F16) {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) out[v] = widen<DT_F16>(ld_b16(r, idx[v] < lim ? idx[v] * 2u : kOOB));
+  } else if (dt == DT_BF16) {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) out[v] = widen<DT_BF16>(ld_b16(r, idx[v] < lim ? idx[v] * 2u : kOOB));
+  } else {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) out[v] = 0.0f;
+  }
+}
+
+// Store four consecutive outputs (one accumulator register group).
+template <int DTO>
+__device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t r, uint32_t off_elems, bool ok,
+                                       float v0, float v1, float v2, float v3) {
+  const uint32_t off = ok ? off_elems * Elem<DTO>::bytes : kOOB;
+  if constexpr (DTO == DT_F32) {
+    u32x4 o;
+    o.x = __float_as_uint(v0); o.y = __float_as_uint(v1);
+    o.z = __float_as_uint(v2); o.w = __float_as_uint(v3);
+    st_b128(r, off, o);
+  } else {
+    u32x2 o;
+    o.x = narrow<DTO>(v0) | (narrow<DTO>(v1) << 16);
+    o.y = narrow<DTO>(v2) | (narrow<DTO>(v3) << 16);
+    st_b64(r, off, o);
+  }
+}
+
+template <int DTO>
+__device__ __forceinline__ void store1(__amdgpu_buffer_rsrc_t r, uint32_t off_elems, bool ok, float v) {
+  const uint32_t off = ok ? off_elems * Elem<DTO>::bytes : kOOB;
+  if constexpr (DTO == DT_F32) st_b32(r, off, __float_as_uint(v));
+  else st_b16(r, off, (uint16_t)narrow<DTO>(v));
+}
+
+}  // namespace biasact

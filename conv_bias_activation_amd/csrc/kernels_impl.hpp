@@ -5,42 +5,12 @@
 // element type.
 #pragma once
 
+#include "epilogue.hpp"
+#include "gemm_pp.hpp"
 #include "launch.hpp"
 #include "mfma_core.hpp"
 
 namespace biasact {
-
-// Per-element bias fetch (fp32, fp16 or bf16 storage), exact widening.
-__device__ __forceinline__ float load_bias(__amdgpu_buffer_rsrc_t r, int dt, uint32_t idx) {
-  if (dt == DT_F32) return __uint_as_float(ld_b32(r, idx * 4));
-  const uint32_t w = ld_b16(r, idx * 2);
-  return dt == DT_F16 ? widen<DT_F16>(w) : widen<DT_BF16>(w);
-}
-
-// Store four consecutive outputs (one accumulator register group).
-template <int DTO>
-__device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t r, uint32_t off_elems, bool ok,
-                                       float v0, float v1, float v2, float v3) {
-  const uint32_t off = ok ? off_elems * Elem<DTO>::bytes : kOOB;
-  if constexpr (DTO == DT_F32) {
-    u32x4 o;
-    o.x = __float_as_uint(v0); o.y = __float_as_uint(v1);
-    o.z = __float_as_uint(v2); o.w = __float_as_uint(v3);
-    st_b128(r, off, o);
-  } else {
-    u32x2 o;
-    o.x = narrow<DTO>(v0) | (narrow<DTO>(v1) << 16);
-    o.y = narrow<DTO>(v2) | (narrow<DTO>(v3) << 16);
-    st_b64(r, off, o);
-  }
-}
-
-template <int DTO>
-__device__ __forceinline__ void store1(__amdgpu_buffer_rsrc_t r, uint32_t off_elems, bool ok, float v) {
-  const uint32_t off = ok ? off_elems * Elem<DTO>::bytes : kOOB;
-  if constexpr (DTO == DT_F32) st_b32(r, off, __float_as_uint(v));
-  else st_b16(r, off, (uint16_t)narrow<DTO>(v));
-}
 
 // ---------------------------------------------------------------------------
 // C[M,N] = act(A[M,K] . B[K,N] + bias[N])   ([MLR] 概述 / 样例规格;
@@ -61,15 +31,19 @@ __global__ __launch_bounds__(TL::threads, 1) void gemm_bias_act_kernel(GemmArgs 
   // accumulator starts at the bias (the extra reduction term)
   f32x16 acc[TL::SN][TL::SM];
   {
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.bias, a.bias_bytes);
+    uint32_t idx[TL::SN * 16];
+    float bv[TL::SN * 16];
+#pragma unroll
+    for (int si = 0; si < TL::SN; ++si)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        idx[si * 16 + r] = n0 + wave_n * TL::WTN + si * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+    load_bias_vec<TL::SN * 16>(a.bias, a.bias_bytes, a.bias_dt, idx, a.N, bv);
 #pragma unroll
     for (int si = 0; si < TL::SN; ++si) {
       f32x16 b;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const uint32_t n = n0 + wave_n * TL::WTN + si * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        b[r] = (a.bias_dt >= 0 && n < a.N) ? load_bias(rb, a.bias_dt, n) : 0.0f;
-      }
+      for (int r = 0; r < 16; ++r) b[r] = bv[si * 16 + r];
 #pragma unroll
       for (int sj = 0; sj < TL::SM; ++sj) acc[si][sj] = b;
     }
@@ -129,16 +103,17 @@ __global__ __launch_bounds__(TL::threads, 1) void conv_bias_act_kernel(ConvArgs 
 
   f32x16 acc[TL::SN][TL::SM];
   {
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.bias, a.bias_bytes);
+    uint32_t idx[TL::SM];
+    float bv[TL::SM];
 #pragma unroll
-    for (int sj = 0; sj < TL::SM; ++sj) {
-      const uint32_t co = m0 + wave_m * TL::WTM + sj * 32 + lrow;
-      const float bv = (a.bias_dt >= 0 && co < G.Co) ? load_bias(rb, a.bias_dt, co) : 0.0f;
+    for (int sj = 0; sj < TL::SM; ++sj) idx[sj] = m0 + wave_m * TL::WTM + sj * 32 + lrow;
+    load_bias_vec<TL::SM>(a.bias, a.bias_bytes, a.bias_dt, idx, G.Co, bv);
+#pragma unroll
+    for (int sj = 0; sj < TL::SM; ++sj)
 #pragma unroll
       for (int si = 0; si < TL::SN; ++si)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[si][sj][r] = bv;
-    }
+        for (int r = 0; r < 16; ++r) acc[si][sj][r] = bv[sj];
   }
 
   DenseRowLoader<DTI, TL> la;
@@ -251,6 +226,15 @@ inline int launch_gemm_tile(int tile, const GemmArgs& a, hipStream_t s) {
     case 3: launch_gemm_t<DTI, DTO, T3>(a, s); return 0;
     case 4: launch_gemm_t<DTI, DTO, T4>(a, s); return 0;
     case 5: launch_gemm_t<DTI, DTO, T5>(a, s); return 0;
+    case 6:
+      if constexpr (DTI != DT_F32) {
+        if (a.vec_a && a.vec_b && a.vec_c) {
+          launch_gemm_pp<DTI, DTO>(a, s);
+          return 0;
+        }
+      }
+      launch_gemm_t<DTI, DTO, T0>(a, s);
+      return 0;
     default: return -1;
   }
 }

@@ -103,6 +103,10 @@ int plan_gemm(const void* A, const void* B, const void* bias, const void* C, int
   p->empty = M == 0 || N == 0;
   int tile = forced_tile();
   if (tile < 0 || tile >= kNumTileConfigs) tile = select_gemm_tile(M, N, K, dti);
+  // the ping-pong kernel takes 16-bit operands with 16-byte aligned rows
+  const bool pp_ok = dti != kF32 && p->vec_a && p->vec_b && p->vec_c;
+  if (tile == 0 && pp_ok && forced_tile() < 0) tile = 6;
+  if (tile == 6 && !pp_ok) tile = 0;
   p->tile = tile;
   p->tiles_m = (uint32_t)ceil_div(M, kTiles[tile].bm);
   p->tiles_n = (uint32_t)ceil_div(N, kTiles[tile].bn);
@@ -156,6 +160,7 @@ int plan_conv(const void* x, const void* w, const void* bias, const void* y, int
   p->empty = N == 0;
   int tile = forced_tile();
   if (tile < 0 || tile >= kNumTileConfigs) tile = select_conv_tile(N, Co, Ho, Wo, K, dti);
+  if (tile == 6) tile = 0;                              // no ping-pong conv kernel
   p->tile = tile;
   p->tiles_m = (uint32_t)ceil_div(Co, kTiles[tile].bm);
   p->tiles_n = (uint32_t)ceil_div(P, kTiles[tile].bn);

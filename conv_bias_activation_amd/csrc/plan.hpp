@@ -20,6 +20,7 @@ constexpr TileShapeDesc kTiles[] = {
     {3, 64, 128, 2, 2},
     {4, 64, 256, 1, 4},
     {5, 64, 64, 2, 2},
+    {6, 256, 256, 2, 4},   // 8-wave ping-pong kernel: aligned 16-bit GEMMs only (else as 0)
 };
 constexpr int kNumTileConfigs = (int)(sizeof(kTiles) / sizeof(kTiles[0]));
 

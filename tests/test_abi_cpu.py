@@ -56,7 +56,8 @@ def test_tile_table_introspection():
     with pytest.raises(ValueError):
         ba.tile_config_name(n)
     assert 0 <= ba.gemm_tile_config(4096, 4096, 4096, _dt(BF16, BF16, F32, BF16)) < n
-    assert ba.gemm_tile_config(4096, 4096, 4096, _dt(BF16, BF16, F32, BF16)) == 0
+    assert ba.gemm_tile_config(4096, 4096, 4096, _dt(BF16, BF16, F32, BF16)) == 6   # ping-pong kernel
+    assert ba.gemm_tile_config(4096, 4096, 4096, _dt(F32, F32, F32, F32)) == 0
     ba.force_tile_config(3)
     try:
         assert ba.gemm_tile_config(4096, 4096, 4096, 0) == 3

@@ -66,12 +66,14 @@ def test_gemm_small_vs_oracle(ba, shape, types):
         assert rep["ok"], rep
 
 
-@pytest.mark.parametrize("tile", range(6))
+@pytest.mark.parametrize("tile", range(7))
 def test_gemm_every_tile_config(ba, tile):
     ba.force_tile_config(tile)
     try:
-        for ti, to in (("bf16", "bf16"), ("f16", "f32"), ("f32", "f32")):
-            case = _gcase(300, 520, 200, ti, to, "f32", "leaky_relu", 0.05)
+        for ti, to, (M, N, K) in (("bf16", "bf16", (300, 520, 200)), ("f16", "f32", (300, 520, 200)),
+                                  ("f32", "f32", (300, 520, 200)), ("bf16", "f16", (513, 264, 1032)),
+                                  ("f16", "bf16", (40, 1000, 72))):
+            case = _gcase(M, N, K, ti, to, "f32", "leaky_relu", 0.05)
             inp = wl.gen_gemm(case, seed=3)
             y = values_of(run_gemm(case, inp), to)
             ref, floor = gemm_reference(case, inp)
@@ -210,7 +212,7 @@ def test_conv_small_vs_oracle(ba, shape, types):
         assert rep["ok"], rep
 
 
-@pytest.mark.parametrize("tile", range(6))
+@pytest.mark.parametrize("tile", range(7))
 def test_conv_every_tile_config(ba, tile):
     ba.force_tile_config(tile)
     try:
