@@ -31,17 +31,50 @@ sys.path.insert(0, ROOT)
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}   # dense MFMA, MI355X datasheet
 PEAK_HBM_GBS = 8000.0
 
+# Sources that define the headline kernel; the HBM-traffic record in profiles/
+# carries their hash and is reported only while they are unchanged.
+KERNEL_SOURCES = ["gemm_pp.hpp", "epilogue.hpp", "device_common.hpp", "mfma_core.hpp", "launch.hpp"]
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gemm_relu_4096_bf16_hbm_traffic.json")
+
+
+def kernel_fingerprint() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "conv_bias_activation_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed counter record (FETCH_SIZE and
+    WRITE_SIZE scaled by a plain copy of known size), or None if absent or
+    taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("workload") != workload or rec.get("kernel_sources_sha256") != kernel_fingerprint():
+        return None
+    return rec.get("bytes_per_launch")
+
 
 def _parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="gemm_relu_4096_bf16")
     ap.add_argument("--no-others", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle sample time")
     ap.add_argument("--tile", type=int, default=-1, help="force a tile config (tuning)")
+    ap.add_argument("--fingerprint", action="store_true", help="print the headline kernel's source hash")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a device copy of 256 MiB (read 256 MiB + write 256 MiB) --steps "
+                         "times; its FETCH_SIZE / WRITE_SIZE counters scale the kernel's counters "
+                         "to bytes")
     return ap.parse_args()
 
 
@@ -148,12 +181,25 @@ def cpu_baseline(case, target_s):
 
 def main():
     args = _parse()
+    if args.fingerprint:
+        print(kernel_fingerprint())
+        return
     if args.gpus != 1:
         print(json.dumps({"error": f"--gpus {args.gpus}: this benchmark runs on exactly one GPU; "
                                    "the fused kernel shards by rows/columns with no exchange, so "
                                    "N GPUs would each run this same step on 1/N of the rows"}))
         sys.exit(2)
     import torch
+    if args.calibrate_copy:
+        n = 256 << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": n, "calibrate_copy_bytes_written": n,
+                          "launches": args.steps}), flush=True)
+        return
     import conv_bias_activation_amd as ba
     import workloads as wl
 
@@ -193,7 +239,7 @@ def main():
         "config": cfg,
         "frac_of_peak": round(tflops / peak, 4),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(tflops / peak, 4), "traffic": None,
+                     "frac": round(tflops / peak, 4), "traffic": measured_traffic(case.name),
                      "kernel": "gemm_bias_act_kernel", "per_launch_flops": case.flops,
                      "mean_launch_ms": round(ms, 5)},
         "wall_s_timed": round(wall, 3),

@@ -25,9 +25,9 @@ LIB = os.path.join(PKG, "libbiasact.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["api.hip", "act_cast.hip",
-               "gemm_bf16.hip", "gemm_f16.hip", "gemm_f32.hip",
-               "conv_bf16.hip", "conv_f16.hip", "conv_f32.hip"]
+_TYPES = ("f32", "f16", "bf16")
+HIP_SOURCES = ["api.hip", "act_cast.hip", "dispatch.hip"] + [
+    f"{op}_{ti}_{to}.hip" for op in ("gemm", "conv") for ti in _TYPES for to in _TYPES]
 CPP_SOURCES = ["plan.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC, "-Wall",

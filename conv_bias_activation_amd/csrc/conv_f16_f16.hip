@@ -1,0 +1,8 @@
+// conv_f16_f16.hip — fused implicit-GEMM conv2d + bias + activation kernels, f16 operands, f16 output.
+#include "kernels_impl.hpp"
+
+namespace biasact {
+int launch_conv_f16_f16(int tile, const ConvArgs& a, hipStream_t s) {
+  return launch_conv_tile<DT_F16, DT_F16>(tile, a, s);
+}
+}  // namespace biasact

@@ -5,29 +5,31 @@
 //   fused_matmul_relu: the intermediate never leaves the chip, one HBM read of
 //   the operands and one write of C)
 //
-// Workgroup: 512 threads = 8 waves, output tile 256 (m) x 256 (n), k-tile 64.
+// Workgroup: 512 threads = 8 waves, output tile 256 (m) x 256 (n), k-tile 32.
 // Waves 0-3 form cluster 0 and waves 4-7 cluster 1; wave w owns the 128 (m) x
 // 64 (n) sub-tile at m = 128*(w/4), n = 64*(w%4), i.e. 4 x 2 accumulator
 // blocks of 32x32 (128 fp32 values per lane).  Each SIMD runs one wave of
 // each cluster.  The clusters alternate phases between workgroup barriers:
-// while one wave of a SIMD multiplies (16 MFMAs, one half k-tile, already in
-// registers), the other reads its next fragments from LDS and issues global
-// loads, so the matrix core is fed without waiting on LDS latency.
+// while one wave of a SIMD multiplies one k-tile (16 MFMAs from registers),
+// the other reads its fragments of the next k-tile from LDS and, between
+// those reads, issues its global loads of the k-tile three ahead, so the LDS
+// pipeline (fragment reads) and the texture path (global loads) work side by
+// side under the matrix-core work of the partner wave.
 //
 // Operands reach LDS without passing through registers: 16-byte buffer loads
 // with the LDS-destination bit write each lane's 16 bytes at base + 16*lane
 // (out-of-range lanes write zeros, which covers ragged M, N and the K tail).
 // The swizzle is applied by choosing which global chunk each lane fetches.
-//   A stage: 256 rows (m) x 64 k = 128 B per row, 16-byte chunk c of row r at
-//            slot c ^ (r & 7) ^ ((r >> 3) & 1); fragments via ds_read_b128.
-//   B stage: 64 rows (k) x 256 n = 512 B per row (n contiguous, as in memory),
+//   A stage: 256 rows (m) x 32 k = 64 B per row, 16-byte chunk c of row r at
+//            slot c ^ ((r >> 2) & 3); fragments via ds_read_b128.
+//   B stage: 32 rows (k) x 256 n = 512 B per row (n contiguous, as in memory),
 //            chunk c of row k at slot c ^ 4*(k & 3); fragments via the
 //            transposing ds_read_b64_tr_b16, two per 32x32x16 operand: lane L
 //            addresses row 8*(L/32) + (L%16)/4 (+4 for the second read),
 //            columns 16*((L/16)%2) + 4*(L%4) .. +3, and receives the 8
 //            consecutive k of column L%32 that the MFMA expects.
-// Two stages (128 KB of the 160 KB LDS): A0 | A1 | B0 | B1, so every stage /
-// subtile / k-step displacement of an LDS address is an instruction immediate.
+// Four stages (128 KB of the 160 KB LDS): A0..A3 | B0..B3; stage, subtile and
+// k-step displacements of LDS addresses are instruction immediates.
 #pragma once
 
 #include "epilogue.hpp"
@@ -41,18 +43,32 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) void lds_void;
 
 namespace pp {
-constexpr int BM = 256, BN = 256, BK = 64, THREADS = 512;
-constexpr int A_STAGE = BM * 128;            // 32 KB
-constexpr int B_STAGE = BK * BN * 2;         // 32 KB
-constexpr int A_OFF = 0, B_OFF = 2 * A_STAGE;
-constexpr int LDS_BYTES = 2 * (A_STAGE + B_STAGE);
+constexpr int BM = 256, BN = 256, BK = 32, THREADS = 512, STAGES = 4;
+constexpr int A_STAGE = BM * BK * 2;         // 16 KB
+constexpr int B_STAGE = BK * BN * 2;         // 16 KB
+constexpr int A_OFF = 0, B_OFF = STAGES * A_STAGE;
+constexpr int LDS_BYTES = STAGES * (A_STAGE + B_STAGE);
+constexpr int LOADS_PER_TILE = 4;            // direct loads per wave per k-tile
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt [3:0]+[15:14], expcnt [6:4], lgkmcnt [11:8])
 constexpr int WAIT_LGKM0 = 0xC07F;
-constexpr int WAIT_VM0 = 0x0F70;
+constexpr int wait_vm(int n) { return 0x0F70 | (n & 0xF) | ((n >> 4) << 14); }
 
-__device__ __forceinline__ int swz_a(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int swz_a(int row) { return (row >> 2) & 3; }
 __device__ __forceinline__ int swz_b(int k) { return 4 * (k & 3); }
+
+// Transposing 8-byte LDS read (see the header comment for the lane layout).
+// Issued as inline assembly: the compiler cannot tell that it does not touch
+// the LDS stages the in-flight direct loads are filling and would otherwise
+// drain every outstanding load before it.  Its completion is covered by the
+// explicit lgkmcnt(0) wait that ends every memory phase.
+template <int OFFSET>
+__device__ __forceinline__ u32x2 ds_read_tr16_b64(uint32_t lds_addr) {
+  u32x2 v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(lds_addr), "i"(OFFSET));
+  return v;
+}
+
 }  // namespace pp
 
 template <int DTI, int DTO>
@@ -90,44 +106,51 @@ __global__ __launch_bounds__(512, 1) void gemm16_pp_kernel(GemmArgs a) {
   }
 
   // ---- per-lane global offsets of this wave's direct loads --------------
+  // A: instruction i covers stage rows (2w + i)*16 .. +16 (16 rows x 64 B);
+  // B: instruction i covers stage rows (k) (2w + i)*2 .. +2 (2 rows x 512 B).
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.A, a.a_bytes);
   const __amdgpu_buffer_rsrc_t rbm = make_rsrc(a.B, a.b_bytes);
-  uint32_t a_off[4], a_k[4], b_off[4], b_k[4];
+  uint32_t a_off[2], a_k[2], b_off[2], b_k[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = w * 32 + i * 8 + (lane >> 3);           // A stage row
-    const int c = (lane & 7) ^ pp::swz_a(row);               // logical k-chunk for slot lane&7
+  for (int i = 0; i < 2; ++i) {
+    const int row = (2 * w + i) * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ pp::swz_a(row);               // logical k-chunk for slot lane&3
     const uint32_t gm = m0 + row;
     a_off[i] = gm < a.M ? (gm * a.K + c * 8) * 2 : kOOB;
     a_k[i] = c * 8;
-    const int k = w * 8 + 2 * i + (lane >> 5);               // B stage row
+    const int k = (2 * w + i) * 2 + (lane >> 5);
     const int cb = (lane & 31) ^ pp::swz_b(k);               // logical n-chunk for slot lane&31
     const uint32_t gn = n0 + cb * 8;
     b_off[i] = (gn < a.N && (uint32_t)k < a.K) ? ((uint32_t)k * a.N + gn) * 2 : kOOB;
     b_k[i] = k;
   }
-  const uint32_t b_kstep = 64u * a.N * 2u;                  // bytes per k-tile of B
+  const uint32_t b_kstep = (uint32_t)pp::BK * a.N * 2u;     // bytes of B per k-tile
 
-  auto issue_loads = [&](int kt, int stage) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t kk = (uint32_t)kt * 64u;
+  // One direct load j (0..3) of k-tile kt: even j = A rows, odd j = B rows.
+  // K-tiles at or beyond K read as zeros (every offset fails the K test), so
+  // the loop can issue its loads unconditionally into the stage it frees.
+  auto issue_one = [&](int kt, int j) {
+    const int stage = kt & (pp::STAGES - 1);
+    const uint32_t kk = (uint32_t)kt * pp::BK;
+    const int i = j >> 1;
+    if ((j & 1) == 0) {
       const uint32_t ao = (a_off[i] != kOOB && kk + a_k[i] < a.K) ? a_off[i] + kk * 2u : kOOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, (lds_void*)(smem + pp::A_OFF + stage * pp::A_STAGE + w * 4096 + i * 1024), 16, ao, 0, 0, 0);
+          ra, (lds_void*)(smem + pp::A_OFF + stage * pp::A_STAGE + (2 * w + i) * 1024), 16, ao, 0, 0, 0);
+    } else {
       const uint32_t bo = (b_off[i] != kOOB && kk + b_k[i] < a.K) ? b_off[i] + (uint32_t)kt * b_kstep : kOOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rbm, (lds_void*)(smem + pp::B_OFF + stage * pp::B_STAGE + w * 4096 + i * 1024), 16, bo, 0, 0, 0);
+          rbm, (lds_void*)(smem + pp::B_OFF + stage * pp::B_STAGE + (2 * w + i) * 1024), 16, bo, 0, 0, 0);
     }
   };
 
   // ---- LDS fragment addresses -------------------------------------------
-  // A (m side): row wm*128 + sj*32 + lrow, chunk 2*ks + half.
-  const int xa = pp::swz_a(lrow);
-  uint32_t a_rd[4];
+  // A (m side): row wm*128 + sj*32 + lrow, chunk 2*ks + half (ks = 0, 1).
+  const int xa = pp::swz_a(lrow);          // (row >> 2) & 3 depends on lrow only
+  uint32_t a_rd[2];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-    a_rd[ks] = pp::A_OFF + (wm * 128 + lrow) * 128 + (((2 * ks + half) ^ xa) * 16);
+  for (int ks = 0; ks < 2; ++ks)
+    a_rd[ks] = pp::A_OFF + (wm * 128 + lrow) * 64 + (((2 * ks + half) ^ xa) * 16);
   // B (n side): k = 8*half + (lane%16)/4 (+ 16*ks + 4*q), n = wn*64 + si*32 + 16*((lane/16)%2) + 4*(lane%4)
   uint32_t b_rd[2];
 #pragma unroll
@@ -139,59 +162,73 @@ __global__ __launch_bounds__(512, 1) void gemm16_pp_kernel(GemmArgs a) {
   }
 
   const int ktiles = (int)((a.K + pp::BK - 1) / pp::BK);
+  // LDS byte address of smem (an address-space-3 pointer converts to its offset)
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)smem;
 
-  // ---- prologue: tile 0 --------------------------------------------------
-  if (ktiles > 0) {
-    issue_loads(0, 0);
-    __builtin_amdgcn_s_waitcnt(pp::WAIT_VM0);
-  }
+  // ---- prologue: k-tiles 0 .. 2 in flight, k-tile 0 landed ----------------
+  for (int t = 0; t < pp::STAGES - 1; ++t)
+#pragma unroll
+    for (int j = 0; j < pp::LOADS_PER_TILE; ++j) issue_one(t, j);
+  __builtin_amdgcn_s_waitcnt(pp::wait_vm(2 * pp::LOADS_PER_TILE));
   __builtin_amdgcn_s_barrier();
   if (wm == 1) __builtin_amdgcn_s_barrier();      // cluster 1 runs one phase behind
 
-  u32x4 fa[4][2];        // [sj][ks within the half]
-  u32x4 fb[2][2];        // [si][ks within the half]
+  // Interval schedule (cluster 0 / cluster 1): M(t) at 2t / 2t+1, C(t) at
+  // 2t+1 / 2t+2.  M(t) loads k-tile t+3 into stage (t+3)%4 = (t-1)%4, whose
+  // last reader, M(t-1), ended by interval 2t-1.  M(t) also waits for its own
+  // loads of k-tile t+1 (issued in M(t-2); k-tiles t+2 and t+3 may remain in
+  // flight) before the barrier that precedes the first read of t+1 at
+  // interval 2t+2.
+  u32x4 fa[4][2];        // [sj][ks]
+  u32x4 fb[2][2];        // [si][ks]
   for (int kt = 0; kt < ktiles; ++kt) {
-    const int stage = kt & 1;
+    const int stage = kt & (pp::STAGES - 1);
+    // ---- memory phase: fragments of k-tile kt, loads of k-tile kt + 3 -------
+    const int kn = kt + pp::STAGES - 1;
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      // ---- memory phase: fragments of this half, next tile's loads -------
-      __builtin_amdgcn_sched_barrier(0);
+    for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int ks = 2 * h + kk;
-#pragma unroll
-        for (int sj = 0; sj < 4; ++sj)
-          fa[sj][kk] = *reinterpret_cast<const u32x4*>(smem + a_rd[ks] + stage * pp::A_STAGE + sj * 4096);
-#pragma unroll
-        for (int si = 0; si < 2; ++si) {
-          const uint32_t base = b_rd[si] + stage * pp::B_STAGE + ks * 16 * 512;
-          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(smem + base));
-          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(smem + base + 4 * 512));
-          u32x4 f;
-          f.x = __builtin_bit_cast(u32x2, lo).x;
-          f.y = __builtin_bit_cast(u32x2, lo).y;
-          f.z = __builtin_bit_cast(u32x2, hi).x;
-          f.w = __builtin_bit_cast(u32x2, hi).y;
-          fb[si][kk] = f;
+      for (int sj = 0; sj < 4; ++sj) {
+        fa[sj][ks] = *reinterpret_cast<const u32x4*>(smem + a_rd[ks] + stage * pp::A_STAGE + sj * 2048);
+        if (sj & 1) {              // one direct load after every second A-fragment read
+          __builtin_amdgcn_sched_barrier(0);
+          issue_one(kn, ks * 2 + (sj >> 1));
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
-      if (h == 0 && kt + 1 < ktiles) issue_loads(kt + 1, stage ^ 1);
-      if (h == 1) __builtin_amdgcn_s_waitcnt(pp::WAIT_VM0);
-      __builtin_amdgcn_s_waitcnt(pp::WAIT_LGKM0);
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      // ---- compute phase: 16 MFMAs from registers ------------------------
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int si = 0; si < 2; ++si)
-#pragma unroll
-          for (int sj = 0; sj < 4; ++sj) mfma_chunk<DTI>(acc[si][sj], fb[si][kk], fa[sj][kk]);
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_barrier();
+      for (int si = 0; si < 2; ++si) {
+        const uint32_t base = lds_base + b_rd[si] + stage * pp::B_STAGE;
+        const u32x2 lo = ks == 0 ? pp::ds_read_tr16_b64<0>(base) : pp::ds_read_tr16_b64<16 * 512>(base);
+        const u32x2 hi = ks == 0 ? pp::ds_read_tr16_b64<4 * 512>(base)
+                                 : pp::ds_read_tr16_b64<16 * 512 + 4 * 512>(base);
+        u32x4 f;
+        f.x = lo.x;
+        f.y = lo.y;
+        f.z = hi.x;
+        f.w = hi.y;
+        fb[si][ks] = f;
+      }
     }
+    // k-tile kt+1 landed for this wave (k-tiles kt+2 and kt+3 may be in flight)
+    __builtin_amdgcn_s_waitcnt(pp::wait_vm(2 * pp::LOADS_PER_TILE));
+    __builtin_amdgcn_s_waitcnt(pp::WAIT_LGKM0);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- compute phase: 16 MFMAs from registers ------------------------------
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int si = 0; si < 2; ++si)
+#pragma unroll
+        for (int sj = 0; sj < 4; ++sj) mfma_chunk<DTI>(acc[si][sj], fb[si][ks], fa[sj][ks]);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
   }
+  // no direct load may still be writing LDS when the workgroup ends
+  __builtin_amdgcn_s_waitcnt(pp::wait_vm(0));
   if (wm == 0) __builtin_amdgcn_s_barrier();      // same barrier count for both clusters
 
   // ---- epilogue: activation, cast, one store per element -----------------

@@ -252,24 +252,4 @@ inline int launch_conv_tile(int tile, const ConvArgs& a, hipStream_t s) {
   }
 }
 
-template <int DTI>
-inline int launch_gemm_in(int dto, int tile, const GemmArgs& a, hipStream_t s) {
-  switch (dto) {
-    case DT_F32: return launch_gemm_tile<DTI, DT_F32>(tile, a, s);
-    case DT_F16: return launch_gemm_tile<DTI, DT_F16>(tile, a, s);
-    case DT_BF16: return launch_gemm_tile<DTI, DT_BF16>(tile, a, s);
-    default: return -1;
-  }
-}
-
-template <int DTI>
-inline int launch_conv_in(int dto, int tile, const ConvArgs& a, hipStream_t s) {
-  switch (dto) {
-    case DT_F32: return launch_conv_tile<DTI, DT_F32>(tile, a, s);
-    case DT_F16: return launch_conv_tile<DTI, DT_F16>(tile, a, s);
-    case DT_BF16: return launch_conv_tile<DTI, DT_BF16>(tile, a, s);
-    default: return -1;
-  }
-}
-
 }  // namespace biasact
