@@ -73,6 +73,33 @@ int launch_conv_plan(const ConvPlan& p, const void* x, const void* w, const void
   a.vec_w = p.vec_w;
   a.vec_y = (p.Ho * p.Wo) % 4 == 0 && ((uintptr_t)y % (dto == DT_F32 ? 16u : 8u)) == 0;
   int rc;
+  if (p.tile == 7) {
+    HaloArgs h;
+    h.x = x;
+    h.w = w;
+    h.bias = bias;
+    h.y = y;
+    h.geom = a.geom;
+    h.x_bytes = a.x_bytes;
+    h.w_bytes = a.w_bytes;
+    h.bias_bytes = a.bias_bytes;
+    h.y_bytes = a.y_bytes;
+    h.bias_dt = a.bias_dt;
+    h.act = act;
+    h.alpha = 0.0f;
+    h.PH = p.h_PH;
+    h.PW = p.h_PW;
+    h.HR = p.h_HR;
+    h.HC = p.h_HC;
+    h.bkc = p.h_bkc;
+    h.co_blocks = p.h_co_blocks;
+    h.w_blocks = p.h_w_blocks;
+    h.h_blocks = p.h_h_blocks;
+    h.blocks = p.h_blocks;
+    rc = launch_conv_halo(p.dti, dto, (int)(p.kh * p.kw), (int)p.h_bm, (int)p.h_wtn, h, s);
+    if (rc) return kErrUnsupported;
+    return hipGetLastError() == hipSuccess ? kOk : kErrHip;
+  }
   switch (p.dti) {
     case DT_F32: rc = launch_conv_f32(dto, p.tile, a, s); break;
     case DT_F16: rc = launch_conv_f16(dto, p.tile, a, s); break;
@@ -170,7 +197,8 @@ int biasact_num_tile_configs(void) { return kNumTileConfigs; }
 int biasact_tile_config_name(int id, char* buf, size_t n) {
   if (id < 0 || id >= kNumTileConfigs || !buf || n == 0) return kErrInvalid;
   const TileShapeDesc& t = kTiles[id];
-  snprintf(buf, n, "%dx%d/%dx%d", t.bm, t.bn, t.waves_m, t.waves_n);
+  const char* kind = id == 6 ? " ping-pong" : (id == 7 ? " conv-halo" : "");
+  snprintf(buf, n, "%dx%d/%dx%d%s", t.bm, t.bn, t.waves_m, t.waves_n, kind);
   return kOk;
 }
 
@@ -186,7 +214,7 @@ int biasact_conv_tile_config(int64_t N, int64_t Co, int64_t Ho, int64_t Wo, int6
                              uint32_t dtypes) {
   int f = forced_tile();
   if (f < 0) f = select_conv_tile(N, Co, Ho, Wo, K_total, (int)(dtypes & 0xffu));
-  return f == 6 ? 0 : f;
+  return f == 6 ? 0 : f;   // the halo tile (7) depends on the filter and alignment: see conv2d_bias_act
 }
 
 int biasact_force_tile_config(int id) {

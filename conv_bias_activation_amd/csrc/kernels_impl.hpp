@@ -5,6 +5,7 @@
 // element type.
 #pragma once
 
+#include "conv_halo.hpp"
 #include "epilogue.hpp"
 #include "gemm_pp.hpp"
 #include "launch.hpp"
@@ -249,6 +250,20 @@ inline int launch_conv_tile(int tile, const ConvArgs& a, hipStream_t s) {
     case 4: launch_conv_t<DTI, DTO, T4>(a, s); return 0;
     case 5: launch_conv_t<DTI, DTO, T5>(a, s); return 0;
     default: return -1;
+  }
+}
+
+template <int DTI, int DTO>
+inline int launch_conv_halo_tile(int taps, int bm, int wtn, const HaloArgs& a, hipStream_t s) {
+  if constexpr (DTI == DT_F32) {
+    return -1;
+  } else {
+    if (wtn != 64) return -1;
+    if (taps == 9 && bm == 64) { launch_conv_halo_t<DTI, DTO, 9, 64, 64>(a, s); return 0; }
+    if (taps == 9 && bm == 128) { launch_conv_halo_t<DTI, DTO, 9, 128, 64>(a, s); return 0; }
+    if (taps == 1 && bm == 64) { launch_conv_halo_t<DTI, DTO, 1, 64, 64>(a, s); return 0; }
+    if (taps == 1 && bm == 128) { launch_conv_halo_t<DTI, DTO, 1, 128, 64>(a, s); return 0; }
+    return -1;
   }
 }
 

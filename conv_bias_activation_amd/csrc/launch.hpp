@@ -38,6 +38,23 @@ struct ConvArgs {
   bool vec_w, vec_y;
 };
 
+// Argument block of the halo-staging conv kernel (conv_halo.hpp).
+struct HaloArgs {
+  const void* x;
+  const void* w;
+  const void* bias;
+  void* y;
+  ConvGeom geom;
+  uint32_t x_bytes, w_bytes, bias_bytes, y_bytes;
+  int bias_dt;
+  int act;
+  float alpha;
+  uint32_t PH, PW;          // output rows / columns per workgroup
+  uint32_t HR, HC;          // halo rows / columns staged per channel chunk (HC even)
+  uint32_t bkc;             // channels per chunk (8, 16, 32 or 64)
+  uint32_t co_blocks, w_blocks, h_blocks, blocks;
+};
+
 // Per-input-type launchers (one translation unit each).  Return 0, or -1 for
 // an unknown output type / tile id.
 int launch_gemm_f32(int dto, int tile, const GemmArgs& a, hipStream_t s);
@@ -46,6 +63,7 @@ int launch_gemm_bf16(int dto, int tile, const GemmArgs& a, hipStream_t s);
 int launch_conv_f32(int dto, int tile, const ConvArgs& a, hipStream_t s);
 int launch_conv_f16(int dto, int tile, const ConvArgs& a, hipStream_t s);
 int launch_conv_bf16(int dto, int tile, const ConvArgs& a, hipStream_t s);
+int launch_conv_halo(int dti, int dto, int taps, int bm, int wtn, const HaloArgs& a, hipStream_t s);
 int launch_act_cast(int dto, const float* ws, void* out, uint32_t n, int act, float alpha,
                     hipStream_t s);
 

@@ -51,6 +51,42 @@ int pick_tile(const int* order, int n_order, int64_t rows_j, int64_t rows_i, int
   return best;
 }
 
+// Halo-kernel parameters for a conv (16-bit operands, C % 8 == 0, even W,
+// 1x1 or 3x3 filters, aligned x / w).  Returns false when it does not apply.
+bool plan_halo(ConvPlan* p, const void* x, const void* w) {
+  if (p->dti == kF32 || p->C % 8 != 0 || p->W % 2 != 0) return false;
+  const uint32_t T = p->kh * p->kw;
+  if (T != 1 && T != 9) return false;
+  if (!aligned(x, 4) || !aligned(w, 16)) return false;
+  const uint32_t bm = p->Co <= 64 ? 64 : 128;
+  const uint32_t bn = 128, wtn = bn / 2;
+  const uint32_t PW = p->Wo < bn ? p->Wo : bn;
+  const uint32_t PH = bn / PW;
+  const uint32_t HR = (PH - 1) * p->sh + (p->kh - 1) * p->dh + 1;
+  uint32_t HC = (PW - 1) * p->sw + (p->kw - 1) * p->dw + 2;   // +1 column of parity shift
+  HC += HC & 1;
+  const uint64_t limit = 144 * 1024;
+  // one MFMA k-step consumes 16 channels: chunks of 64, 32 or 16 (zero-filled past C)
+  uint32_t bkc = 64;
+  while (bkc > 16 && (uint64_t)HR * HC * bkc * 2 + (uint64_t)T * bm * bkc * 2 > limit) bkc /= 2;
+  while (bkc > 16 && bkc / 2 >= p->C) bkc /= 2;                // no wider than the channel count needs
+  if ((uint64_t)HR * HC * bkc * 2 + (uint64_t)T * bm * bkc * 2 > limit) return false;
+  p->h_bm = bm;
+  p->h_wtn = wtn;
+  p->h_PH = PH;
+  p->h_PW = PW;
+  p->h_HR = HR;
+  p->h_HC = HC;
+  p->h_bkc = bkc;
+  p->h_co_blocks = (p->Co + bm - 1) / bm;
+  p->h_w_blocks = (p->Wo + PW - 1) / PW;
+  p->h_h_blocks = (p->Ho + PH - 1) / PH;
+  const uint64_t blocks = (uint64_t)p->h_co_blocks * p->h_w_blocks * p->h_h_blocks * p->N;
+  if (blocks >= (1u << 31)) return false;
+  p->h_blocks = (uint32_t)blocks;
+  return true;
+}
+
 }  // namespace
 
 int forced_tile() { return g_forced_tile.load(std::memory_order_relaxed); }
@@ -107,6 +143,7 @@ int plan_gemm(const void* A, const void* B, const void* bias, const void* C, int
   const bool pp_ok = dti != kF32 && p->vec_a && p->vec_b && p->vec_c;
   if (tile == 0 && pp_ok && forced_tile() < 0) tile = 6;
   if (tile == 6 && !pp_ok) tile = 0;
+  if (tile == 7) tile = 2;                              // the halo tile is conv-only
   p->tile = tile;
   p->tiles_m = (uint32_t)ceil_div(M, kTiles[tile].bm);
   p->tiles_n = (uint32_t)ceil_div(N, kTiles[tile].bn);
@@ -159,8 +196,12 @@ int plan_conv(const void* x, const void* w, const void* bias, const void* y, int
   p->vec_y = (Ho * Wo) % 4 == 0 && aligned(y, 4 * (uintptr_t)elem_bytes(dto));
   p->empty = N == 0;
   int tile = forced_tile();
-  if (tile < 0 || tile >= kNumTileConfigs) tile = select_conv_tile(N, Co, Ho, Wo, K, dti);
+  const bool auto_tile = tile < 0 || tile >= kNumTileConfigs;
+  if (auto_tile) tile = select_conv_tile(N, Co, Ho, Wo, K, dti);
   if (tile == 6) tile = 0;                              // no ping-pong conv kernel
+  const bool halo_ok = plan_halo(p, x, w);
+  if (halo_ok && (auto_tile || tile == 7)) tile = 7;
+  if (tile == 7 && !halo_ok) tile = 3;
   p->tile = tile;
   p->tiles_m = (uint32_t)ceil_div(Co, kTiles[tile].bm);
   p->tiles_n = (uint32_t)ceil_div(P, kTiles[tile].bn);

@@ -21,6 +21,7 @@ constexpr TileShapeDesc kTiles[] = {
     {4, 64, 256, 1, 4},
     {5, 64, 64, 2, 2},
     {6, 256, 256, 2, 4},   // 8-wave ping-pong kernel: aligned 16-bit GEMMs only (else as 0)
+    {7, 128, 128, 2, 2},   // conv with a channel-last LDS halo: 16-bit, 1x1 or 3x3 (else as 3)
 };
 constexpr int kNumTileConfigs = (int)(sizeof(kTiles) / sizeof(kTiles[0]));
 
@@ -44,6 +45,8 @@ struct ConvPlan {
   bool empty;                      // N == 0
   int tile;
   uint32_t tiles_m, tiles_n;
+  // halo kernel (tile 7) parameters
+  uint32_t h_bm, h_wtn, h_PH, h_PW, h_HR, h_HC, h_bkc, h_co_blocks, h_w_blocks, h_h_blocks, h_blocks;
 };
 
 int plan_gemm(const void* A, const void* B, const void* bias, const void* C, int64_t M, int64_t N,

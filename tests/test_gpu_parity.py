@@ -66,7 +66,7 @@ def test_gemm_small_vs_oracle(ba, shape, types):
         assert rep["ok"], rep
 
 
-@pytest.mark.parametrize("tile", range(7))
+@pytest.mark.parametrize("tile", range(8))
 def test_gemm_every_tile_config(ba, tile):
     ba.force_tile_config(tile)
     try:
@@ -212,7 +212,7 @@ def test_conv_small_vs_oracle(ba, shape, types):
         assert rep["ok"], rep
 
 
-@pytest.mark.parametrize("tile", range(7))
+@pytest.mark.parametrize("tile", range(8))
 def test_conv_every_tile_config(ba, tile):
     ba.force_tile_config(tile)
     try:
@@ -226,6 +226,41 @@ def test_conv_every_tile_config(ba, tile):
             assert rep["ok"], rep
     finally:
         ba.force_tile_config(-1)
+
+
+# Shapes that take the channel-last halo kernel (16-bit, C % 8 == 0, even W,
+# 1x1 or 3x3): several channel chunks, ragged Co, narrow and wide outputs,
+# strides, dilations, asymmetric padding.
+HALO_SHAPES = [
+    (2, 64, 14, 14, 64, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1)),
+    (1, 128, 12, 10, 96, 3, 3, (1, 1), (2, 2, 2, 2), (2, 2)),
+    (3, 16, 8, 8, 70, 1, 1, (2, 2), (0, 0, 0, 0), (1, 1)),
+    (1, 8, 9, 150, 33, 3, 3, (1, 1), (1, 0, 2, 1), (1, 1)),
+    (2, 256, 7, 6, 130, 3, 3, (2, 1), (1, 1, 0, 1), (1, 2)),
+    (1, 24, 30, 2, 64, 3, 3, (3, 1), (1, 1, 1, 1), (1, 1)),
+    (2, 32, 5, 40, 17, 1, 1, (1, 2), (1, 0, 0, 1), (1, 1)),
+]
+
+
+@pytest.mark.parametrize("shape", HALO_SHAPES, ids=lambda s: "x".join(map(str, s[:7])))
+@pytest.mark.parametrize("types", [("f16", "f16", "f16"), ("bf16", "bf16", "bf16"), ("bf16", "f32", "f32"),
+                                   ("f16", "bf16", "f32")], ids=lambda t: "-".join(t))
+def test_conv_halo_path_vs_oracle(ba, shape, types):
+    N, C, H, W, Co, kh, kw, st, pd, dl = shape
+    ti, to, tb = types
+    for tile in (-1, 7):
+        ba.force_tile_config(tile)
+        try:
+            for j, act in enumerate(("tanh", "relu")):
+                case = _ccase(N, C, H, W, Co, kh, kw, st, pd, dl, ti, to, tb, act)
+                inp = wl.gen_conv(case, seed=41 + j)
+                y = values_of(run_conv(case, inp), to)
+                ref, floor = conv_reference(case, inp)
+                rep = check(y, ref, floor, case)
+                _report(f"halo {shape} {types} {act} tile {tile}", rep)
+                assert rep["ok"], rep
+        finally:
+            ba.force_tile_config(-1)
 
 
 def test_conv_no_bias(ba):
