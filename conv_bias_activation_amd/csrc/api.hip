@@ -96,7 +96,8 @@ int launch_conv_plan(const ConvPlan& p, const void* x, const void* w, const void
     h.w_blocks = p.h_w_blocks;
     h.h_blocks = p.h_h_blocks;
     h.blocks = p.h_blocks;
-    rc = launch_conv_halo(p.dti, dto, (int)(p.kh * p.kw), (int)p.h_bm, (int)p.h_wtn, h, s);
+    h.vec_y = p.Wo % 4 == 0 && ((uintptr_t)y % (dto == DT_F32 ? 16u : 8u)) == 0;
+    rc = launch_conv_halo(p.dti, dto, (int)(p.kh * p.kw), (int)p.h_bm, (int)p.h_ks, h, s);
     if (rc) return kErrUnsupported;
     return hipGetLastError() == hipSuccess ? kOk : kErrHip;
   }

@@ -10,19 +10,32 @@
 //   halo  [row][col][c] : input rows  ih = oh*sh - pt + r*dh of the patch,
 //                         columns iw = iw_lo + col (iw_lo even, <= ow0*sw - pl)
 //   wts   [t][co][c]
-// Channels are staged in chunks of BKC = 64, 32 or 16 (zero-filled past C).
 // so every MFMA fragment is one ds_read_b128 whatever the stride, padding or
 // dilation, and each input element is fetched from memory once per channel
-// chunk instead of once per tap.
+// chunk instead of once per tap.  Channels are staged in chunks of
+// BKC = 16 * KS (KS = 1, 2, 4 MFMA k-steps per tap; zero-filled past C).
 //
 // Workgroup: 256 threads (2 x 2 waves), BM output channels x a patch of PH
-// output rows x PW output columns (positions q = row * PW + col, BN = PH * PW
-// rounded up to 32 per wave column).  Channel chunks of BKC are staged with
-// register-transposed 4-byte input loads (two columns x 8 channels -> two
-// 16-byte LDS writes) and 16-byte weight loads (8 channels x T taps -> T
-// 16-byte LDS writes).  Each 16-byte chunk of an LDS row sits at slot
-// chunk ^ (row % 8) (rows of 8 chunks) so 8 consecutive rows hit 8 slots.
+// output rows x PW output columns (positions q = row * PW + col, at most 128).
+// Staging items: input (halo row, column pair, 8 channels) — eight 4-byte
+// loads transposed in registers into two 16-byte LDS writes; weights (output
+// channel, 8 channels) — T 16-byte loads (8 channels x T taps are contiguous
+// in OIHW) regrouped into T 16-byte LDS writes.  The first HB input items
+// and WB weight items of each thread form a batch whose offsets are computed
+// once; the batch of chunk 0 is issued before anything waits, and the batch of
+// chunk ck + 1 is spread over the MFMA steps of chunk ck.  Items beyond the
+// batch (large halos) are staged with their own loads before the multiply.
+// The multiply is unrolled over its T * KS (tap, k-step) steps; the fragments
+// of step s + 1 are read while the MFMAs of step s run.
+//
+// LDS rows (one halo position, or one (tap, co) weight row) hold NCH = 2 * KS
+// chunks of 16 bytes; chunk c of row p sits at slot c ^ ((p >> S) % NCH) with
+// 2^S = 16 / NCH rows per 256 bytes, so the 16 lanes of a read phase that
+// take 16 consecutive rows hit all 64 banks once.  The bias is fetched as raw
+// words after the first staging loads and added in the epilogue.
 #pragma once
+
+#include <utility>
 
 #include "epilogue.hpp"
 #include "launch.hpp"
@@ -33,23 +46,61 @@ namespace biasact {
 namespace halo {
 constexpr int THREADS = 256;
 constexpr int LDS_BYTES = 144 * 1024;
-}  // namespace halo
+constexpr int HB = 4;     // input items per thread in the precomputed batch
+constexpr int WB = 2;     // weight items per thread in the precomputed batch
+constexpr int WTN = 64;   // positions per wave (two 32-wide MFMA tiles)
+constexpr uint32_t kNone = 0xffffffffu;   // "no LDS write" marker of an item
+constexpr uint32_t kFar = 1u << 30;       // channel offset that fails every c < C test
 
-// Slot of 16-byte chunk `c` in a row `row` holding `nch` chunks (power of 2).
-__device__ __forceinline__ uint32_t halo_slot(uint32_t row, uint32_t c, uint32_t nch) {
-  return c ^ (row & (nch - 1) & 7);
+// Row -> slot-mask shift for rows of NCH 16-byte chunks.
+template <int NCH>
+constexpr int row_shift() { return NCH == 8 ? 1 : (NCH == 4 ? 2 : 3); }
+
+template <int NCH>
+__device__ __forceinline__ uint32_t slot(uint32_t row, uint32_t c) {
+  return c ^ ((row >> row_shift<NCH>()) & (NCH - 1));
 }
 
-// T = taps (kh*kw) known at compile time (1, 9, ...): 16-byte weight loads.
-// BM: output channels per workgroup (64 or 128); WTN: positions per wave (multiple of 32).
-template <int DTI, int DTO, int T, int BM, int WTN>
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>), in order.
+template <class F, int... I>
+__device__ __forceinline__ void unroll_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void unroll(F&& f) {
+  unroll_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Scheduling groups of one multiply step: NM MFMAs, with the ND LDS reads and
+// NV global loads of the step spread evenly behind them.
+template <int NM, int ND, int NV, int I = 0>
+__device__ __forceinline__ void interleave() {
+  if constexpr (I < NM) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    constexpr int d = (I + 1) * ND / NM - I * ND / NM;
+    if constexpr (d > 0) __builtin_amdgcn_sched_group_barrier(0x100, d, 0);
+    constexpr int v = (I + 1) * NV / NM - I * NV / NM;
+    if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x020, v, 0);
+    interleave<NM, ND, NV, I + 1>();
+  }
+}
+}  // namespace halo
+
+// T = taps (kh*kw: 1 or 9), BM = output channels per workgroup (64 or 128),
+// KS = 16-channel k-steps per tap and chunk (1, 2 or 4).
+template <int DTI, int DTO, int T, int BM, int KS>
 __global__ __launch_bounds__(256, 1) void conv16_halo_kernel(HaloArgs a) {
   static_assert(DTI == DT_F16 || DTI == DT_BF16, "16-bit operands only");
-  constexpr int WTM = BM / 2, SM = WTM / 32, SN = WTN / 32;
+  constexpr int WTM = BM / 2, SM = WTM / 32, SN = halo::WTN / 32;
+  constexpr int BKC = 16 * KS, NCH = 2 * KS, ROWB = NCH * 16;
+  constexpr int NSTEP = T * KS;
+  constexpr int HB = halo::HB, WB = halo::WB, NTH = halo::THREADS;
+  constexpr int NPF = HB * 8 + WB * T;                  // loads of one batch
+  constexpr int PER = (NPF + NSTEP - 1) / NSTEP;        // batch loads per multiply step
   __shared__ __attribute__((aligned(16))) uint8_t smem[halo::LDS_BYTES];
   const ConvGeom& G = a.geom;
 
-  // workgroup -> (co block, image, output-row block, output-column block)
+  // workgroup -> (co block, output-column block, output-row block, image)
   uint32_t bid = blockIdx.x;
   const uint32_t cb = bid % a.co_blocks;  bid /= a.co_blocks;
   const uint32_t wb = bid % a.w_blocks;   bid /= a.w_blocks;
@@ -66,168 +117,285 @@ __global__ __launch_bounds__(256, 1) void conv16_halo_kernel(HaloArgs a) {
   const int32_t iw_first = (int32_t)ow0 * G.sw - G.pl;
   const int32_t iw_lo = iw_first & ~1;                 // even (floor) so column pairs are 4-byte aligned
   const uint32_t col_shift = (uint32_t)(iw_first - iw_lo);
-  const uint32_t BKC = a.bkc, NCH = BKC / 8;
-  const uint32_t HR = a.HR, HC = a.HC;                 // halo rows, columns (HC even)
-  const uint32_t halo_bytes = HR * HC * BKC * 2;
-  uint8_t* s_halo = smem;
-  uint8_t* s_wts = smem + halo_bytes;                  // T * BM * BKC * 2 bytes
-
-  // ---- accumulators start at the bias ------------------------------------
-  f32x16 acc[SN][SM];
-  {
-    uint32_t idx[SM];
-    float bv[SM];
-#pragma unroll
-    for (int sj = 0; sj < SM; ++sj) idx[sj] = co0 + wave_m * WTM + sj * 32 + lrow;
-    load_bias_vec<SM>(a.bias, a.bias_bytes, a.bias_dt, idx, G.Co, bv);
-#pragma unroll
-    for (int sj = 0; sj < SM; ++sj)
-#pragma unroll
-      for (int si = 0; si < SN; ++si)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[si][sj][r] = bv[sj];
-  }
-
-  // ---- per-lane B-fragment positions (position -> halo row/col) -----------
-  uint32_t pos_rowcol[SN];     // halo (row, col) of tap (0, 0) as row * HC + col
-  bool pos_ok[SN];
-#pragma unroll
-  for (int si = 0; si < SN; ++si) {
-    const uint32_t q = wave_n * WTN + si * 32 + lrow;
-    const uint32_t qh = q / a.PW, qw = q - qh * a.PW;
-    pos_ok[si] = q < a.PH * a.PW;
-    // lanes past the patch read halo position 0 (in range); their results are never stored
-    pos_rowcol[si] = pos_ok[si] ? (qh * G.sh) * HC + qw * G.sw + col_shift : 0u;
-  }
+  const uint32_t HC = a.HC;                            // halo columns (even)
+  const uint32_t wts_base = a.HR * HC * ROWB;          // weights follow the halo
 
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, a.x_bytes);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w, a.w_bytes);
-  const uint32_t HW = G.H * G.W;
+  const uint32_t HW2 = G.H * G.W * 2u;                 // bytes between channels of x
   const uint32_t nchunks = (G.C + BKC - 1) / BKC;
+  const uint32_t pairs = HC / 2;
+  const uint32_t h_items = a.HR * pairs * NCH;
+  constexpr uint32_t w_items = BM * NCH;
 
-  for (uint32_t ck = 0; ck < nchunks; ++ck) {
-    const uint32_t c0 = ck * BKC;
-    if (ck > 0) __syncthreads();                       // previous chunk fully consumed
-    // ---- stage the input halo: item = (row, column pair, 8-channel group)
-    {
-      const uint32_t pairs = HC / 2, items = HR * pairs * NCH;
-      for (uint32_t it = threadIdx.x; it < items; it += halo::THREADS) {
-        const uint32_t g = it % NCH;
-        const uint32_t rp = it / NCH;
-        const uint32_t pr = rp % pairs, hr = rp / pairs;
-        const int32_t ih = ih_lo + (int32_t)hr;
-        const int32_t iw = iw_lo + 2 * (int32_t)pr;
-        const bool rok = (uint32_t)ih < G.H && (uint32_t)iw < G.W;   // W even: iw+1 < W too
-        uint32_t d[8];
+  // ---- staging items ---------------------------------------------------------
+  // input item it = (halo row hr, column pair pr, channel group g):
+  // x offset of channel 8g of chunk 0 (kOOB outside the image), channel offset
+  // 8g (kFar when the item does not exist), LDS addresses of its two columns.
+  auto halo_item = [&](uint32_t it, uint32_t& src, uint32_t& g8, uint32_t& lo, uint32_t& hi) {
+    const uint32_t g = it % NCH, rp = it / NCH;
+    const uint32_t pr = rp % pairs, hr = rp / pairs;
+    const int32_t ih = ih_lo + (int32_t)hr, iw = iw_lo + 2 * (int32_t)pr;
+    const bool exists = it < h_items;
+    // W even: iw + 1 < W too
+    src = (uint32_t)ih < G.H && (uint32_t)iw < G.W
+              ? ((img * G.C + g * 8) * G.H * G.W + (uint32_t)ih * G.W + (uint32_t)iw) * 2u
+              : kOOB;
+    g8 = exists ? g * 8 : halo::kFar;
+    const uint32_t p0 = hr * HC + 2 * pr, p1 = p0 + 1;
+    lo = exists ? p0 * ROWB + halo::slot<NCH>(p0, g) * 16 : halo::kNone;
+    hi = p1 * ROWB + halo::slot<NCH>(p1, g) * 16;
+  };
+  // weight item it = (co column col, channel group g): w offset of channel 8g
+  // of chunk 0, channel offset (kFar when absent), LDS address of its tap-0 row.
+  auto wts_item = [&](uint32_t it, uint32_t& src, uint32_t& g8, uint32_t& dst) {
+    const uint32_t g = it % NCH, col = it / NCH;
+    const bool exists = it < w_items && co0 + col < G.Co;
+    src = ((co0 + col) * G.C + g * 8) * T * 2u;
+    g8 = exists ? g * 8 : halo::kFar;
+    dst = it < w_items ? wts_base + col * ROWB + halo::slot<NCH>(col, g) * 16 : halo::kNone;
+  };
+
+  uint32_t hreg[HB][8];
+  uint32_t wreg[WB][4 * T];
+  auto halo_load1 = [&](uint32_t (&d)[8], uint32_t src, uint32_t g8, uint32_t c0) {
+    const bool ok = src != kOOB && c0 + g8 < G.C;    // C % 8 == 0: the group is all in or all out
+    const uint32_t off = src + c0 * HW2;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t c = c0 + g * 8 + e;
-          const uint32_t off = (img * G.C + c) * HW + (uint32_t)ih * G.W + (uint32_t)iw;
-          d[e] = ld_b32(rx, (rok && c < G.C) ? off * 2u : kOOB);
-        }
-        // d[e] = (col 2pr: channel e | col 2pr+1: channel e); transpose to two channel chunks
-        u32x4 lo, hi;
-        lo.x = (d[0] & 0xffffu) | (d[1] << 16);
-        lo.y = (d[2] & 0xffffu) | (d[3] << 16);
-        lo.z = (d[4] & 0xffffu) | (d[5] << 16);
-        lo.w = (d[6] & 0xffffu) | (d[7] << 16);
-        hi.x = (d[0] >> 16) | (d[1] & 0xffff0000u);
-        hi.y = (d[2] >> 16) | (d[3] & 0xffff0000u);
-        hi.z = (d[4] >> 16) | (d[5] & 0xffff0000u);
-        hi.w = (d[6] >> 16) | (d[7] & 0xffff0000u);
-        const uint32_t p0 = hr * HC + 2 * pr, p1 = p0 + 1;
-        *reinterpret_cast<u32x4*>(s_halo + (p0 * NCH + halo_slot(p0, g, NCH)) * 16) = lo;
-        *reinterpret_cast<u32x4*>(s_halo + (p1 * NCH + halo_slot(p1, g, NCH)) * 16) = hi;
-      }
-    }
-    // ---- stage the weights: item = (co, 8-channel group); 8*T contiguous values
-    {
-      const uint32_t items = BM * NCH;
-      for (uint32_t it = threadIdx.x; it < items; it += halo::THREADS) {
-        const uint32_t g = it % NCH, col = it / NCH;
-        const uint32_t co = co0 + col;
-        const uint32_t cbase = c0 + g * 8;
-        const bool ok = co < G.Co && cbase < G.C;     // C % 8 == 0: whole group in or out
-        const uint32_t base = (co * G.C + cbase) * T * 2u;
-        uint32_t v[4 * T];
+    for (int e = 0; e < 8; ++e) d[e] = ld_b32(rx, ok ? off + e * HW2 : kOOB);
+  };
+  auto halo_store1 = [&](const uint32_t (&d)[8], uint32_t lo, uint32_t hi) {
+    if (lo == halo::kNone) return;
+    // d[e] = (column 2pr: channel e | column 2pr+1: channel e); transpose into two chunks
+    u32x4 vlo, vhi;
+    vlo.x = __builtin_amdgcn_perm(d[1], d[0], 0x05040100u);
+    vlo.y = __builtin_amdgcn_perm(d[3], d[2], 0x05040100u);
+    vlo.z = __builtin_amdgcn_perm(d[5], d[4], 0x05040100u);
+    vlo.w = __builtin_amdgcn_perm(d[7], d[6], 0x05040100u);
+    vhi.x = __builtin_amdgcn_perm(d[1], d[0], 0x07060302u);
+    vhi.y = __builtin_amdgcn_perm(d[3], d[2], 0x07060302u);
+    vhi.z = __builtin_amdgcn_perm(d[5], d[4], 0x07060302u);
+    vhi.w = __builtin_amdgcn_perm(d[7], d[6], 0x07060302u);
+    *reinterpret_cast<u32x4*>(smem + lo) = vlo;
+    *reinterpret_cast<u32x4*>(smem + hi) = vhi;
+  };
+  auto wts_load1 = [&](uint32_t (&v)[4 * T], uint32_t src, uint32_t g8, uint32_t c0, int j) {
+    const u32x4 q = ld_b128(rw, c0 + g8 < G.C ? src + c0 * T * 2u + 16u * j : kOOB);
+    v[4 * j + 0] = q.x;
+    v[4 * j + 1] = q.y;
+    v[4 * j + 2] = q.z;
+    v[4 * j + 3] = q.w;
+  };
+  auto wts_store1 = [&](const uint32_t (&v)[4 * T], uint32_t dst) {
+    if (dst == halo::kNone) return;
+    // the loaded run holds (channel e, tap t) at element e*T + t
 #pragma unroll
-        for (int j = 0; j < T; ++j) {
-          const u32x4 q = ld_b128(rw, ok ? base + 16u * j : kOOB);
-          v[4 * j + 0] = q.x; v[4 * j + 1] = q.y; v[4 * j + 2] = q.z; v[4 * j + 3] = q.w;
-        }
-        // element (channel e, tap t) is value e*T + t of the run
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-          uint32_t w16[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int p = e * T + t;
-            w16[e] = (v[p >> 1] >> (16 * (p & 1))) & 0xffffu;
-          }
-          u32x4 o;
-          o.x = w16[0] | (w16[1] << 16);
-          o.y = w16[2] | (w16[3] << 16);
-          o.z = w16[4] | (w16[5] << 16);
-          o.w = w16[6] | (w16[7] << 16);
-          const uint32_t row = t * BM + col;
-          *reinterpret_cast<u32x4*>(s_wts + (row * NCH + halo_slot(row, g, NCH)) * 16) = o;
-        }
-      }
-    }
-    __syncthreads();
-    // ---- multiply: every tap, every 16-channel step ---------------------------
-    const uint32_t ksteps = BKC / 16;
     for (int t = 0; t < T; ++t) {
-      const uint32_t r = t / G.kw, s = t - r * G.kw;
-      const uint32_t tap_rc = (r * G.dh) * HC + s * G.dw;
-      for (uint32_t ks = 0; ks < ksteps; ++ks) {
-        const uint32_t ch = 2 * ks + half;                 // 16-byte chunk of this lane
-        u32x4 fi[SN], fj[SM];
+      uint32_t o[4];
 #pragma unroll
-        for (int si = 0; si < SN; ++si) {
-          const uint32_t p = pos_rowcol[si] + tap_rc;
-          fi[si] = *reinterpret_cast<const u32x4*>(s_halo + (p * NCH + halo_slot(p, ch, NCH)) * 16);
-        }
+      for (int k = 0; k < 4; ++k) {
+        const int p0 = (2 * k) * T + t, p1 = (2 * k + 1) * T + t;
+        const uint32_t sel = (uint32_t)((p0 & 1) * 2) | ((uint32_t)((p0 & 1) * 2 + 1) << 8) |
+                             ((uint32_t)(4 + (p1 & 1) * 2) << 16) | ((uint32_t)(5 + (p1 & 1) * 2) << 24);
+        o[k] = __builtin_amdgcn_perm(v[p1 >> 1], v[p0 >> 1], sel);
+      }
+      *reinterpret_cast<u32x4*>(smem + dst + t * BM * ROWB) = u32x4{o[0], o[1], o[2], o[3]};
+    }
+  };
+
+  // batch descriptors (fixed for the whole workgroup)
+  uint32_t hd_src[HB], hd_g8[HB], hd_lo[HB], hd_hi[HB];
+  uint32_t wd_src[WB], wd_g8[WB], wd_dst[WB];
 #pragma unroll
-        for (int sj = 0; sj < SM; ++sj) {
-          const uint32_t row = t * BM + wave_m * WTM + sj * 32 + lrow;
-          fj[sj] = *reinterpret_cast<const u32x4*>(s_wts + (row * NCH + halo_slot(row, ch, NCH)) * 16);
-        }
+  for (int b = 0; b < HB; ++b) halo_item(b * NTH + threadIdx.x, hd_src[b], hd_g8[b], hd_lo[b], hd_hi[b]);
 #pragma unroll
-        for (int si = 0; si < SN; ++si)
+  for (int b = 0; b < WB; ++b) wts_item(b * NTH + threadIdx.x, wd_src[b], wd_g8[b], wd_dst[b]);
+
+  // load number i of the batch of the chunk starting at channel c0
+  auto batch_load = [&](auto i_c, uint32_t c0) {
+    constexpr int i = decltype(i_c)::value;
+    if constexpr (i < HB * 8) {
+      constexpr int b = i / 8, e = i % 8;
+      const bool ok = hd_src[b] != kOOB && c0 + hd_g8[b] < G.C;
+      hreg[b][e] = ld_b32(rx, ok ? hd_src[b] + (c0 + e) * HW2 : kOOB);
+    } else {
+      constexpr int b = (i - HB * 8) / T, j = (i - HB * 8) % T;
+      wts_load1(wreg[b], wd_src[b], wd_g8[b], c0, j);
+    }
+  };
+
+  // ---- fragment addresses (k-step 0); k-step ks flips slot bits by 2*ks ----
+  uint32_t h_addr[T][SN];
+  {
+    uint32_t pos[SN];
 #pragma unroll
-          for (int sj = 0; sj < SM; ++sj) mfma_chunk<DTI>(acc[si][sj], fi[si], fj[sj]);
+    for (int si = 0; si < SN; ++si) {
+      const uint32_t q = wave_n * halo::WTN + si * 32 + lrow;
+      const uint32_t qh = q / a.PW, qw = q - qh * a.PW;
+      // lanes past the patch read halo position 0 (in range); their results are never stored
+      pos[si] = q < a.PH * a.PW ? (qh * G.sh) * HC + qw * G.sw + col_shift : 0u;
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const uint32_t r = (uint32_t)t / G.kw, s = (uint32_t)t - r * G.kw;
+      const uint32_t tap = (r * G.dh) * HC + s * G.dw;
+#pragma unroll
+      for (int si = 0; si < SN; ++si) {
+        const uint32_t p = pos[si] + tap;
+        h_addr[t][si] = p * ROWB + halo::slot<NCH>(p, (uint32_t)half) * 16;
       }
     }
   }
+  // weights: rows t*BM + row0 share the slot pattern of row0 (BM * t is a multiple of 64)
+  uint32_t w_addr[SM];
+#pragma unroll
+  for (int sj = 0; sj < SM; ++sj) {
+    const uint32_t row = wave_m * WTM + sj * 32 + lrow;
+    w_addr[sj] = wts_base + row * ROWB + halo::slot<NCH>(row, (uint32_t)half) * 16;
+  }
 
-  // ---- epilogue: activation, cast, one store per element -------------------
-  const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.y, a.y_bytes);
-  const uint32_t howo = G.Ho * G.Wo;
+  auto load_frags = [&](auto st_c, u32x4 (&fi)[SN], u32x4 (&fj)[SM]) {
+    constexpr int st = decltype(st_c)::value;
+    constexpr int t = st / KS, ks = st % KS;
+    constexpr uint32_t flip = (uint32_t)(2 * ks) << 4;
+#pragma unroll
+    for (int si = 0; si < SN; ++si)
+      fi[si] = *reinterpret_cast<const u32x4*>(smem + (h_addr[t][si] ^ flip));
+#pragma unroll
+    for (int sj = 0; sj < SM; ++sj)
+      fj[sj] = *reinterpret_cast<const u32x4*>(smem + ((w_addr[sj] + (uint32_t)(t * BM * ROWB)) ^ flip));
+  };
+
+  f32x16 acc[SN][SM];
 #pragma unroll
   for (int si = 0; si < SN; ++si)
 #pragma unroll
+    for (int sj = 0; sj < SM; ++sj)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[si][sj][r] = 0.0f;
+
+  // All T * KS steps of one chunk; with PREFETCH the batch loads of the chunk
+  // at channel c1 ride along, PER per step.
+  auto multiply = [&](auto prefetch_c, uint32_t c1) {
+    constexpr bool PREFETCH = decltype(prefetch_c)::value;
+    u32x4 fi[2][SN], fj[2][SM];
+    load_frags(std::integral_constant<int, 0>{}, fi[0], fj[0]);
+    halo::unroll<NSTEP>([&](auto st_c) {
+      constexpr int st = decltype(st_c)::value;
+      constexpr int cur = st & 1;
+      if constexpr (st + 1 < NSTEP) load_frags(std::integral_constant<int, st + 1>{}, fi[cur ^ 1], fj[cur ^ 1]);
+      constexpr int v0 = PREFETCH ? (st * PER < NPF ? st * PER : NPF) : 0;
+      constexpr int v1 = PREFETCH ? ((st + 1) * PER < NPF ? (st + 1) * PER : NPF) : 0;
+      halo::unroll<v1 - v0>([&](auto k_c) {
+        batch_load(std::integral_constant<int, v0 + decltype(k_c)::value>{}, c1);
+      });
+#pragma unroll
+      for (int si = 0; si < SN; ++si)
+#pragma unroll
+        for (int sj = 0; sj < SM; ++sj) mfma_chunk<DTI>(acc[si][sj], fi[cur][si], fj[cur][sj]);
+      constexpr int nd = st + 1 < NSTEP ? SN + SM : 0;
+      constexpr int nv = PREFETCH ? v1 - v0 : 0;
+      halo::interleave<SN * SM, nd, nv>();
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  // ---- chunk loop ------------------------------------------------------------
+  halo::unroll<NPF>([&](auto i_c) { batch_load(i_c, 0u); });
+  // raw bias words of this lane's output channels, converted in the epilogue
+  uint32_t braw[SM];
+  {
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.bias, a.bias_bytes);
+    const bool b32 = a.bias_dt == DT_F32;
+#pragma unroll
     for (int sj = 0; sj < SM; ++sj) {
       const uint32_t co = co0 + wave_m * WTM + sj * 32 + lrow;
-      const bool cok = co < G.Co;
+      const uint32_t off = co < G.Co ? co * (b32 ? 4u : 2u) : kOOB;
+      braw[sj] = b32 ? ld_b32(rb, off) : (uint32_t)ld_b16(rb, off);
+    }
+  }
+  for (uint32_t ck = 0; ck < nchunks; ++ck) {
+    const uint32_t c0 = ck * BKC;
+    if (ck > 0) __syncthreads();                       // previous chunk fully consumed
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+    for (int b = 0; b < HB; ++b) halo_store1(hreg[b], hd_lo[b], hd_hi[b]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t q = wave_n * WTN + si * 32 + 8 * g + 4 * half + e;
-          const uint32_t qh = q / a.PW, qw = q - qh * a.PW;
-          const uint32_t oh = oh0 + qh, ow = ow0 + qw;
-          const bool ok = cok && q < a.PH * a.PW && oh < G.Ho && ow < G.Wo;
-          const float v = apply_act(a.act, acc[si][sj][4 * g + e], a.alpha);
-          store1<DTO>(ry, (img * G.Co + co) * howo + oh * G.Wo + ow, ok, v);
+    for (int b = 0; b < WB; ++b) wts_store1(wreg[b], wd_dst[b]);
+    // items past the batch (large halos, wide weight chunks)
+    for (uint32_t f = HB * NTH; f < h_items; f += NTH) {
+      uint32_t src, g8, lo, hi;
+      halo_item(f + threadIdx.x, src, g8, lo, hi);
+      halo_load1(hreg[0], src, g8, c0);
+      halo_store1(hreg[0], lo, hi);
+    }
+    for (uint32_t f = WB * NTH; f < w_items; f += NTH) {
+      uint32_t src, g8, dst;
+      wts_item(f + threadIdx.x, src, g8, dst);
+#pragma unroll
+      for (int j = 0; j < T; ++j) wts_load1(wreg[0], src, g8, c0, j);
+      wts_store1(wreg[0], dst);
+    }
+    __syncthreads();
+    if (ck + 1 < nchunks)
+      multiply(std::true_type{}, c0 + BKC);
+    else
+      multiply(std::false_type{}, 0u);
+  }
+
+  // ---- epilogue: bias, activation, cast, store -------------------------------
+  float bv[SM];
+#pragma unroll
+  for (int sj = 0; sj < SM; ++sj)
+    bv[sj] = a.bias_dt == DT_F32 ? __uint_as_float(braw[sj])
+             : a.bias_dt == DT_F16 ? widen<DT_F16>(braw[sj]) : widen<DT_BF16>(braw[sj]);
+  const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.y, a.y_bytes);
+  const uint32_t howo = G.Ho * G.Wo;
+  const uint32_t npos = a.PH * a.PW;
+  auto epilogue = [&](auto act_c) {
+    constexpr int ACT = decltype(act_c)::value;
+#pragma unroll
+    for (int si = 0; si < SN; ++si)
+#pragma unroll
+      for (int sj = 0; sj < SM; ++sj) {
+        const uint32_t co = co0 + wave_m * WTM + sj * 32 + lrow;
+        const bool cok = co < G.Co;
+        const uint32_t ybase = (img * G.Co + co) * howo;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t q = wave_n * halo::WTN + si * 32 + 8 * g + 4 * half;
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = act_fn<ACT>(acc[si][sj][4 * g + e] + bv[sj], a.alpha);
+          if (a.vec_y) {
+            // PW % 4 == 0 and Wo % 4 == 0: positions q..q+3 share an output row
+            const uint32_t qh = q / a.PW, qw = q - qh * a.PW;
+            const uint32_t oh = oh0 + qh, ow = ow0 + qw;
+            const bool ok = cok && q < npos && oh < G.Ho && ow < G.Wo;
+            store4<DTO>(ry, ybase + oh * G.Wo + ow, ok, v[0], v[1], v[2], v[3]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t qe = q + e;
+              const uint32_t qh = qe / a.PW, qw = qe - qh * a.PW;
+              const uint32_t oh = oh0 + qh, ow = ow0 + qw;
+              const bool ok = cok && qe < npos && oh < G.Ho && ow < G.Wo;
+              store1<DTO>(ry, ybase + oh * G.Wo + ow, ok, v[e]);
+            }
+          }
         }
       }
-    }
+  };
+  switch (a.act) {
+    case ACT_RELU: epilogue(std::integral_constant<int, ACT_RELU>{}); break;
+    case ACT_LEAKY: epilogue(std::integral_constant<int, ACT_LEAKY>{}); break;
+    case ACT_TANH: epilogue(std::integral_constant<int, ACT_TANH>{}); break;
+    default: epilogue(std::integral_constant<int, ACT_NONE>{}); break;
+  }
 }
 
-template <int DTI, int DTO, int T, int BM, int WTN>
+template <int DTI, int DTO, int T, int BM, int KS>
 inline void launch_conv_halo_t(const HaloArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((conv16_halo_kernel<DTI, DTO, T, BM, WTN>), dim3(a.blocks), dim3(halo::THREADS), 0,
+  hipLaunchKernelGGL((conv16_halo_kernel<DTI, DTO, T, BM, KS>), dim3(a.blocks), dim3(halo::THREADS), 0,
                      s, a);
 }
 

@@ -253,16 +253,25 @@ inline int launch_conv_tile(int tile, const ConvArgs& a, hipStream_t s) {
   }
 }
 
+template <int DTI, int DTO, int T, int BM>
+inline int launch_conv_halo_ks(int ks, const HaloArgs& a, hipStream_t s) {
+  switch (ks) {
+    case 1: launch_conv_halo_t<DTI, DTO, T, BM, 1>(a, s); return 0;
+    case 2: launch_conv_halo_t<DTI, DTO, T, BM, 2>(a, s); return 0;
+    case 4: launch_conv_halo_t<DTI, DTO, T, BM, 4>(a, s); return 0;
+    default: return -1;
+  }
+}
+
 template <int DTI, int DTO>
-inline int launch_conv_halo_tile(int taps, int bm, int wtn, const HaloArgs& a, hipStream_t s) {
+inline int launch_conv_halo_tile(int taps, int bm, int ks, const HaloArgs& a, hipStream_t s) {
   if constexpr (DTI == DT_F32) {
     return -1;
   } else {
-    if (wtn != 64) return -1;
-    if (taps == 9 && bm == 64) { launch_conv_halo_t<DTI, DTO, 9, 64, 64>(a, s); return 0; }
-    if (taps == 9 && bm == 128) { launch_conv_halo_t<DTI, DTO, 9, 128, 64>(a, s); return 0; }
-    if (taps == 1 && bm == 64) { launch_conv_halo_t<DTI, DTO, 1, 64, 64>(a, s); return 0; }
-    if (taps == 1 && bm == 128) { launch_conv_halo_t<DTI, DTO, 1, 128, 64>(a, s); return 0; }
+    if (taps == 9 && bm == 64) return launch_conv_halo_ks<DTI, DTO, 9, 64>(ks, a, s);
+    if (taps == 9 && bm == 128) return launch_conv_halo_ks<DTI, DTO, 9, 128>(ks, a, s);
+    if (taps == 1 && bm == 64) return launch_conv_halo_ks<DTI, DTO, 1, 64>(ks, a, s);
+    if (taps == 1 && bm == 128) return launch_conv_halo_ks<DTI, DTO, 1, 128>(ks, a, s);
     return -1;
   }
 }

@@ -53,6 +53,7 @@ struct HaloArgs {
   uint32_t HR, HC;          // halo rows / columns staged per channel chunk (HC even)
   uint32_t bkc;             // channels per chunk (8, 16, 32 or 64)
   uint32_t co_blocks, w_blocks, h_blocks, blocks;
+  bool vec_y;               // Wo % 4 == 0 and y aligned for 4-element stores
 };
 
 // Per-input-type launchers (one translation unit each).  Return 0, or -1 for
@@ -63,7 +64,7 @@ int launch_gemm_bf16(int dto, int tile, const GemmArgs& a, hipStream_t s);
 int launch_conv_f32(int dto, int tile, const ConvArgs& a, hipStream_t s);
 int launch_conv_f16(int dto, int tile, const ConvArgs& a, hipStream_t s);
 int launch_conv_bf16(int dto, int tile, const ConvArgs& a, hipStream_t s);
-int launch_conv_halo(int dti, int dto, int taps, int bm, int wtn, const HaloArgs& a, hipStream_t s);
+int launch_conv_halo(int dti, int dto, int taps, int bm, int ks, const HaloArgs& a, hipStream_t s);
 int launch_act_cast(int dto, const float* ws, void* out, uint32_t n, int act, float alpha,
                     hipStream_t s);
 

@@ -59,7 +59,7 @@ bool plan_halo(ConvPlan* p, const void* x, const void* w) {
   if (T != 1 && T != 9) return false;
   if (!aligned(x, 4) || !aligned(w, 16)) return false;
   const uint32_t bm = p->Co <= 64 ? 64 : 128;
-  const uint32_t bn = 128, wtn = bn / 2;
+  const uint32_t bn = 128;
   const uint32_t PW = p->Wo < bn ? p->Wo : bn;
   const uint32_t PH = bn / PW;
   const uint32_t HR = (PH - 1) * p->sh + (p->kh - 1) * p->dh + 1;
@@ -72,7 +72,7 @@ bool plan_halo(ConvPlan* p, const void* x, const void* w) {
   while (bkc > 16 && bkc / 2 >= p->C) bkc /= 2;                // no wider than the channel count needs
   if ((uint64_t)HR * HC * bkc * 2 + (uint64_t)T * bm * bkc * 2 > limit) return false;
   p->h_bm = bm;
-  p->h_wtn = wtn;
+  p->h_ks = bkc / 16;                                          // k-steps of 16 channels per tap
   p->h_PH = PH;
   p->h_PW = PW;
   p->h_HR = HR;
