@@ -87,17 +87,23 @@ __device__ __forceinline__ void interleave() {
 }  // namespace halo
 
 // T = taps (kh*kw: 1 or 9), BM = output channels per workgroup (64 or 128),
-// KS = 16-channel k-steps per tap and chunk (1, 2 or 4).
+// KS = 16-channel k-steps per tap and chunk (1, 2 or 4; KS * BM / 64 <= 4).
 template <int DTI, int DTO, int T, int BM, int KS>
 __global__ __launch_bounds__(256, 1) void conv16_halo_kernel(HaloArgs a) {
   static_assert(DTI == DT_F16 || DTI == DT_BF16, "16-bit operands only");
   constexpr int WTM = BM / 2, SM = WTM / 32, SN = halo::WTN / 32;
+  static_assert(KS * SM <= 4, "weight fragments of a chunk must fit in registers");
   constexpr int BKC = 16 * KS, NCH = 2 * KS, ROWB = NCH * 16;
   constexpr int NSTEP = T * KS;
-  constexpr int HB = halo::HB, WB = halo::WB, NTH = halo::THREADS;
-  constexpr int NPF = HB * 8 + WB * T;                  // loads of one batch
+  constexpr int HB = halo::HB, NTH = halo::THREADS;
+  constexpr int RP = BKC * T / 8;                       // 16-byte pieces of one weight row
+  constexpr int RSTR = (RP + 1) * 16;                   // row stride: the pieces and a pad
+  constexpr int NPIECE = BM * (RP + 1);
+  constexpr int NDMA = (NPIECE + 63) / 64;              // direct loads of one chunk (all waves)
+  constexpr int NPF = HB * 8;                           // input loads of one batch
   constexpr int PER = (NPF + NSTEP - 1) / NSTEP;        // batch loads per multiply step
-  __shared__ __attribute__((aligned(16))) uint8_t smem[halo::LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_raw[NDMA * 1024];
+  __shared__ __attribute__((aligned(16))) uint8_t s_halo[halo::LDS_BYTES - NDMA * 1024];
   const ConvGeom& G = a.geom;
 
   // workgroup -> (co block, output-column block, output-row block, image)
@@ -108,7 +114,8 @@ __global__ __launch_bounds__(256, 1) void conv16_halo_kernel(HaloArgs a) {
   const uint32_t img = bid;
   const uint32_t co0 = cb * BM, oh0 = hb * a.PH, ow0 = wb * a.PW;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wave_m = wave >> 1, wave_n = wave & 1;
   const int half = lane >> 5, lrow = lane & 31;
 
@@ -118,7 +125,6 @@ __global__ __launch_bounds__(256, 1) void conv16_halo_kernel(HaloArgs a) {
   const int32_t iw_lo = iw_first & ~1;                 // even (floor) so column pairs are 4-byte aligned
   const uint32_t col_shift = (uint32_t)(iw_first - iw_lo);
   const uint32_t HC = a.HC;                            // halo columns (even)
-  const uint32_t wts_base = a.HR * HC * ROWB;          // weights follow the halo
 
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, a.x_bytes);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w, a.w_bytes);
@@ -126,10 +132,35 @@ __global__ __launch_bounds__(256, 1) void conv16_halo_kernel(HaloArgs a) {
   const uint32_t nchunks = (G.C + BKC - 1) / BKC;
   const uint32_t pairs = HC / 2;
   const uint32_t h_items = a.HR * pairs * NCH;
-  constexpr uint32_t w_items = BM * NCH;
 
-  // ---- staging items ---------------------------------------------------------
-  // input item it = (halo row hr, column pair pr, channel group g):
+  // ---- weights: raw OIHW rows of a chunk, copied straight into LDS ---------
+  // Piece P of the chunk = (row P / (RP+1), piece P % (RP+1)); the last piece
+  // of a row is padding so rows start in different banks.  Padding, rows past
+  // Co and channel groups past C are filled with zeros (out-of-range loads).
+  // Wave w issues the direct loads w, w + 4, ...: piece P advances by 256.
+  auto weights_to_lds = [&](uint32_t c0) {
+    constexpr uint32_t DROW = 256 / (RP + 1), DPC = 256 % (RP + 1);
+    uint32_t row = (uint32_t)(wave * 64 + lane) / (RP + 1);
+    uint32_t pc = (uint32_t)(wave * 64 + lane) - row * (RP + 1);
+    const uint32_t cbase = c0 * T * 2u;
+#pragma unroll
+    for (int k = 0; k < (NDMA + 3) / 4; ++k) {
+      const int i = wave + 4 * k;
+      if (i < NDMA) {
+        const bool ok = pc < RP && row < BM && co0 + row < G.Co && c0 + 8 * (pc / T) < G.C;
+        const uint32_t src = ok ? (co0 + row) * G.C * T * 2u + cbase + pc * 16u : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(s_raw + i * 1024), 16, src, 0, 0, 0);
+      }
+      pc += DPC;
+      row += DROW;
+      if (pc >= RP + 1) {
+        pc -= RP + 1;
+        ++row;
+      }
+    }
+  };
+
+  // ---- input halo: item it = (halo row, column pair, channel group) --------
   // x offset of channel 8g of chunk 0 (kOOB outside the image), channel offset
   // 8g (kFar when the item does not exist), LDS addresses of its two columns.
   auto halo_item = [&](uint32_t it, uint32_t& src, uint32_t& g8, uint32_t& lo, uint32_t& hi) {
@@ -146,18 +177,7 @@ __global__ __launch_bounds__(256, 1) void conv16_halo_kernel(HaloArgs a) {
     lo = exists ? p0 * ROWB + halo::slot<NCH>(p0, g) * 16 : halo::kNone;
     hi = p1 * ROWB + halo::slot<NCH>(p1, g) * 16;
   };
-  // weight item it = (co column col, channel group g): w offset of channel 8g
-  // of chunk 0, channel offset (kFar when absent), LDS address of its tap-0 row.
-  auto wts_item = [&](uint32_t it, uint32_t& src, uint32_t& g8, uint32_t& dst) {
-    const uint32_t g = it % NCH, col = it / NCH;
-    const bool exists = it < w_items && co0 + col < G.Co;
-    src = ((co0 + col) * G.C + g * 8) * T * 2u;
-    g8 = exists ? g * 8 : halo::kFar;
-    dst = it < w_items ? wts_base + col * ROWB + halo::slot<NCH>(col, g) * 16 : halo::kNone;
-  };
-
   uint32_t hreg[HB][8];
-  uint32_t wreg[WB][4 * T];
   auto halo_load1 = [&](uint32_t (&d)[8], uint32_t src, uint32_t g8, uint32_t c0) {
     const bool ok = src != kOOB && c0 + g8 < G.C;    // C % 8 == 0: the group is all in or all out
     const uint32_t off = src + c0 * HW2;
@@ -176,55 +196,22 @@ __global__ __launch_bounds__(256, 1) void conv16_halo_kernel(HaloArgs a) {
     vhi.y = __builtin_amdgcn_perm(d[3], d[2], 0x07060302u);
     vhi.z = __builtin_amdgcn_perm(d[5], d[4], 0x07060302u);
     vhi.w = __builtin_amdgcn_perm(d[7], d[6], 0x07060302u);
-    *reinterpret_cast<u32x4*>(smem + lo) = vlo;
-    *reinterpret_cast<u32x4*>(smem + hi) = vhi;
+    *reinterpret_cast<u32x4*>(s_halo + lo) = vlo;
+    *reinterpret_cast<u32x4*>(s_halo + hi) = vhi;
   };
-  auto wts_load1 = [&](uint32_t (&v)[4 * T], uint32_t src, uint32_t g8, uint32_t c0, int j) {
-    const u32x4 q = ld_b128(rw, c0 + g8 < G.C ? src + c0 * T * 2u + 16u * j : kOOB);
-    v[4 * j + 0] = q.x;
-    v[4 * j + 1] = q.y;
-    v[4 * j + 2] = q.z;
-    v[4 * j + 3] = q.w;
-  };
-  auto wts_store1 = [&](const uint32_t (&v)[4 * T], uint32_t dst) {
-    if (dst == halo::kNone) return;
-    // the loaded run holds (channel e, tap t) at element e*T + t
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      uint32_t o[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int p0 = (2 * k) * T + t, p1 = (2 * k + 1) * T + t;
-        const uint32_t sel = (uint32_t)((p0 & 1) * 2) | ((uint32_t)((p0 & 1) * 2 + 1) << 8) |
-                             ((uint32_t)(4 + (p1 & 1) * 2) << 16) | ((uint32_t)(5 + (p1 & 1) * 2) << 24);
-        o[k] = __builtin_amdgcn_perm(v[p1 >> 1], v[p0 >> 1], sel);
-      }
-      *reinterpret_cast<u32x4*>(smem + dst + t * BM * ROWB) = u32x4{o[0], o[1], o[2], o[3]};
-    }
-  };
-
   // batch descriptors (fixed for the whole workgroup)
   uint32_t hd_src[HB], hd_g8[HB], hd_lo[HB], hd_hi[HB];
-  uint32_t wd_src[WB], wd_g8[WB], wd_dst[WB];
 #pragma unroll
   for (int b = 0; b < HB; ++b) halo_item(b * NTH + threadIdx.x, hd_src[b], hd_g8[b], hd_lo[b], hd_hi[b]);
-#pragma unroll
-  for (int b = 0; b < WB; ++b) wts_item(b * NTH + threadIdx.x, wd_src[b], wd_g8[b], wd_dst[b]);
-
   // load number i of the batch of the chunk starting at channel c0
   auto batch_load = [&](auto i_c, uint32_t c0) {
-    constexpr int i = decltype(i_c)::value;
-    if constexpr (i < HB * 8) {
-      constexpr int b = i / 8, e = i % 8;
-      const bool ok = hd_src[b] != kOOB && c0 + hd_g8[b] < G.C;
-      hreg[b][e] = ld_b32(rx, ok ? hd_src[b] + (c0 + e) * HW2 : kOOB);
-    } else {
-      constexpr int b = (i - HB * 8) / T, j = (i - HB * 8) % T;
-      wts_load1(wreg[b], wd_src[b], wd_g8[b], c0, j);
-    }
+    constexpr int b = decltype(i_c)::value / 8, e = decltype(i_c)::value % 8;
+    const bool ok = hd_src[b] != kOOB && c0 + hd_g8[b] < G.C;
+    hreg[b][e] = ld_b32(rx, ok ? hd_src[b] + (c0 + e) * HW2 : kOOB);
   };
 
-  // ---- fragment addresses (k-step 0); k-step ks flips slot bits by 2*ks ----
+  // ---- fragment addresses --------------------------------------------------
+  // input (k-step 0; k-step ks flips slot bits by 2*ks): tap t, MFMA tile si
   uint32_t h_addr[T][SN];
   {
     uint32_t pos[SN];
@@ -246,24 +233,53 @@ __global__ __launch_bounds__(256, 1) void conv16_halo_kernel(HaloArgs a) {
       }
     }
   }
-  // weights: rows t*BM + row0 share the slot pattern of row0 (BM * t is a multiple of 64)
-  uint32_t w_addr[SM];
+  // weights: this lane's rows (output channels) in the raw chunk
+  uint32_t w_row[SM];
 #pragma unroll
-  for (int sj = 0; sj < SM; ++sj) {
-    const uint32_t row = wave_m * WTM + sj * 32 + lrow;
-    w_addr[sj] = wts_base + row * ROWB + halo::slot<NCH>(row, (uint32_t)half) * 16;
-  }
+  for (int sj = 0; sj < SM; ++sj) w_row[sj] = (uint32_t)(wave_m * WTM + sj * 32 + lrow) * RSTR;
 
-  auto load_frags = [&](auto st_c, u32x4 (&fi)[SN], u32x4 (&fj)[SM]) {
+  // Weight fragments of a chunk: for k-step ks and row tile sj, this lane's
+  // 8 channels (8 * (2 ks + half) ...) of every tap, regrouped from the raw run
+  // (channel e, tap t at element e * T + t); channels past C arrive as zeros.
+  u32x4 afr[KS][T][SM];
+  auto build_weights = [&]() {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int sj = 0; sj < SM; ++sj) {
+        const uint32_t g = 2 * ks + half;
+        const uint8_t* base = s_raw + w_row[sj] + g * 16 * T;
+        uint32_t v[4 * T];
+#pragma unroll
+        for (int j = 0; j < T; ++j) {
+          const u32x4 q = *reinterpret_cast<const u32x4*>(base + 16 * j);
+          v[4 * j + 0] = q.x;
+          v[4 * j + 1] = q.y;
+          v[4 * j + 2] = q.z;
+          v[4 * j + 3] = q.w;
+        }
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          uint32_t o[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int p0 = (2 * k) * T + t, p1 = (2 * k + 1) * T + t;
+            const uint32_t sel = (uint32_t)((p0 & 1) * 2) | ((uint32_t)((p0 & 1) * 2 + 1) << 8) |
+                                 ((uint32_t)(4 + (p1 & 1) * 2) << 16) | ((uint32_t)(5 + (p1 & 1) * 2) << 24);
+            o[k] = __builtin_amdgcn_perm(v[p1 >> 1], v[p0 >> 1], sel);
+          }
+          afr[ks][t][sj] = u32x4{o[0], o[1], o[2], o[3]};
+        }
+      }
+  };
+
+  auto load_b = [&](auto st_c, u32x4 (&fi)[SN]) {
     constexpr int st = decltype(st_c)::value;
-    constexpr int t = st / KS, ks = st % KS;
+    constexpr int ks = st / T, t = st % T;
     constexpr uint32_t flip = (uint32_t)(2 * ks) << 4;
 #pragma unroll
     for (int si = 0; si < SN; ++si)
-      fi[si] = *reinterpret_cast<const u32x4*>(smem + (h_addr[t][si] ^ flip));
-#pragma unroll
-    for (int sj = 0; sj < SM; ++sj)
-      fj[sj] = *reinterpret_cast<const u32x4*>(smem + ((w_addr[sj] + (uint32_t)(t * BM * ROWB)) ^ flip));
+      fi[si] = *reinterpret_cast<const u32x4*>(s_halo + (h_addr[t][si] ^ flip));
   };
 
   f32x16 acc[SN][SM];
@@ -274,16 +290,16 @@ __global__ __launch_bounds__(256, 1) void conv16_halo_kernel(HaloArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[si][sj][r] = 0.0f;
 
-  // All T * KS steps of one chunk; with PREFETCH the batch loads of the chunk
-  // at channel c1 ride along, PER per step.
+  // All KS * T steps of one chunk (k-step major); with PREFETCH the input
+  // batch of the chunk at channel c1 rides along, PER loads per step.
   auto multiply = [&](auto prefetch_c, uint32_t c1) {
     constexpr bool PREFETCH = decltype(prefetch_c)::value;
-    u32x4 fi[2][SN], fj[2][SM];
-    load_frags(std::integral_constant<int, 0>{}, fi[0], fj[0]);
+    u32x4 fi[2][SN];
+    load_b(std::integral_constant<int, 0>{}, fi[0]);
     halo::unroll<NSTEP>([&](auto st_c) {
       constexpr int st = decltype(st_c)::value;
-      constexpr int cur = st & 1;
-      if constexpr (st + 1 < NSTEP) load_frags(std::integral_constant<int, st + 1>{}, fi[cur ^ 1], fj[cur ^ 1]);
+      constexpr int cur = st & 1, ks = st / T, t = st % T;
+      if constexpr (st + 1 < NSTEP) load_b(std::integral_constant<int, st + 1>{}, fi[cur ^ 1]);
       constexpr int v0 = PREFETCH ? (st * PER < NPF ? st * PER : NPF) : 0;
       constexpr int v1 = PREFETCH ? ((st + 1) * PER < NPF ? (st + 1) * PER : NPF) : 0;
       halo::unroll<v1 - v0>([&](auto k_c) {
@@ -292,15 +308,14 @@ __global__ __launch_bounds__(256, 1) void conv16_halo_kernel(HaloArgs a) {
 #pragma unroll
       for (int si = 0; si < SN; ++si)
 #pragma unroll
-        for (int sj = 0; sj < SM; ++sj) mfma_chunk<DTI>(acc[si][sj], fi[cur][si], fj[cur][sj]);
-      constexpr int nd = st + 1 < NSTEP ? SN + SM : 0;
-      constexpr int nv = PREFETCH ? v1 - v0 : 0;
-      halo::interleave<SN * SM, nd, nv>();
+        for (int sj = 0; sj < SM; ++sj) mfma_chunk<DTI>(acc[si][sj], fi[cur][si], afr[ks][t][sj]);
+      halo::interleave<SN * SM, st + 1 < NSTEP ? SN : 0, v1 - v0>();
       __builtin_amdgcn_sched_barrier(0);
     });
   };
 
   // ---- chunk loop ------------------------------------------------------------
+  weights_to_lds(0);
   halo::unroll<NPF>([&](auto i_c) { batch_load(i_c, 0u); });
   // raw bias words of this lane's output channels, converted in the epilogue
   uint32_t braw[SM];
@@ -316,30 +331,27 @@ __global__ __launch_bounds__(256, 1) void conv16_halo_kernel(HaloArgs a) {
   }
   for (uint32_t ck = 0; ck < nchunks; ++ck) {
     const uint32_t c0 = ck * BKC;
-    if (ck > 0) __syncthreads();                       // previous chunk fully consumed
+    const bool more = ck + 1 < nchunks;
+    if (ck > 0) __syncthreads();                       // the previous multiply is done with the halo
 #pragma unroll
     for (int b = 0; b < HB; ++b) halo_store1(hreg[b], hd_lo[b], hd_hi[b]);
-#pragma unroll
-    for (int b = 0; b < WB; ++b) wts_store1(wreg[b], wd_dst[b]);
-    // items past the batch (large halos, wide weight chunks)
+    // input items past the batch (large halos)
     for (uint32_t f = HB * NTH; f < h_items; f += NTH) {
       uint32_t src, g8, lo, hi;
       halo_item(f + threadIdx.x, src, g8, lo, hi);
       halo_load1(hreg[0], src, g8, c0);
       halo_store1(hreg[0], lo, hi);
     }
-    for (uint32_t f = WB * NTH; f < w_items; f += NTH) {
-      uint32_t src, g8, dst;
-      wts_item(f + threadIdx.x, src, g8, dst);
-#pragma unroll
-      for (int j = 0; j < T; ++j) wts_load1(wreg[0], src, g8, c0, j);
-      wts_store1(wreg[0], dst);
-    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);                // this thread's direct weight loads have landed
     __syncthreads();
-    if (ck + 1 < nchunks)
+    build_weights();
+    if (more) {
+      __syncthreads();                                 // every wave has its fragments: reuse the raw rows
+      weights_to_lds(c0 + BKC);
       multiply(std::true_type{}, c0 + BKC);
-    else
+    } else {
       multiply(std::false_type{}, 0u);
+    }
   }
 
   // ---- epilogue: bias, activation, cast, store -------------------------------

@@ -23,6 +23,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;   // LDS destination of direct loads
 
 // Offset used for a masked-off access: beyond every num_records the library
 // creates (all tensors are < 2^31 bytes), so the hardware range check turns

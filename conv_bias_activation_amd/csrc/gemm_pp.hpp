@@ -40,7 +40,6 @@ namespace biasact {
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-typedef __attribute__((address_space(3))) void lds_void;
 
 namespace pp {
 constexpr int BM = 256, BN = 256, BK = 32, THREADS = 512, STAGES = 4;

@@ -255,10 +255,17 @@ inline int launch_conv_tile(int tile, const ConvArgs& a, hipStream_t s) {
 
 template <int DTI, int DTO, int T, int BM>
 inline int launch_conv_halo_ks(int ks, const HaloArgs& a, hipStream_t s) {
+  // a wave keeps KS * BM / 64 weight-fragment sets of a chunk in registers: at most 4
   switch (ks) {
     case 1: launch_conv_halo_t<DTI, DTO, T, BM, 1>(a, s); return 0;
     case 2: launch_conv_halo_t<DTI, DTO, T, BM, 2>(a, s); return 0;
-    case 4: launch_conv_halo_t<DTI, DTO, T, BM, 4>(a, s); return 0;
+    case 4:
+      if constexpr (BM == 64) {
+        launch_conv_halo_t<DTI, DTO, T, BM, 4>(a, s);
+        return 0;
+      } else {
+        return -1;
+      }
     default: return -1;
   }
 }

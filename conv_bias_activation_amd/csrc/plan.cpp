@@ -65,12 +65,20 @@ bool plan_halo(ConvPlan* p, const void* x, const void* w) {
   const uint32_t HR = (PH - 1) * p->sh + (p->kh - 1) * p->dh + 1;
   uint32_t HC = (PW - 1) * p->sw + (p->kw - 1) * p->dw + 2;   // +1 column of parity shift
   HC += HC & 1;
+  // LDS: the halo (HR x HC positions x bkc channels) and one raw weight chunk
+  // (bm rows of bkc*T values plus a 16-byte pad, rounded up to whole 1 KiB
+  // direct loads).  One MFMA k-step consumes 16 channels: chunks of 64, 32 or
+  // 16 (zero-filled past C), with at most four (k-step, 32-row) weight-fragment
+  // sets per wave held in registers.
   const uint64_t limit = 144 * 1024;
-  // one MFMA k-step consumes 16 channels: chunks of 64, 32 or 16 (zero-filled past C)
-  uint32_t bkc = 64;
-  while (bkc > 16 && (uint64_t)HR * HC * bkc * 2 + (uint64_t)T * bm * bkc * 2 > limit) bkc /= 2;
+  auto lds_bytes = [&](uint64_t b) {
+    const uint64_t raw = ((uint64_t)bm * (b * T / 8 + 1) + 63) / 64 * 1024;   // whole 1 KiB direct loads
+    return (uint64_t)HR * HC * b * 2 + raw;
+  };
+  uint32_t bkc = bm == 64 ? 64 : 32;
+  while (bkc > 16 && lds_bytes(bkc) > limit) bkc /= 2;
   while (bkc > 16 && bkc / 2 >= p->C) bkc /= 2;                // no wider than the channel count needs
-  if ((uint64_t)HR * HC * bkc * 2 + (uint64_t)T * bm * bkc * 2 > limit) return false;
+  if (lds_bytes(bkc) > limit) return false;
   p->h_bm = bm;
   p->h_ks = bkc / 16;                                          // k-steps of 16 channels per tap
   p->h_PH = PH;
