@@ -33,8 +33,10 @@ PEAK_HBM_GBS = 8000.0
 
 # Sources that define the headline kernel; the HBM-traffic record in profiles/
 # carries their hash and is reported only while they are unchanged.
-KERNEL_SOURCES = ["gemm_pp.hpp", "epilogue.hpp", "device_common.hpp", "mfma_core.hpp", "launch.hpp"]
+KERNEL_SOURCES = ["gemm_pp.hpp", "epilogue.hpp", "device_common.hpp", "gemm_args.hpp", "tile_map.hpp"]
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gemm_relu_4096_bf16_hbm_traffic.json")
+# kernels of the specialised tile configs (the other ids run the generic kernels)
+KERNEL_NAMES = {6: "gemm16_pp_kernel", 7: "conv16_halo_kernel"}
 
 
 def kernel_fingerprint() -> str:
@@ -223,8 +225,7 @@ def main():
         cfg = {"workload": case.name, "in": case.in_dtype, "out": case.out_dtype, "act": case.act}
     cfg["tile"] = ba.tile_config_name(tile)
     line = {
-        "metric": "TFLOP/s of fused act(A.B+bias) (gemm_relu_4096_bf16: M=N=K=4096, bf16 in/out, "
-                  "fp32 bias, ReLU)",
+        "metric": "TFLOP/s of fused act(A\u00b7B+bias) and conv2d+tanh; % of MI355X MFMA peak",
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -240,7 +241,9 @@ def main():
         "frac_of_peak": round(tflops / peak, 4),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 4), "traffic": measured_traffic(case.name),
-                     "kernel": "gemm_bias_act_kernel", "per_launch_flops": case.flops,
+                     "kernel": KERNEL_NAMES.get(tile, "gemm_bias_act_kernel" if isinstance(case, wl.GemmCase)
+                                                else "conv_bias_act_kernel"),
+                     "per_launch_flops": case.flops,
                      "mean_launch_ms": round(ms, 5)},
         "wall_s_timed": round(wall, 3),
     }

@@ -33,8 +33,8 @@
 #pragma once
 
 #include "epilogue.hpp"
-#include "launch.hpp"
-#include "mfma_core.hpp"
+#include "gemm_args.hpp"
+#include "tile_map.hpp"
 
 namespace biasact {
 

@@ -23,6 +23,7 @@
 #pragma once
 
 #include "device_common.hpp"
+#include "tile_map.hpp"
 
 namespace biasact {
 
@@ -45,24 +46,6 @@ struct Tile {
   static constexpr int stage_bytes = a_bytes + b_bytes;
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32x32");
 };
-
-// Workgroup id -> output tile.  The dispatcher hands workgroup b to XCD b % 8;
-// renumbering gives every XCD one contiguous range of tile ids, and the
-// grouped raster (8 tile rows at a time, row index fastest) makes the tiles of
-// one range share A row panels and B column panels in that XCD's L2.
-__device__ __forceinline__ void map_tile(uint32_t bid, uint32_t nblk, uint32_t tiles_m,
-                                         uint32_t tiles_n, uint32_t& tm, uint32_t& tn) {
-  const uint32_t xcd = bid & 7u, idx = bid >> 3;
-  const uint32_t q = nblk >> 3, r = nblk & 7u;
-  const uint32_t t = xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
-  constexpr uint32_t GM = 8;
-  const uint32_t per_group = GM * tiles_n;
-  const uint32_t first_m = (t / per_group) * GM;
-  const uint32_t gm = min(tiles_m - first_m, GM);
-  const uint32_t in = t - (t / per_group) * per_group;
-  tm = first_m + in % gm;
-  tn = in / gm;
-}
 
 // Pack EPC loaded elements (each in the low bits of a dword) into a chunk.
 template <int DT>
