@@ -61,7 +61,7 @@ bool plan_halo(ConvPlan* p, const void* x, const void* w) {
   const uint32_t bm = p->Co <= 64 ? 64 : 128;
   const uint32_t bn = 128;
   const uint32_t PW = p->Wo < bn ? p->Wo : bn;
-  const uint32_t PH = bn / PW;
+  const uint32_t PH = bn / PW < p->Ho ? bn / PW : p->Ho;      // rows of one image only
   const uint32_t HR = (PH - 1) * p->sh + (p->kh - 1) * p->dh + 1;
   uint32_t HC = (PW - 1) * p->sw + (p->kw - 1) * p->dw + 2;   // +1 column of parity shift
   HC += HC & 1;

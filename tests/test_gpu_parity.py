@@ -239,6 +239,11 @@ HALO_SHAPES = [
     (2, 256, 7, 6, 130, 3, 3, (2, 1), (1, 1, 0, 1), (1, 2)),
     (1, 24, 30, 2, 64, 3, 3, (3, 1), (1, 1, 1, 1), (1, 1)),
     (2, 32, 5, 40, 17, 1, 1, (1, 2), (1, 0, 0, 1), (1, 1)),
+    (2, 40, 10, 12, 48, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1)),      # 64-channel chunk, 40 used
+    (1, 104, 9, 8, 64, 3, 3, (1, 1), (0, 1, 1, 0), (1, 1)),       # two chunks, the last partial
+    (2, 16, 11, 14, 80, 3, 3, (2, 2), (1, 1, 1, 1), (1, 1)),      # 128-row blocks, one k-step
+    (1, 72, 6, 16, 200, 1, 1, (1, 1), (0, 0, 0, 0), (1, 1)),      # three chunks, two co blocks
+    (1, 64, 9, 130, 32, 3, 3, (2, 2), (1, 1, 1, 1), (1, 1)),      # halo past one load batch
 ]
 
 
