@@ -97,6 +97,11 @@ int launch_conv_plan(const ConvPlan& p, const void* x, const void* w, const void
     h.h_blocks = p.h_h_blocks;
     h.blocks = p.h_blocks;
     h.vec_y = p.Wo % 4 == 0 && ((uintptr_t)y % (dto == DT_F32 ? 16u : 8u)) == 0;
+    h.hrcp = p.h_hrcp;
+    h.div_hc = make_fastdiv(p.h_HC ? p.h_HC : 1u);
+    h.kstr = p.h_kstr;
+    h.kpad = p.h_kpad;
+    h.div_kstr = make_fastdiv(p.h_kstr ? p.h_kstr : 1u);
     rc = launch_conv_halo(p.dti, dto, (int)(p.kh * p.kw), (int)p.h_bm, (int)p.h_ks, h, s);
     if (rc) return kErrUnsupported;
     return hipGetLastError() == hipSuccess ? kOk : kErrHip;

@@ -1,0 +1,274 @@
+// conv_halo32.hpp — implicit-GEMM conv2d + bias + activation for fp32
+// operands, any filter larger than 1x1, stride, padding and dilation ([FCT]
+// "这个算子到底在算什么": y = act(conv2d(x, filter, bias)); "双 Kernel 是怎么
+// 分工的": weights as the co x k operand, input features as the k x spatial
+// operand).
+//
+// v_mfma_f32_32x32x2_f32 takes one value per lane from each operand: lane l
+// gives row l % 32 at reduction index k0 + l / 32.  Both operands are therefore
+// read from LDS one float per lane, and the reduction keeps the filter's own
+// order, k = c * T + t (t = r * kw + s), so a shallow stem (C = 3, 7x7) wastes
+// no MFMA lanes on padding.
+//
+// Workgroup: 256 threads (2 x 2 waves), BM output channels x a patch of PH
+// output rows x PW output columns of one image (at most 128 positions).  A
+// channel chunk of bkc channels is staged as
+//   halo   [c][row][col] : input rows ih = oh0*sh - pt + row, columns
+//                          iw = ow0*sw - pl + col; HR*HC floats per channel,
+//                          rounded up to 64
+//   wts    [co][h][kp]   : filter value k = 2 kp + h of the chunk for each
+//                          output channel; rows KSTR = 2 KPAD + 4 floats
+//                          apart (16-byte reads of 16 rows hit all banks)
+// both by direct loads: one wave instruction moves 64 consecutive floats of
+// one channel's halo, or of the weight block (padding, rows
+// past Co, channels past C and positions outside the image arrive as zeros).
+// Chunks alternate between two LDS arrays, so the next chunk's copy overlaps
+// the multiply of the current one and the multiply's reads carry no wait on
+// it; two buffers and the offset table fit 80 KB, so two workgroups share a
+// CU.  A table of the halo offset of every reduction index of a chunk lets a
+// lane fetch the offsets of 4 steps with one read.
+#pragma once
+
+#include <utility>
+
+#include "epilogue.hpp"
+#include "launch.hpp"
+#include "mfma_core.hpp"
+
+namespace biasact {
+
+namespace halo32 {
+constexpr int THREADS = 256;
+constexpr int KOFF_MAX = 256;               // reduction-offset table: 2 x (k-pairs per chunk)
+constexpr int BUF_FLOATS = (80 * 1024 - KOFF_MAX * 4) / 8;   // two chunk buffers, 80 KB in all
+constexpr int WTN = 64;                     // positions per wave (two 32-wide MFMA tiles)
+}  // namespace halo32
+
+// BM = output channels per workgroup (64 or 128).
+template <int DTO, int BM>
+__global__ __launch_bounds__(256, 2) void conv32_halo_kernel(HaloArgs a) {
+  constexpr int WTM = BM / 2, SM = WTM / 32, SN = halo32::WTN / 32;
+  __shared__ __attribute__((aligned(16))) float s_buf0[halo32::BUF_FLOATS];
+  __shared__ __attribute__((aligned(16))) float s_buf1[halo32::BUF_FLOATS];
+  __shared__ __attribute__((aligned(16))) uint32_t s_koff[halo32::KOFF_MAX];
+  const ConvGeom& G = a.geom;
+
+  // workgroup -> (co block, output-column block, output-row block, image)
+  uint32_t bid = blockIdx.x;
+  const uint32_t cb = bid % a.co_blocks;  bid /= a.co_blocks;
+  const uint32_t wb = bid % a.w_blocks;   bid /= a.w_blocks;
+  const uint32_t hb = bid % a.h_blocks;   bid /= a.h_blocks;
+  const uint32_t img = bid;
+  const uint32_t co0 = cb * BM, oh0 = hb * a.PH, ow0 = wb * a.PW;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave_m = wave >> 1, wave_n = wave & 1;
+  const int half = lane >> 5, lrow = lane & 31;
+
+  const int32_t ih_lo = (int32_t)oh0 * G.sh - G.pt;
+  const int32_t iw_lo = (int32_t)ow0 * G.sw - G.pl;
+  const uint32_t HR = a.HR, HC = a.HC, HRC = a.hrcp;       // halo rows, columns, floats per channel
+  const uint32_t T = G.kh * G.kw, KSTR = a.kstr, BKC = a.bkc;
+  const uint32_t KPAD = a.kpad;                             // k-pairs per chunk, multiple of 4
+  const uint32_t wofs = BKC * HRC;                          // weights follow the halo
+  const uint32_t nchunks = (G.C + BKC - 1) / BKC;
+
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, a.x_bytes);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w, a.w_bytes);
+
+  // ---- reduction offsets: s_koff[h * KPAD + kp] = halo offset of k = 2 kp + h
+  // (k = c*T + r*kw + s -> c*HRC + r*dh*HC + s*dw; 0 past the chunk's indices,
+  // where the weights are zero and the input is a finite value of the patch)
+  for (uint32_t idx = threadIdx.x; idx < 2 * KPAD; idx += halo32::THREADS) {
+    const uint32_t h = idx >= KPAD, kp = idx - h * KPAD, k = 2 * kp + h;
+    uint32_t off = 0;
+    if (k < BKC * T) {
+      const uint32_t c = k / T, t = k - c * T, r = t / G.kw, sx = t - r * G.kw;
+      off = c * HRC + r * G.dh * HC + sx * G.dw;
+    }
+    s_koff[idx] = off;
+  }
+
+  // ---- one chunk into LDS buffer s (direct loads, 64 floats per instruction)
+  // halo: channel cl, floats [64 pb, 64 pb + 64) of its HR x HC positions;
+  // position f = (row, col) reads x at (ih_lo + row, iw_lo + col).
+  const uint32_t npi = HRC / 64;                            // instructions per channel
+  const uint32_t n_halo = BKC * npi;
+  const uint32_t n_wts = (BM * KSTR + 63) / 64;             // weight instructions
+  auto chunk_to_lds = [&](float* s, uint32_t c0) {
+    const uint32_t bc = G.C - c0 < BKC ? G.C - c0 : BKC;  // channels in this chunk
+    uint32_t cl = 0, pbk = (uint32_t)wave;                  // instruction wave + 4j = (cl, pbk)
+    while (pbk >= npi) { pbk -= npi; ++cl; }
+    for (uint32_t i = wave; i < n_halo; i += 4) {
+      const uint32_t f = pbk * 64 + lane;
+      const uint32_t row = fdiv(f, a.div_hc), col = f - row * HC;
+      const int32_t ih = ih_lo + (int32_t)row;
+      const int32_t iw = iw_lo + (int32_t)col;
+      const bool ok = cl < bc && row < HR && (uint32_t)ih < G.H && (uint32_t)iw < G.W;
+      const uint32_t src = ok ? (((img * G.C + c0 + cl) * G.H + (uint32_t)ih) * G.W + (uint32_t)iw) * 4u : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(s + cl * HRC + pbk * 64), 4, src, 0, 0, 0);
+      pbk += 4;
+      while (pbk >= npi) { pbk -= npi; ++cl; }
+    }
+    // weight block [row][h][kp] = w[co0 + row][c0*T + 2 kp + h]; rows KSTR apart
+    const uint32_t kc = bc * T;
+    for (uint32_t i = wave; i < n_wts; i += 4) {
+      const uint32_t f = i * 64 + lane;
+      const uint32_t row = fdiv(f, a.div_kstr), rem = f - row * KSTR;
+      const uint32_t h = rem >= KPAD, kp = rem - h * KPAD, k = 2 * kp + h;
+      const bool ok = row < BM && co0 + row < G.Co && rem < 2 * KPAD && k < kc;
+      const uint32_t src = ok ? ((co0 + row) * G.C * T + c0 * T + k) * 4u : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(s + wofs + i * 64), 4, src, 0, 0, 0);
+    }
+  };
+
+  // ---- per-lane read offsets (floats) ----------------------------------------
+  uint32_t pb[SN];                     // halo offset of this lane's positions (tap 0, channel 0)
+#pragma unroll
+  for (int si = 0; si < SN; ++si) {
+    const uint32_t q = wave_n * halo32::WTN + si * 32 + lrow;
+    const uint32_t qh = q / a.PW, qw = q - qh * a.PW;
+    // lanes past the patch read position 0 (in range); their results are never stored
+    pb[si] = q < a.PH * a.PW ? qh * G.sh * HC + qw * G.sw : 0u;
+  }
+  uint32_t wrow[SM];                   // this lane's weights: row, parity half
+#pragma unroll
+  for (int sj = 0; sj < SM; ++sj)
+    wrow[sj] = wofs + (uint32_t)(wave_m * WTM + sj * 32 + lrow) * KSTR + (uint32_t)half * KPAD;
+  const uint32_t krow = (uint32_t)half * KPAD;
+
+  f32x16 acc[SN][SM];
+#pragma unroll
+  for (int si = 0; si < SN; ++si)
+#pragma unroll
+    for (int sj = 0; sj < SM; ++sj)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[si][sj][r] = 0.0f;
+
+  // Multiply one chunk in groups of 4 k-pairs: one 16-byte read gives a lane
+  // its 4 reduction offsets, one per row tile its 4 weights, then 4 * SN input
+  // reads; the next group's reads are issued before this group's MFMAs.
+  struct Group {
+    float b[4][SN];
+    u32x4 w[SM];
+  };
+  auto load_group = [&](const float* s, uint32_t g, Group& G4) {
+    const u32x4 ko = *reinterpret_cast<const u32x4*>(s_koff + krow + 4 * g);
+#pragma unroll
+    for (int sj = 0; sj < SM; ++sj) G4.w[sj] = *reinterpret_cast<const u32x4*>(s + wrow[sj] + 4 * g);
+    const uint32_t kos[4] = {ko.x, ko.y, ko.z, ko.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int si = 0; si < SN; ++si) G4.b[j][si] = s[pb[si] + kos[j]];
+  };
+  auto mma_group = [&](const Group& G4) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int si = 0; si < SN; ++si)
+#pragma unroll
+        for (int sj = 0; sj < SM; ++sj)
+          acc[si][sj] = __builtin_amdgcn_mfma_f32_32x32x2f32(G4.b[j][si], __uint_as_float(G4.w[sj][j]),
+                                                             acc[si][sj], 0, 0, 0);
+  };
+  auto multiply = [&](const float* s, uint32_t kc) {
+    const uint32_t ngroups = ((kc + 1) / 2 + 3) / 4;
+    Group g0, g1;
+    load_group(s, 0, g0);
+    uint32_t g = 0;
+    for (; g + 2 <= ngroups; g += 2) {
+      load_group(s, g + 1, g1);
+      mma_group(g0);
+      if (g + 2 < ngroups) load_group(s, g + 2, g0);
+      mma_group(g1);
+    }
+    if (g < ngroups) mma_group(g0);
+  };
+
+  // ---- chunk loop: chunk ck in buffer ck % 2 -------------------------------
+  chunk_to_lds(s_buf0, 0);
+  // raw bias words of this lane's output channels, converted in the epilogue
+  uint32_t braw[SM];
+  {
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.bias, a.bias_bytes);
+    const bool b32 = a.bias_dt == DT_F32;
+#pragma unroll
+    for (int sj = 0; sj < SM; ++sj) {
+      const uint32_t co = co0 + wave_m * WTM + sj * 32 + lrow;
+      const uint32_t off = co < G.Co ? co * (b32 ? 4u : 2u) : kOOB;
+      braw[sj] = b32 ? ld_b32(rb, off) : (uint32_t)ld_b16(rb, off);
+    }
+  }
+  for (uint32_t ck = 0; ck < nchunks; ++ck) {
+    const uint32_t c0 = ck * BKC;
+    const uint32_t bc = G.C - c0 < BKC ? G.C - c0 : BKC;
+    __builtin_amdgcn_s_waitcnt(0x0F70);                // this thread's direct loads of chunk ck have landed
+    __syncthreads();                                   // ... everyone's, and chunk ck-1's buffer is free
+    if (ck & 1) {
+      if (ck + 1 < nchunks) chunk_to_lds(s_buf0, c0 + BKC);
+      multiply(s_buf1, bc * T);
+    } else {
+      if (ck + 1 < nchunks) chunk_to_lds(s_buf1, c0 + BKC);
+      multiply(s_buf0, bc * T);
+    }
+  }
+
+  // ---- epilogue: bias, activation, cast, store -------------------------------
+  float bvv[SM];
+#pragma unroll
+  for (int sj = 0; sj < SM; ++sj)
+    bvv[sj] = a.bias_dt == DT_F32 ? __uint_as_float(braw[sj])
+              : a.bias_dt == DT_F16 ? widen<DT_F16>(braw[sj]) : widen<DT_BF16>(braw[sj]);
+  const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.y, a.y_bytes);
+  const uint32_t howo = G.Ho * G.Wo;
+  const uint32_t npos = a.PH * a.PW;
+  auto epilogue = [&](auto act_c) {
+    constexpr int ACT = decltype(act_c)::value;
+#pragma unroll
+    for (int si = 0; si < SN; ++si)
+#pragma unroll
+      for (int sj = 0; sj < SM; ++sj) {
+        const uint32_t co = co0 + wave_m * WTM + sj * 32 + lrow;
+        const bool cok = co < G.Co;
+        const uint32_t ybase = (img * G.Co + co) * howo;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t q = wave_n * halo32::WTN + si * 32 + 8 * g + 4 * half;
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = act_fn<ACT>(acc[si][sj][4 * g + e] + bvv[sj], a.alpha);
+          if (a.vec_y) {
+            // PW % 4 == 0 and Wo % 4 == 0: positions q..q+3 share an output row
+            const uint32_t qh = q / a.PW, qw = q - qh * a.PW;
+            const uint32_t oh = oh0 + qh, ow = ow0 + qw;
+            const bool ok = cok && q < npos && oh < G.Ho && ow < G.Wo;
+            store4<DTO>(ry, ybase + oh * G.Wo + ow, ok, v[0], v[1], v[2], v[3]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t qe = q + e;
+              const uint32_t qh = qe / a.PW, qw = qe - qh * a.PW;
+              const uint32_t oh = oh0 + qh, ow = ow0 + qw;
+              const bool ok = cok && qe < npos && oh < G.Ho && ow < G.Wo;
+              store1<DTO>(ry, ybase + oh * G.Wo + ow, ok, v[e]);
+            }
+          }
+        }
+      }
+  };
+  switch (a.act) {
+    case ACT_RELU: epilogue(std::integral_constant<int, ACT_RELU>{}); break;
+    case ACT_LEAKY: epilogue(std::integral_constant<int, ACT_LEAKY>{}); break;
+    case ACT_TANH: epilogue(std::integral_constant<int, ACT_TANH>{}); break;
+    default: epilogue(std::integral_constant<int, ACT_NONE>{}); break;
+  }
+}
+
+template <int DTO, int BM>
+inline void launch_conv32_halo_t(const HaloArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((conv32_halo_kernel<DTO, BM>), dim3(a.blocks), dim3(halo32::THREADS), 0, s, a);
+}
+
+}  // namespace biasact

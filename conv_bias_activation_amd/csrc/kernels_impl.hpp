@@ -6,6 +6,7 @@
 #pragma once
 
 #include "conv_halo.hpp"
+#include "conv_halo32.hpp"
 #include "epilogue.hpp"
 #include "gemm_pp.hpp"
 #include "launch.hpp"
@@ -273,6 +274,10 @@ inline int launch_conv_halo_ks(int ks, const HaloArgs& a, hipStream_t s) {
 template <int DTI, int DTO>
 inline int launch_conv_halo_tile(int taps, int bm, int ks, const HaloArgs& a, hipStream_t s) {
   if constexpr (DTI == DT_F32) {
+    (void)taps;
+    (void)ks;
+    if (bm == 64) { launch_conv32_halo_t<DTO, 64>(a, s); return 0; }
+    if (bm == 128) { launch_conv32_halo_t<DTO, 128>(a, s); return 0; }
     return -1;
   } else {
     if (taps == 9 && bm == 64) return launch_conv_halo_ks<DTI, DTO, 9, 64>(ks, a, s);

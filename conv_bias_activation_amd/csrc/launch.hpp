@@ -40,6 +40,12 @@ struct HaloArgs {
   uint32_t bkc;             // channels per chunk (8, 16, 32 or 64)
   uint32_t co_blocks, w_blocks, h_blocks, blocks;
   bool vec_y;               // Wo % 4 == 0 and y aligned for 4-element stores
+  // fp32 kernel only
+  uint32_t hrcp;            // halo floats per channel (HR * HC rounded up to 64)
+  FastDiv div_hc;
+  uint32_t kpad;            // k-pairs per chunk rounded up to 4
+  uint32_t kstr;            // weight row stride in LDS (floats): 2 kpad + 4
+  FastDiv div_kstr;
 };
 
 // Per-input-type launchers (one translation unit each).  Return 0, or -1 for

@@ -51,10 +51,67 @@ int pick_tile(const int* order, int n_order, int64_t rows_j, int64_t rows_i, int
   return best;
 }
 
+// Halo-kernel parameters for an fp32 conv (any filter larger than 1x1, any
+// stride, padding and dilation): the channel chunk is the widest whose halo (HR x HC positions
+// per channel, rounded up to 64) and weight block (bm rows of 2 kpad + 4
+// floats) fit one of two chunk buffers, evened out over the chunks it takes.  Returns false when a single
+// channel does not fit.
+bool plan_halo32(ConvPlan* p, const void* x, const void* w) {
+  // A 1x1 filter is a strided GEMM: the generic kernel stages exactly the
+  // operands it reads and measures faster there.
+  if (p->kh * p->kw == 1) return false;
+  if (!aligned(x, 4) || !aligned(w, 4)) return false;
+  const uint64_t T = (uint64_t)p->kh * p->kw;
+  const uint32_t bm = p->Co <= 64 ? 64 : 128;
+  const uint32_t bn = 128;
+  const uint32_t PW = p->Wo < bn ? p->Wo : bn;
+  const uint32_t PH = bn / PW < p->Ho ? bn / PW : p->Ho;      // rows of one image only
+  const uint64_t HR = (uint64_t)(PH - 1) * p->sh + (uint64_t)(p->kh - 1) * p->dh + 1;
+  const uint64_t HC = (uint64_t)(PW - 1) * p->sw + (uint64_t)(p->kw - 1) * p->dw + 1;
+  const uint64_t HRCP = (HR * HC + 63) / 64 * 64;
+  const uint64_t limit = (80 * 1024 - 256 * 4) / 8;          // floats per buffer (two + offset table)
+  auto kpad = [&](uint64_t b) { return ((b * T + 1) / 2 + 3) / 4 * 4; };
+  auto kstr = [&](uint64_t b) { return 2 * kpad(b) + 4; };
+  auto fits = [&](uint64_t b) {
+    return kpad(b) <= 128 && b * HRCP + (bm * kstr(b) + 63) / 64 * 64 <= limit;
+  };
+  if (!fits(1)) return false;
+  uint64_t lo = 1, hi = p->C;                                  // largest chunk that fits
+  while (lo < hi) {
+    const uint64_t mid = (lo + hi + 1) / 2;
+    if (fits(mid)) lo = mid;
+    else hi = mid - 1;
+  }
+  const uint64_t n = (p->C + lo - 1) / lo;                    // same chunk count, even split
+  lo = (p->C + n - 1) / n;
+  p->h_bm = bm;
+  p->h_ks = 0;
+  p->h_PH = PH;
+  p->h_PW = PW;
+  p->h_HR = (uint32_t)HR;
+  p->h_HC = (uint32_t)HC;
+  p->h_hrcp = (uint32_t)HRCP;
+  p->h_bkc = (uint32_t)lo;
+  p->h_kpad = (uint32_t)kpad(lo);
+  p->h_kstr = (uint32_t)kstr(lo);
+  p->h_co_blocks = (p->Co + bm - 1) / bm;
+  p->h_w_blocks = (p->Wo + PW - 1) / PW;
+  p->h_h_blocks = (p->Ho + PH - 1) / PH;
+  const uint64_t blocks = (uint64_t)p->h_co_blocks * p->h_w_blocks * p->h_h_blocks * p->N;
+  if (blocks >= (1u << 31)) return false;
+  p->h_blocks = (uint32_t)blocks;
+  return true;
+}
+
 // Halo-kernel parameters for a conv (16-bit operands, C % 8 == 0, even W,
-// 1x1 or 3x3 filters, aligned x / w).  Returns false when it does not apply.
+// 1x1 or 3x3 filters, aligned x / w; fp32 operands go to plan_halo32).
+// Returns false when it does not apply.
 bool plan_halo(ConvPlan* p, const void* x, const void* w) {
-  if (p->dti == kF32 || p->C % 8 != 0 || p->W % 2 != 0) return false;
+  p->h_hrcp = 0;
+  p->h_kpad = 0;
+  p->h_kstr = 0;
+  if (p->dti == kF32) return plan_halo32(p, x, w);
+  if (p->C % 8 != 0 || p->W % 2 != 0) return false;
   const uint32_t T = p->kh * p->kw;
   if (T != 1 && T != 9) return false;
   if (!aligned(x, 4) || !aligned(w, 16)) return false;

@@ -268,6 +268,35 @@ def test_conv_halo_path_vs_oracle(ba, shape, types):
             ba.force_tile_config(-1)
 
 
+HALO32_SHAPES = [
+    (2, 3, 20, 22, 64, 7, 7, (2, 2), (3, 3, 3, 3), (1, 1)),       # stem-like: C = 3, two chunks
+    (1, 5, 13, 9, 70, 5, 5, (1, 1), (2, 1, 0, 2), (1, 1)),        # odd C, asymmetric pads, 128-row block
+    (2, 40, 9, 11, 33, 1, 3, (1, 2), (0, 0, 1, 1), (1, 3)),       # 1x3 filter, dilation 3, odd chunk K
+    (1, 300, 6, 7, 20, 3, 3, (1, 1), (1, 1, 1, 1), (2, 1)),       # many chunks, the last partial
+    (3, 16, 30, 140, 8, 3, 2, (2, 3), (1, 2, 1, 0), (1, 1)),      # 3x2 filter, wide rows
+    (1, 7, 5, 300, 130, 1, 2, (1, 1), (0, 0, 0, 1), (1, 1)),      # rows past 128 columns, two co blocks
+]
+
+
+@pytest.mark.parametrize("shape", HALO32_SHAPES, ids=lambda s: "x".join(map(str, s[:7])))
+@pytest.mark.parametrize("to", ["f32", "bf16", "f16"])
+def test_conv_halo32_path_vs_oracle(ba, shape, to):
+    N, C, H, W, Co, kh, kw, st, pd, dl = shape
+    for tile in (-1, 7):
+        ba.force_tile_config(tile)
+        try:
+            for j, act in enumerate(("tanh", "relu")):
+                case = _ccase(N, C, H, W, Co, kh, kw, st, pd, dl, "f32", to, "f32", act)
+                inp = wl.gen_conv(case, seed=71 + j)
+                y = values_of(run_conv(case, inp), to)
+                ref, floor = conv_reference(case, inp)
+                rep = check(y, ref, floor, case)
+                _report(f"halo32 {shape} {to} {act} tile {tile}", rep)
+                assert rep["ok"], rep
+        finally:
+            ba.force_tile_config(-1)
+
+
 def test_conv_no_bias(ba):
     case = _ccase(2, 8, 10, 10, 16, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1), "bf16", "f32", None, "none")
     inp = wl.gen_conv(case, seed=2)
