@@ -69,6 +69,8 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="gemm_relu_4096_bf16")
     ap.add_argument("--no-others", action="store_true", help="skip the other workloads")
+    ap.add_argument("--path", choices=("fused", "2k"), default="fused",
+                    help="time the fused kernel (default) or the two-kernel ablation for --workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle sample time")
     ap.add_argument("--tile", type=int, default=-1, help="force a tile config (tuning)")
@@ -208,7 +210,7 @@ def main():
     case = wl.CASES[args.workload]
     if args.tile >= 0:
         ba.force_tile_config(args.tile)
-    step, _ = make_step(case, 0, "fused")
+    step, _ = make_step(case, 0, args.path)
     ms, wall = time_steps(step, args.steps, args.warmup)
     tflops = case.flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[case.in_dtype]
@@ -224,6 +226,8 @@ def main():
                                                   case.out_dtype))
         cfg = {"workload": case.name, "in": case.in_dtype, "out": case.out_dtype, "act": case.act}
     cfg["tile"] = ba.tile_config_name(tile)
+    if args.path != "fused":
+        cfg["path"] = args.path
     line = {
         "metric": "TFLOP/s of fused act(A\u00b7B+bias) and conv2d+tanh; % of MI355X MFMA peak",
         "value": round(tflops, 2),

@@ -6,8 +6,8 @@ int launch_act_cast(int dto, const float* ws, void* out, uint32_t n, int act, fl
                     hipStream_t s) {
   if (n == 0) return 0;
   const uint32_t threads = 256;
-  uint32_t blocks = (n + threads * 8 - 1) / (threads * 8);
-  if (blocks > 256u * 32u) blocks = 256u * 32u;     // grid-stride beyond 32 waves of workgroups per CU
+  uint32_t blocks = (n + threads * 16 - 1) / (threads * 16);
+  if (blocks > 256u * 8u) blocks = 256u * 8u;       // 8 workgroups per CU, then grid-stride
   switch (dto) {
     case DT_F32:
       hipLaunchKernelGGL(act_cast_kernel<DT_F32>, dim3(blocks), dim3(threads), 0, s, ws, out, n, act, alpha);

@@ -162,37 +162,56 @@ __global__ __launch_bounds__(TL::threads, 1) void conv_bias_act_kernel(ConvArgs 
 // ---------------------------------------------------------------------------
 // Second kernel of the two-kernel path: out[i] = cast(act(ws[i])) over a
 // packed fp32 workspace that already holds A.B + bias (GEMM, [M,N]) or
-// conv + bias (conv, NCHW).  Each thread handles 8 consecutive elements with
-// two 16-byte loads; grid-stride over the array.
+// conv + bias (conv, NCHW).  Each thread handles 16 consecutive elements per
+// pass with four 16-byte loads issued before any is used (64 bytes in flight
+// per lane); grid-stride over the array with a grid that fills every CU.
 // ---------------------------------------------------------------------------
 template <int DTO>
 __global__ __launch_bounds__(256) void act_cast_kernel(const float* ws, void* out, uint32_t n,
                                                        int act, float alpha) {
+  constexpr uint32_t EPT = 16;
   const __amdgpu_buffer_rsrc_t ri = make_rsrc(ws, n * 4u);
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(out, n * (uint32_t)Elem<DTO>::bytes);
-  const uint32_t stride = gridDim.x * blockDim.x * 8u;
-  for (uint32_t base = (blockIdx.x * blockDim.x + threadIdx.x) * 8u; base < n; base += stride) {
-    const bool full = base + 8u <= n;
-    u32x4 v0 = ld_b128(ri, full ? base * 4u : kOOB);
-    u32x4 v1 = ld_b128(ri, full ? base * 4u + 16u : kOOB);
-    float z[8] = {__uint_as_float(v0.x), __uint_as_float(v0.y), __uint_as_float(v0.z),
-                  __uint_as_float(v0.w), __uint_as_float(v1.x), __uint_as_float(v1.y),
-                  __uint_as_float(v1.z), __uint_as_float(v1.w)};
-    if (!full) {
+  const uint32_t stride = gridDim.x * blockDim.x * EPT;
+  auto run = [&](auto act_c) {
+    constexpr int ACT = decltype(act_c)::value;
+    for (uint32_t base = (blockIdx.x * blockDim.x + threadIdx.x) * EPT; base < n; base += stride) {
+      const bool full = base + EPT <= n;
+      float z[EPT];
+      if (full) {
+        u32x4 v[EPT / 4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        z[e] = __uint_as_float(ld_b32(ri, base + e < n ? (base + e) * 4u : kOOB));
+        for (uint32_t q = 0; q < EPT / 4; ++q) v[q] = ld_b128(ri, (base + 4 * q) * 4u);
+#pragma unroll
+        for (uint32_t q = 0; q < EPT / 4; ++q) {
+          z[4 * q + 0] = __uint_as_float(v[q].x);
+          z[4 * q + 1] = __uint_as_float(v[q].y);
+          z[4 * q + 2] = __uint_as_float(v[q].z);
+          z[4 * q + 3] = __uint_as_float(v[q].w);
+        }
+      } else {
+#pragma unroll
+        for (uint32_t e = 0; e < EPT; ++e)
+          z[e] = __uint_as_float(ld_b32(ri, base + e < n ? (base + e) * 4u : kOOB));
+      }
+      float y[EPT];
+#pragma unroll
+      for (uint32_t e = 0; e < EPT; ++e) y[e] = act_fn<ACT>(z[e], alpha);
+      if (full) {
+#pragma unroll
+        for (uint32_t q = 0; q < EPT / 4; ++q)
+          store4<DTO>(ro, base + 4 * q, true, y[4 * q], y[4 * q + 1], y[4 * q + 2], y[4 * q + 3]);
+      } else {
+#pragma unroll
+        for (uint32_t e = 0; e < EPT; ++e) store1<DTO>(ro, base + e, base + e < n, y[e]);
+      }
     }
-    float y[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = apply_act(act, z[e], alpha);
-    if (full) {
-      store4<DTO>(ro, base, true, y[0], y[1], y[2], y[3]);
-      store4<DTO>(ro, base + 4, true, y[4], y[5], y[6], y[7]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) store1<DTO>(ro, base + e, base + e < n, y[e]);
-    }
+  };
+  switch (act) {                        // activation dispatched once per thread
+    case ACT_RELU: run(std::integral_constant<int, ACT_RELU>{}); break;
+    case ACT_LEAKY: run(std::integral_constant<int, ACT_LEAKY>{}); break;
+    case ACT_TANH: run(std::integral_constant<int, ACT_TANH>{}); break;
+    default: run(std::integral_constant<int, ACT_NONE>{}); break;
   }
 }
 
