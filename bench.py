@@ -69,6 +69,8 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="gemm_relu_4096_bf16")
     ap.add_argument("--no-others", action="store_true", help="skip the other workloads")
+    ap.add_argument("--halo-variant", type=int, default=-1,
+                    help="force the fp16/bf16 conv-halo variant (0 widest, 1 and 2 two per CU; -1 auto)")
     ap.add_argument("--path", choices=("fused", "2k"), default="fused",
                     help="time the fused kernel (default) or the two-kernel ablation for --workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -210,6 +212,8 @@ def main():
     case = wl.CASES[args.workload]
     if args.tile >= 0:
         ba.force_tile_config(args.tile)
+    if args.halo_variant >= 0:
+        ba.force_halo_variant(args.halo_variant)
     step, _ = make_step(case, 0, args.path)
     ms, wall = time_steps(step, args.steps, args.warmup)
     tflops = case.flops / (ms * 1e-3) / 1e12
@@ -228,6 +232,8 @@ def main():
     cfg["tile"] = ba.tile_config_name(tile)
     if args.path != "fused":
         cfg["path"] = args.path
+    if args.halo_variant >= 0:
+        cfg["halo_variant"] = args.halo_variant
     line = {
         "metric": "TFLOP/s of fused act(A\u00b7B+bias) and conv2d+tanh; % of MI355X MFMA peak",
         "value": round(tflops, 2),

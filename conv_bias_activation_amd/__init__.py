@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     conv2d_bias_act_workspace_size,
     conv_out_hw,
     dtypes_code,
+    force_halo_variant,
     force_tile_config,
     gemm_bias_act,
     gemm_bias_act_2k,

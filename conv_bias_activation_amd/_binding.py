@@ -52,6 +52,8 @@ def _load():
     l.biasact_conv_tile_config.restype = ctypes.c_int
     l.biasact_force_tile_config.argtypes = [ctypes.c_int]
     l.biasact_force_tile_config.restype = ctypes.c_int
+    l.biasact_force_halo_variant.argtypes = [ctypes.c_int]
+    l.biasact_force_halo_variant.restype = ctypes.c_int
     return l
 
 
@@ -250,3 +252,8 @@ def conv_tile_config(N, Co, Ho, Wo, K, dtypes: int) -> int:
 
 def force_tile_config(i: int):
     _check(lib.biasact_force_tile_config(int(i)), "force_tile_config")
+
+
+def force_halo_variant(v: int):
+    """-1 automatic; 0 widest conv-halo tile; 1, 2 the two-per-CU variants."""
+    _check(lib.biasact_force_halo_variant(int(v)), "force_halo_variant")

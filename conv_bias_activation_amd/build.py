@@ -1,6 +1,8 @@
 """Build libbiasact.so (gfx950) in-tree with hipcc.
 
-    python -m conv_bias_activation_amd.build        # always recompiles
+    python conv_bias_activation_amd/build.py        # always recompiles
+
+(Run it as a script: importing the package would first load the library.)
 
 Every HIP translation unit is compiled for gfx950 only, with packed-fp32
 instructions disabled (-Xclang -target-feature -Xclang -packed-fp32-ops), in

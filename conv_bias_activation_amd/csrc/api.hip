@@ -102,7 +102,7 @@ int launch_conv_plan(const ConvPlan& p, const void* x, const void* w, const void
     h.kstr = p.h_kstr;
     h.kpad = p.h_kpad;
     h.div_kstr = make_fastdiv(p.h_kstr ? p.h_kstr : 1u);
-    rc = launch_conv_halo(p.dti, dto, (int)(p.kh * p.kw), (int)p.h_bm, (int)p.h_ks, h, s);
+    rc = launch_conv_halo(p.dti, dto, (int)(p.kh * p.kw), (int)p.h_bm, (int)p.h_ks, (int)p.h_sn, h, s);
     if (rc) return kErrUnsupported;
     return hipGetLastError() == hipSuccess ? kOk : kErrHip;
   }
@@ -226,6 +226,12 @@ int biasact_conv_tile_config(int64_t N, int64_t Co, int64_t Ho, int64_t Wo, int6
 int biasact_force_tile_config(int id) {
   if (id < -1 || id >= kNumTileConfigs) return kErrInvalid;
   set_forced_tile(id);
+  return kOk;
+}
+
+int biasact_force_halo_variant(int v) {
+  if (v < -1 || v > 2) return kErrInvalid;
+  set_forced_halo_variant(v);
   return kOk;
 }
 

@@ -16,7 +16,10 @@
 // BKC = 16 * KS (KS = 1, 2, 4 MFMA k-steps per tap; zero-filled past C).
 //
 // Workgroup: 256 threads (2 x 2 waves), BM output channels x a patch of PH
-// output rows x PW output columns (positions q = row * PW + col, at most 128).
+// output rows x PW output columns (positions q = row * PW + col, at most
+// 64 * SN).  Variants small enough for two workgroups per CU (80 KB of LDS,
+// two fragment sets per wave) let one workgroup's staging and epilogue
+// overlap another's MFMAs.
 // Staging items: input (halo row, column pair, 8 channels) — eight 4-byte
 // loads transposed in registers into two 16-byte LDS writes; weights (output
 // channel, 8 channels) — T 16-byte loads (8 channels x T taps are contiguous
@@ -45,10 +48,10 @@ namespace biasact {
 
 namespace halo {
 constexpr int THREADS = 256;
-constexpr int LDS_BYTES = 144 * 1024;
-constexpr int HB = 4;     // input items per thread in the precomputed batch
+constexpr int LDS_ONE = 144 * 1024;     // LDS of a workgroup that has its CU alone
+constexpr int LDS_TWO = 80 * 1024;      // LDS of a workgroup that shares its CU with another
+constexpr int HB = 4;     // input items per thread in the precomputed batch (2 at occupancy 2)
 constexpr int WB = 2;     // weight items per thread in the precomputed batch
-constexpr int WTN = 64;   // positions per wave (two 32-wide MFMA tiles)
 constexpr uint32_t kNone = 0xffffffffu;   // "no LDS write" marker of an item
 constexpr uint32_t kFar = 1u << 30;       // channel offset that fails every c < C test
 
@@ -86,16 +89,23 @@ __device__ __forceinline__ void interleave() {
 }
 }  // namespace halo
 
+// Two workgroups share a CU when a wave holds at most two weight-fragment
+// sets and two accumulator tiles (then 256 registers per lane suffice).
+template <int BM, int KS, int SN>
+constexpr int occupancy() { return KS * (BM / 64) <= 2 && SN * (BM / 64) <= 2 ? 2 : 1; }
+
 // T = taps (kh*kw: 1 or 9), BM = output channels per workgroup (64 or 128),
-// KS = 16-channel k-steps per tap and chunk (1, 2 or 4; KS * BM / 64 <= 4).
-template <int DTI, int DTO, int T, int BM, int KS>
-__global__ __launch_bounds__(256, 1) void conv16_halo_kernel(HaloArgs a) {
+// KS = 16-channel k-steps per tap and chunk (1, 2 or 4; KS * BM / 64 <= 4),
+// SN = 32-position MFMA tiles per wave (2 x SN x 32 positions per workgroup).
+template <int DTI, int DTO, int T, int BM, int KS, int SN>
+__global__ __launch_bounds__(256, (occupancy<BM, KS, SN>())) void conv16_halo_kernel(HaloArgs a) {
   static_assert(DTI == DT_F16 || DTI == DT_BF16, "16-bit operands only");
-  constexpr int WTM = BM / 2, SM = WTM / 32, SN = halo::WTN / 32;
+  constexpr int WTM = BM / 2, SM = WTM / 32, WTN = 32 * SN;
+  constexpr int LDS = occupancy<BM, KS, SN>() == 2 ? halo::LDS_TWO : halo::LDS_ONE;
   static_assert(KS * SM <= 4, "weight fragments of a chunk must fit in registers");
   constexpr int BKC = 16 * KS, NCH = 2 * KS, ROWB = NCH * 16;
   constexpr int NSTEP = T * KS;
-  constexpr int HB = halo::HB, NTH = halo::THREADS;
+  constexpr int HB = occupancy<BM, KS, SN>() == 2 ? 2 : halo::HB, NTH = halo::THREADS;
   constexpr int RP = BKC * T / 8;                       // 16-byte pieces of one weight row
   constexpr int RSTR = (RP + 1) * 16;                   // row stride: the pieces and a pad
   constexpr int NPIECE = BM * (RP + 1);
@@ -103,7 +113,7 @@ __global__ __launch_bounds__(256, 1) void conv16_halo_kernel(HaloArgs a) {
   constexpr int NPF = HB * 8;                           // input loads of one batch
   constexpr int PER = (NPF + NSTEP - 1) / NSTEP;        // batch loads per multiply step
   __shared__ __attribute__((aligned(16))) uint8_t s_raw[NDMA * 1024];
-  __shared__ __attribute__((aligned(16))) uint8_t s_halo[halo::LDS_BYTES - NDMA * 1024];
+  __shared__ __attribute__((aligned(16))) uint8_t s_halo[LDS - NDMA * 1024];
   const ConvGeom& G = a.geom;
 
   // workgroup -> (co block, output-column block, output-row block, image)
@@ -217,7 +227,7 @@ __global__ __launch_bounds__(256, 1) void conv16_halo_kernel(HaloArgs a) {
     uint32_t pos[SN];
 #pragma unroll
     for (int si = 0; si < SN; ++si) {
-      const uint32_t q = wave_n * halo::WTN + si * 32 + lrow;
+      const uint32_t q = wave_n * WTN + si * 32 + lrow;
       const uint32_t qh = q / a.PW, qw = q - qh * a.PW;
       // lanes past the patch read halo position 0 (in range); their results are never stored
       pos[si] = q < a.PH * a.PW ? (qh * G.sh) * HC + qw * G.sw + col_shift : 0u;
@@ -374,7 +384,7 @@ __global__ __launch_bounds__(256, 1) void conv16_halo_kernel(HaloArgs a) {
         const uint32_t ybase = (img * G.Co + co) * howo;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const uint32_t q = wave_n * halo::WTN + si * 32 + 8 * g + 4 * half;
+          const uint32_t q = wave_n * WTN + si * 32 + 8 * g + 4 * half;
           float v[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = act_fn<ACT>(acc[si][sj][4 * g + e] + bv[sj], a.alpha);
@@ -405,9 +415,9 @@ __global__ __launch_bounds__(256, 1) void conv16_halo_kernel(HaloArgs a) {
   }
 }
 
-template <int DTI, int DTO, int T, int BM, int KS>
+template <int DTI, int DTO, int T, int BM, int KS, int SN>
 inline void launch_conv_halo_t(const HaloArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((conv16_halo_kernel<DTI, DTO, T, BM, KS>), dim3(a.blocks), dim3(halo::THREADS), 0,
+  hipLaunchKernelGGL((conv16_halo_kernel<DTI, DTO, T, BM, KS, SN>), dim3(a.blocks), dim3(halo::THREADS), 0,
                      s, a);
 }
 

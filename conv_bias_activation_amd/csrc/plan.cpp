@@ -18,6 +18,7 @@ bool valid_dt(int dt) { return dt == kF32 || dt == kF16 || dt == kBF16; }
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 std::atomic<int> g_forced_tile{-1};
+std::atomic<int> g_forced_halo{-1};
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -86,6 +87,7 @@ bool plan_halo32(ConvPlan* p, const void* x, const void* w) {
   lo = (p->C + n - 1) / n;
   p->h_bm = bm;
   p->h_ks = 0;
+  p->h_sn = 2;
   p->h_PH = PH;
   p->h_PW = PW;
   p->h_HR = (uint32_t)HR;
@@ -115,46 +117,88 @@ bool plan_halo(ConvPlan* p, const void* x, const void* w) {
   const uint32_t T = p->kh * p->kw;
   if (T != 1 && T != 9) return false;
   if (!aligned(x, 4) || !aligned(w, 16)) return false;
-  const uint32_t bm = p->Co <= 64 ? 64 : 128;
-  const uint32_t bn = 128;
-  const uint32_t PW = p->Wo < bn ? p->Wo : bn;
-  const uint32_t PH = bn / PW < p->Ho ? bn / PW : p->Ho;      // rows of one image only
-  const uint32_t HR = (PH - 1) * p->sh + (p->kh - 1) * p->dh + 1;
-  uint32_t HC = (PW - 1) * p->sw + (p->kw - 1) * p->dw + 2;   // +1 column of parity shift
-  HC += HC & 1;
+  // One configuration = (bm output channels, 2 x 32 sn positions, LDS budget).
   // LDS: the halo (HR x HC positions x bkc channels) and one raw weight chunk
   // (bm rows of bkc*T values plus a 16-byte pad, rounded up to whole 1 KiB
   // direct loads).  One MFMA k-step consumes 16 channels: chunks of 64, 32 or
   // 16 (zero-filled past C), with at most four (k-step, 32-row) weight-fragment
-  // sets per wave held in registers.
-  const uint64_t limit = 144 * 1024;
-  auto lds_bytes = [&](uint64_t b) {
-    const uint64_t raw = ((uint64_t)bm * (b * T / 8 + 1) + 63) / 64 * 1024;   // whole 1 KiB direct loads
-    return (uint64_t)HR * HC * b * 2 + raw;
+  // sets per wave held in registers -- two where two workgroups share a CU.
+  struct Cfg {
+    uint32_t bm, sn, ks, PH, PW, HR, HC, bkc, co_blocks, w_blocks, h_blocks;
+    uint64_t blocks;
+    bool ok;
   };
-  uint32_t bkc = bm == 64 ? 64 : 32;
-  while (bkc > 16 && lds_bytes(bkc) > limit) bkc /= 2;
-  while (bkc > 16 && bkc / 2 >= p->C) bkc /= 2;                // no wider than the channel count needs
-  if (lds_bytes(bkc) > limit) return false;
-  p->h_bm = bm;
-  p->h_ks = bkc / 16;                                          // k-steps of 16 channels per tap
-  p->h_PH = PH;
-  p->h_PW = PW;
-  p->h_HR = HR;
-  p->h_HC = HC;
-  p->h_bkc = bkc;
-  p->h_co_blocks = (p->Co + bm - 1) / bm;
-  p->h_w_blocks = (p->Wo + PW - 1) / PW;
-  p->h_h_blocks = (p->Ho + PH - 1) / PH;
-  const uint64_t blocks = (uint64_t)p->h_co_blocks * p->h_w_blocks * p->h_h_blocks * p->N;
-  if (blocks >= (1u << 31)) return false;
-  p->h_blocks = (uint32_t)blocks;
+  auto make = [&](uint32_t bm, uint32_t sn, bool shared) {
+    Cfg c{};
+    c.bm = bm;
+    c.sn = sn;
+    const uint32_t bn = 64 * sn;
+    c.PW = p->Wo < bn ? p->Wo : bn;
+    c.PH = bn / c.PW < p->Ho ? bn / c.PW : p->Ho;            // rows of one image only
+    c.HR = (c.PH - 1) * p->sh + (p->kh - 1) * p->dh + 1;
+    c.HC = (c.PW - 1) * p->sw + (p->kw - 1) * p->dw + 2;     // +1 column of parity shift
+    c.HC += c.HC & 1;
+    // the kernel's occupancy rule: two workgroups per CU (80 KB of LDS each)
+    // when a wave holds at most two fragment sets and two accumulator tiles
+    auto limit = [&](uint64_t b) {
+      const bool two = (b / 16) * (bm / 64) <= 2 && sn * (bm / 64) <= 2;
+      return (uint64_t)(two ? 80 : 144) * 1024;
+    };
+    auto lds_bytes = [&](uint64_t b) {
+      const uint64_t raw = ((uint64_t)bm * (b * T / 8 + 1) + 63) / 64 * 1024;
+      return (uint64_t)c.HR * c.HC * b * 2 + raw;
+    };
+    const uint32_t max_sets = shared ? 2 : 4;                  // k-steps x 32-row tiles per wave
+    uint32_t bkc = 16 * (max_sets / (bm / 64));
+    if (bkc > 64) bkc = 64;
+    while (bkc > 16 && bkc / 2 >= p->C) bkc /= 2;            // no wider than the channel count needs
+    while (bkc > 16 && lds_bytes(bkc) > limit(bkc)) bkc /= 2;
+    c.ok = lds_bytes(bkc) <= limit(bkc) && (!shared || sn * (bm / 64) <= 2);
+    c.bkc = bkc;
+    c.ks = bkc / 16;
+    c.co_blocks = (p->Co + bm - 1) / bm;
+    c.w_blocks = (p->Wo + c.PW - 1) / c.PW;
+    c.h_blocks = (p->Ho + c.PH - 1) / c.PH;
+    c.blocks = (uint64_t)c.co_blocks * c.w_blocks * c.h_blocks * p->N;
+    c.ok = c.ok && c.blocks < (1u << 31);
+    return c;
+  };
+  // A workgroup per CU with the widest tile, unless that leaves fewer than two
+  // workgroups per CU: then tiles half as wide in channels (or positions) that
+  // two workgroups can share a CU with, when they give 1.5x the workgroups.
+  Cfg c = make(p->Co <= 64 ? 64 : 128, 2, false);
+  const Cfg alt[2] = {make(64, 2, true), make(64, 1, true)};
+  const int forced = forced_halo_variant();
+  if (forced == 1 || forced == 2) {
+    if (alt[forced - 1].ok) c = alt[forced - 1];
+  } else if (forced < 0 && c.ok && c.blocks < 512) {
+    for (const Cfg& a2 : alt)
+      if (a2.ok && a2.blocks * 2 >= c.blocks * 3) {
+        c = a2;
+        break;
+      }
+  }
+  if (!c.ok) return false;
+  p->h_bm = c.bm;
+  p->h_ks = c.ks;                                              // k-steps of 16 channels per tap
+  p->h_sn = c.sn;
+  p->h_PH = c.PH;
+  p->h_PW = c.PW;
+  p->h_HR = c.HR;
+  p->h_HC = c.HC;
+  p->h_bkc = c.bkc;
+  p->h_co_blocks = c.co_blocks;
+  p->h_w_blocks = c.w_blocks;
+  p->h_h_blocks = c.h_blocks;
+  p->h_blocks = (uint32_t)c.blocks;
   return true;
 }
 
 }  // namespace
 
 int forced_tile() { return g_forced_tile.load(std::memory_order_relaxed); }
+int forced_halo_variant() { return g_forced_halo.load(std::memory_order_relaxed); }
+void set_forced_halo_variant(int v) { g_forced_halo.store(v, std::memory_order_relaxed); }
 void set_forced_tile(int id) { g_forced_tile.store(id, std::memory_order_relaxed); }
 
 int select_gemm_tile(int64_t M, int64_t N, int64_t /*K*/, int /*dti*/) {

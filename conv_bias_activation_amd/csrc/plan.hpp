@@ -46,7 +46,7 @@ struct ConvPlan {
   int tile;
   uint32_t tiles_m, tiles_n;
   // halo kernel (tile 7) parameters
-  uint32_t h_bm, h_ks, h_PH, h_PW, h_HR, h_HC, h_bkc, h_co_blocks, h_w_blocks, h_h_blocks, h_blocks;
+  uint32_t h_bm, h_ks, h_sn, h_PH, h_PW, h_HR, h_HC, h_bkc, h_co_blocks, h_w_blocks, h_h_blocks, h_blocks;
   uint32_t h_hrcp, h_kpad, h_kstr;   // fp32 halo kernel (see plan_halo32)
 };
 
@@ -63,6 +63,9 @@ int select_conv_tile(int64_t N, int64_t Co, int64_t Ho, int64_t Wo, int64_t K, i
 // -1 = automatic
 int forced_tile();
 void set_forced_tile(int id);
+// -1 automatic, 0 widest tile, 1 / 2 the two-per-CU variants (see biasact.h)
+int forced_halo_variant();
+void set_forced_halo_variant(int v);
 
 const char* status_string(int s);
 

@@ -67,6 +67,15 @@ def test_tile_table_introspection():
         ba.force_tile_config(n)
 
 
+def test_halo_variant_override_range():
+    for v in (-1, 0, 1, 2):
+        ba.force_halo_variant(v)
+    ba.force_halo_variant(-1)
+    for v in (-2, 3):
+        with pytest.raises(ValueError):
+            ba.force_halo_variant(v)
+
+
 def test_workspace_sizes():
     assert L.gemm_bias_act_workspace_size(4096, 4096) == 4096 * 4096 * 4
     assert L.gemm_bias_act_workspace_size(-1, 3) == 0

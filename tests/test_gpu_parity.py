@@ -253,8 +253,10 @@ HALO_SHAPES = [
 def test_conv_halo_path_vs_oracle(ba, shape, types):
     N, C, H, W, Co, kh, kw, st, pd, dl = shape
     ti, to, tb = types
-    for tile in (-1, 7):
+    # automatic choice, then every conv-halo variant forced
+    for tile, variant in ((-1, -1), (7, 0), (7, 1), (7, 2)):
         ba.force_tile_config(tile)
+        ba.force_halo_variant(variant)
         try:
             for j, act in enumerate(("tanh", "relu")):
                 case = _ccase(N, C, H, W, Co, kh, kw, st, pd, dl, ti, to, tb, act)
@@ -262,10 +264,11 @@ def test_conv_halo_path_vs_oracle(ba, shape, types):
                 y = values_of(run_conv(case, inp), to)
                 ref, floor = conv_reference(case, inp)
                 rep = check(y, ref, floor, case)
-                _report(f"halo {shape} {types} {act} tile {tile}", rep)
+                _report(f"halo {shape} {types} {act} tile {tile} variant {variant}", rep)
                 assert rep["ok"], rep
         finally:
             ba.force_tile_config(-1)
+            ba.force_halo_variant(-1)
 
 
 HALO32_SHAPES = [
