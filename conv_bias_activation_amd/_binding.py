@@ -24,6 +24,15 @@ def _load():
     if not os.path.exists(lib_path):
         raise ImportError(f"{lib_path} is not built; run `python -m conv_bias_activation_amd.build` "
                           "(or __graft_entry__.build()) first")
+    # The library and torch must share one HIP runtime: device pointers and
+    # stream handles cross the boundary.  torch ships its own libamdhip64
+    # with the same soname the library links against, so loading torch first
+    # makes the dynamic linker bind the library to that instance; loading the
+    # library first would bring in a second runtime beside torch's.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     l = ctypes.CDLL(lib_path)
     vp, i64, u32, i32p = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.POINTER(ctypes.c_int32)
     l.gemm_bias_act.argtypes = [vp, vp, vp, vp, i64, i64, i64, u32, ctypes.c_int, ctypes.c_float, vp]
@@ -42,6 +51,10 @@ def _load():
     l.conv2d_bias_act_workspace_size.restype = ctypes.c_size_t
     l.biasact_status_string.argtypes = [ctypes.c_int]
     l.biasact_status_string.restype = ctypes.c_char_p
+    l.biasact_last_hip_error.argtypes = []
+    l.biasact_last_hip_error.restype = ctypes.c_int
+    l.biasact_last_hip_error_string.argtypes = []
+    l.biasact_last_hip_error_string.restype = ctypes.c_char_p
     l.biasact_num_tile_configs.argtypes = []
     l.biasact_num_tile_configs.restype = ctypes.c_int
     l.biasact_tile_config_name.argtypes = [ctypes.c_int, ctypes.c_char_p, ctypes.c_size_t]
@@ -70,6 +83,9 @@ def _check(status: int, what: str):
     msg = f"{what}: {status_string(status)}"
     if status in (BA_ERR_INVALID, BA_ERR_UNSUPPORTED):
         raise ValueError(msg)
+    if status == BA_ERR_HIP:
+        msg += (f" (hipError {lib.biasact_last_hip_error()}: "
+                f"{lib.biasact_last_hip_error_string().decode()})")
     raise BiasActError(status, msg)
 
 

@@ -10,13 +10,13 @@ int launch_act_cast(int dto, const float* ws, void* out, uint32_t n, int act, fl
   if (blocks > 256u * 8u) blocks = 256u * 8u;       // 8 workgroups per CU, then grid-stride
   switch (dto) {
     case DT_F32:
-      hipLaunchKernelGGL(act_cast_kernel<DT_F32>, dim3(blocks), dim3(threads), 0, s, ws, out, n, act, alpha);
+      launch_kernel(act_cast_kernel<DT_F32>, dim3(blocks), dim3(threads), s, ws, out, n, act, alpha);
       return 0;
     case DT_F16:
-      hipLaunchKernelGGL(act_cast_kernel<DT_F16>, dim3(blocks), dim3(threads), 0, s, ws, out, n, act, alpha);
+      launch_kernel(act_cast_kernel<DT_F16>, dim3(blocks), dim3(threads), s, ws, out, n, act, alpha);
       return 0;
     case DT_BF16:
-      hipLaunchKernelGGL(act_cast_kernel<DT_BF16>, dim3(blocks), dim3(threads), 0, s, ws, out, n, act, alpha);
+      launch_kernel(act_cast_kernel<DT_BF16>, dim3(blocks), dim3(threads), s, ws, out, n, act, alpha);
       return 0;
     default:
       return -1;

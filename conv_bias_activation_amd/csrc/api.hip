@@ -7,11 +7,29 @@
 
 #include "biasact.h"
 #include "launch.hpp"
+#include "launch_kernel.hpp"
 #include "plan.hpp"
 
 using namespace biasact;
 
+namespace biasact {
+thread_local hipError_t t_launch_error = hipSuccess;
+}
+
 namespace {
+
+// the HIP error behind the most recent BA_ERR_HIP on this thread
+thread_local hipError_t t_last_hip = hipSuccess;
+
+// Status of the launches queued since the last call (launch_kernel records
+// the first refusal).
+int launch_status() {
+  const hipError_t e = t_launch_error;
+  t_launch_error = hipSuccess;
+  if (e == hipSuccess) return kOk;
+  t_last_hip = e;
+  return kErrHip;
+}
 
 int launch_gemm_plan(const GemmPlan& p, const void* A, const void* B, const void* bias, void* C,
                      int dto, int act, float alpha, hipStream_t s) {
@@ -43,7 +61,7 @@ int launch_gemm_plan(const GemmPlan& p, const void* A, const void* B, const void
     default: return kErrUnsupported;
   }
   if (rc) return kErrUnsupported;
-  return hipGetLastError() == hipSuccess ? kOk : kErrHip;
+  return launch_status();
 }
 
 int launch_conv_plan(const ConvPlan& p, const void* x, const void* w, const void* bias, void* y,
@@ -104,7 +122,7 @@ int launch_conv_plan(const ConvPlan& p, const void* x, const void* w, const void
     h.div_kstr = make_fastdiv(p.h_kstr ? p.h_kstr : 1u);
     rc = launch_conv_halo(p.dti, dto, (int)(p.kh * p.kw), (int)p.h_bm, (int)p.h_ks, (int)p.h_sn, h, s);
     if (rc) return kErrUnsupported;
-    return hipGetLastError() == hipSuccess ? kOk : kErrHip;
+    return launch_status();
   }
   switch (p.dti) {
     case DT_F32: rc = launch_conv_f32(dto, p.tile, a, s); break;
@@ -113,14 +131,14 @@ int launch_conv_plan(const ConvPlan& p, const void* x, const void* w, const void
     default: return kErrUnsupported;
   }
   if (rc) return kErrUnsupported;
-  return hipGetLastError() == hipSuccess ? kOk : kErrHip;
+  return launch_status();
 }
 
 int launch_second_kernel(int dto, const void* ws, void* out, uint64_t n, int act, float alpha,
                          hipStream_t s) {
   if (launch_act_cast(dto, static_cast<const float*>(ws), out, (uint32_t)n, act, alpha, s))
     return kErrUnsupported;
-  return hipGetLastError() == hipSuccess ? kOk : kErrHip;
+  return launch_status();
 }
 
 }  // namespace
@@ -197,6 +215,12 @@ int conv2d_bias_act_2k(const void* x, const void* w, const void* bias, void* y, 
 }
 
 const char* biasact_status_string(int status) { return status_string(status); }
+
+int biasact_last_hip_error(void) { return (int)t_last_hip; }
+
+const char* biasact_last_hip_error_string(void) {
+  return t_last_hip == hipSuccess ? "no HIP error" : hipGetErrorString(t_last_hip);
+}
 
 int biasact_num_tile_configs(void) { return kNumTileConfigs; }
 

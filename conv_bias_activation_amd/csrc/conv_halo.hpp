@@ -42,6 +42,7 @@
 
 #include "epilogue.hpp"
 #include "launch.hpp"
+#include "launch_kernel.hpp"
 #include "mfma_core.hpp"
 
 namespace biasact {
@@ -417,8 +418,7 @@ __global__ __launch_bounds__(256, (occupancy<BM, KS, SN>())) void conv16_halo_ke
 
 template <int DTI, int DTO, int T, int BM, int KS, int SN>
 inline void launch_conv_halo_t(const HaloArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((conv16_halo_kernel<DTI, DTO, T, BM, KS, SN>), dim3(a.blocks), dim3(halo::THREADS), 0,
-                     s, a);
+  launch_kernel(conv16_halo_kernel<DTI, DTO, T, BM, KS, SN>, dim3(a.blocks), dim3(halo::THREADS), s, a);
 }
 
 }  // namespace biasact

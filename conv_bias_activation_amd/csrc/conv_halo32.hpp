@@ -33,6 +33,7 @@
 
 #include "epilogue.hpp"
 #include "launch.hpp"
+#include "launch_kernel.hpp"
 #include "mfma_core.hpp"
 
 namespace biasact {
@@ -268,7 +269,7 @@ __global__ __launch_bounds__(256, 2) void conv32_halo_kernel(HaloArgs a) {
 
 template <int DTO, int BM>
 inline void launch_conv32_halo_t(const HaloArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((conv32_halo_kernel<DTO, BM>), dim3(a.blocks), dim3(halo32::THREADS), 0, s, a);
+  launch_kernel(conv32_halo_kernel<DTO, BM>, dim3(a.blocks), dim3(halo32::THREADS), s, a);
 }
 
 }  // namespace biasact

@@ -34,6 +34,7 @@
 
 #include "epilogue.hpp"
 #include "gemm_args.hpp"
+#include "launch_kernel.hpp"
 #include "tile_map.hpp"
 
 namespace biasact {
@@ -251,7 +252,7 @@ __global__ __launch_bounds__(512, 1) void gemm16_pp_kernel(GemmArgs a) {
 
 template <int DTI, int DTO>
 inline void launch_gemm_pp(const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((gemm16_pp_kernel<DTI, DTO>), dim3(a.tiles_m * a.tiles_n), dim3(pp::THREADS), 0, s, a);
+  launch_kernel(gemm16_pp_kernel<DTI, DTO>, dim3(a.tiles_m * a.tiles_n), dim3(pp::THREADS), s, a);
 }
 
 }  // namespace biasact

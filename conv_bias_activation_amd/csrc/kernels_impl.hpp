@@ -10,17 +10,19 @@
 #include "epilogue.hpp"
 #include "gemm_pp.hpp"
 #include "launch.hpp"
+#include "launch_kernel.hpp"
 #include "mfma_core.hpp"
 
 namespace biasact {
 
 // ---------------------------------------------------------------------------
 // C[M,N] = act(A[M,K] . B[K,N] + bias[N])   ([MLR] 概述 / 样例规格;
-// [FMR] fused_matmul_relu).  One workgroup per BM x BN output tile.
+// [FMR] fused_matmul_relu).  One workgroup per BM x BN output tile.  NK > 0:
+// the reduction is at most NK k-tiles, all loaded at once (main_loop_allk).
 // ---------------------------------------------------------------------------
-template <int DTI, int DTO, class TL>
+template <int DTI, int DTO, class TL, int NK = 0>
 __global__ __launch_bounds__(TL::threads, 1) void gemm_bias_act_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TL::stage_bytes];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[(NK > 2 ? NK : 2) * TL::stage_bytes];
   constexpr int BK = kChunks * Elem<DTI>::epc;
 
   uint32_t tm, tn;
@@ -30,9 +32,10 @@ __global__ __launch_bounds__(TL::threads, 1) void gemm_bias_act_kernel(GemmArgs 
   const int wave_m = wave / TL::WAVES_N, wave_n = wave % TL::WAVES_N;
   const int half = lane >> 5, lrow = lane & 31;
 
-  // accumulator starts at the bias (the extra reduction term)
+  // accumulator starts at the bias (the extra reduction term), fetched once
+  // the first operand loads are in flight
   f32x16 acc[TL::SN][TL::SM];
-  {
+  auto init_acc = [&]() {
     uint32_t idx[TL::SN * 16];
     float bv[TL::SN * 16];
 #pragma unroll
@@ -49,14 +52,17 @@ __global__ __launch_bounds__(TL::threads, 1) void gemm_bias_act_kernel(GemmArgs 
 #pragma unroll
       for (int sj = 0; sj < TL::SM; ++sj) acc[si][sj] = b;
     }
-  }
+  };
 
   DenseRowLoader<DTI, TL> la;
   DenseColLoader<DTI, TL> lb;
   la.init(a.A, a.a_bytes, a.M, a.K, m0, a.vec_a);
   lb.init(a.B, a.b_bytes, a.K, a.N, n0, a.vec_b);
   const int ktiles = (int)((a.K + BK - 1) / BK);
-  main_loop<DTI, TL>(acc, la, lb, smem, ktiles);
+  if constexpr (NK > 0)
+    main_loop_allk<DTI, TL, NK>(acc, la, lb, smem, ktiles, init_acc);
+  else
+    main_loop<DTI, TL>(acc, la, lb, smem, ktiles, init_acc);
 
   // epilogue: activation, cast, one store per element
   const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.C, a.c_bytes);
@@ -104,7 +110,7 @@ __global__ __launch_bounds__(TL::threads, 1) void conv_bias_act_kernel(ConvArgs 
   const int half = lane >> 5, lrow = lane & 31;
 
   f32x16 acc[TL::SN][TL::SM];
-  {
+  auto init_acc = [&]() {
     uint32_t idx[TL::SM];
     float bv[TL::SM];
 #pragma unroll
@@ -116,14 +122,14 @@ __global__ __launch_bounds__(TL::threads, 1) void conv_bias_act_kernel(ConvArgs 
       for (int si = 0; si < TL::SN; ++si)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[si][sj][r] = bv[sj];
-  }
+  };
 
   DenseRowLoader<DTI, TL> la;
   ConvGatherLoader<DTI, TL> lb;
   la.init(a.w, a.w_bytes, G.Co, G.K, m0, a.vec_w);
   lb.init(a.x, a.x_bytes, G, p0);
   const int ktiles = (int)((G.K + BK - 1) / BK);
-  main_loop<DTI, TL>(acc, la, lb, smem, ktiles);
+  main_loop<DTI, TL>(acc, la, lb, smem, ktiles, init_acc);
 
   const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.y, a.y_bytes);
   const uint32_t howo = G.Ho * G.Wo;
@@ -218,16 +224,16 @@ __global__ __launch_bounds__(256) void act_cast_kernel(const float* ws, void* ou
 // ---------------------------------------------------------------------------
 // Host-side launch helpers (instantiated per input type in its own TU).
 // ---------------------------------------------------------------------------
-template <int DTI, int DTO, class TL>
+template <int DTI, int DTO, class TL, int NK = 0>
 inline void launch_gemm_t(const GemmArgs& a, hipStream_t s) {
   const uint32_t nblk = a.tiles_m * a.tiles_n;
-  hipLaunchKernelGGL((gemm_bias_act_kernel<DTI, DTO, TL>), dim3(nblk), dim3(TL::threads), 0, s, a);
+  launch_kernel(gemm_bias_act_kernel<DTI, DTO, TL, NK>, dim3(nblk), dim3(TL::threads), s, a);
 }
 
 template <int DTI, int DTO, class TL>
 inline void launch_conv_t(const ConvArgs& a, hipStream_t s) {
   const uint32_t nblk = a.tiles_m * a.tiles_n;
-  hipLaunchKernelGGL((conv_bias_act_kernel<DTI, DTO, TL>), dim3(nblk), dim3(TL::threads), 0, s, a);
+  launch_kernel(conv_bias_act_kernel<DTI, DTO, TL>, dim3(nblk), dim3(TL::threads), s, a);
 }
 
 // The tile table (same ids and order as kTiles in plan.hpp).
@@ -246,7 +252,14 @@ inline int launch_gemm_tile(int tile, const GemmArgs& a, hipStream_t s) {
     case 2: launch_gemm_t<DTI, DTO, T2>(a, s); return 0;
     case 3: launch_gemm_t<DTI, DTO, T3>(a, s); return 0;
     case 4: launch_gemm_t<DTI, DTO, T4>(a, s); return 0;
-    case 5: launch_gemm_t<DTI, DTO, T5>(a, s); return 0;
+    case 5:
+      // a reduction of at most 4 k-tiles has no steady state to pipeline:
+      // load all of it at once
+      if (a.K <= 4u * (kChunks * Elem<DTI>::epc))
+        launch_gemm_t<DTI, DTO, T5, 4>(a, s);
+      else
+        launch_gemm_t<DTI, DTO, T5>(a, s);
+      return 0;
     case 6:
       if constexpr (DTI != DT_F32) {
         if (a.vec_a && a.vec_b && a.vec_c) {

@@ -328,16 +328,42 @@ struct ConvGatherLoader {
 // of this wave.  Double-buffered: the global loads of k-tile kt+1 are in
 // flight while k-tile kt is multiplied out of LDS.
 // ---------------------------------------------------------------------------
-template <int DT, class TL, class LA, class LB>
-__device__ __forceinline__ void main_loop(f32x16 (&acc)[TL::SN][TL::SM], LA& la, LB& lb,
-                                          uint8_t* smem, int ktiles) {
+// One k-tile from LDS stage (sA, sB): 4 k-steps of 16-byte chunks.
+template <int DT, class TL>
+__device__ __forceinline__ void tile_mma(f32x16 (&acc)[TL::SN][TL::SM], const uint8_t* sA, const uint8_t* sB) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wave_m = wave / TL::WAVES_N, wave_n = wave % TL::WAVES_N;
   const int half = lane >> 5, lrow = lane & 31;
+#pragma unroll
+  for (int ks = 0; ks < kChunks / 2; ++ks) {
+    const int ch = 2 * ks + half;
+    u32x4 fi[TL::SN], fj[TL::SM];
+#pragma unroll
+    for (int si = 0; si < TL::SN; ++si)
+      fi[si] = *reinterpret_cast<const u32x4*>(sB + lds_off(wave_n * TL::WTN + si * 32 + lrow, ch));
+#pragma unroll
+    for (int sj = 0; sj < TL::SM; ++sj)
+      fj[sj] = *reinterpret_cast<const u32x4*>(sA + lds_off(wave_m * TL::WTM + sj * 32 + lrow, ch));
+#pragma unroll
+    for (int si = 0; si < TL::SN; ++si)
+#pragma unroll
+      for (int sj = 0; sj < TL::SM; ++sj) mfma_chunk<DT>(acc[si][sj], fi[si], fj[sj]);
+  }
+}
 
-  if (ktiles <= 0) return;
+// Double-buffered main loop: the loads of k-tile kt+1 are in flight while
+// k-tile kt is multiplied.  init_acc() runs once the first loads are issued,
+// so its own loads (the bias) do not delay them.
+template <int DT, class TL, class LA, class LB, class F>
+__device__ __forceinline__ void main_loop(f32x16 (&acc)[TL::SN][TL::SM], LA& la, LB& lb,
+                                          uint8_t* smem, int ktiles, F&& init_acc) {
+  if (ktiles <= 0) {
+    init_acc();
+    return;
+  }
   la.load(0);
   lb.load(0);
+  init_acc();
   la.store(smem);
   lb.store(smem + TL::a_bytes);
   __syncthreads();
@@ -350,29 +376,42 @@ __device__ __forceinline__ void main_loop(f32x16 (&acc)[TL::SN][TL::SM], LA& la,
       la.load(kt + 1);
       lb.load(kt + 1);
     }
-    const uint8_t* sA = cur;
-    const uint8_t* sB = cur + TL::a_bytes;
-#pragma unroll
-    for (int ks = 0; ks < kChunks / 2; ++ks) {
-      const int ch = 2 * ks + half;
-      u32x4 fi[TL::SN], fj[TL::SM];
-#pragma unroll
-      for (int si = 0; si < TL::SN; ++si)
-        fi[si] = *reinterpret_cast<const u32x4*>(sB + lds_off(wave_n * TL::WTN + si * 32 + lrow, ch));
-#pragma unroll
-      for (int sj = 0; sj < TL::SM; ++sj)
-        fj[sj] = *reinterpret_cast<const u32x4*>(sA + lds_off(wave_m * TL::WTM + sj * 32 + lrow, ch));
-#pragma unroll
-      for (int si = 0; si < TL::SN; ++si)
-#pragma unroll
-        for (int sj = 0; sj < TL::SM; ++sj) mfma_chunk<DT>(acc[si][sj], fi[si], fj[sj]);
-    }
+    tile_mma<DT, TL>(acc, cur, cur + TL::a_bytes);
     if (more) {
       la.store(nxt);
       lb.store(nxt + TL::a_bytes);
     }
     __syncthreads();
   }
+}
+
+// Short reduction (ktiles <= NK): every k-tile's loads are issued before any
+// is stored, so the operands cost one memory round trip, then NK LDS stages.
+template <int DT, class TL, int NK, class LA, class LB, class F>
+__device__ __forceinline__ void main_loop_allk(f32x16 (&acc)[TL::SN][TL::SM], const LA& la0,
+                                               const LB& lb0, uint8_t* smem, int ktiles, F&& init_acc) {
+  LA la[NK];
+  LB lb[NK];
+#pragma unroll
+  for (int k = 0; k < NK; ++k) {
+    la[k] = la0;
+    lb[k] = lb0;
+    if (k < ktiles) {
+      la[k].load(k);
+      lb[k].load(k);
+    }
+  }
+  init_acc();
+#pragma unroll
+  for (int k = 0; k < NK; ++k)
+    if (k < ktiles) {
+      la[k].store(smem + k * TL::stage_bytes);
+      lb[k].store(smem + k * TL::stage_bytes + TL::a_bytes);
+    }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < NK; ++k)
+    if (k < ktiles) tile_mma<DT, TL>(acc, smem + k * TL::stage_bytes, smem + k * TL::stage_bytes + TL::a_bytes);
 }
 
 }  // namespace biasact

@@ -123,6 +123,11 @@ int conv2d_bias_act_2k(const void* x, const void* w, const void* bias, void* y,
 
 /* Introspection and tuning. */
 const char* biasact_status_string(int status);  /* static string, never NULL */
+/* The hipError_t behind the most recent BA_ERR_HIP returned on the calling
+ * thread (hipSuccess = 0 if there was none), and its hipGetErrorString text
+ * (static, never NULL).  Other calls leave it unchanged. */
+int biasact_last_hip_error(void);
+const char* biasact_last_hip_error_string(void);
 int biasact_num_tile_configs(void);
 /* Describe tile config `id` ("BMxBN/waves_mxwaves_n") into buf (NUL-terminated,
  * truncated to n bytes); BA_ERR_INVALID for an unknown id. */

@@ -47,6 +47,26 @@ def test_status_strings():
         assert len(L.biasact_status_string(s)) > 0
 
 
+def test_last_hip_error_starts_clear():
+    # nothing has failed a launch on this thread: hipSuccess and a fixed text
+    assert L.biasact_last_hip_error() == 0
+    assert L.biasact_last_hip_error_string() == b"no HIP error"
+
+
+def test_one_hip_runtime_beside_torch():
+    # importing the package before torch must still leave one libamdhip64 in
+    # the process (the library binds to torch's instance)
+    import subprocess
+    import sys
+    code = ("import conv_bias_activation_amd, torch\n"
+            "paths = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+            "print(len(paths)); print(sorted(paths))")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.splitlines()[0] == "1", r.stdout
+
+
 def test_tile_table_introspection():
     n = ba.num_tile_configs()
     assert n >= 5

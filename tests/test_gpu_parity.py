@@ -84,6 +84,26 @@ def test_gemm_every_tile_config(ba, tile):
         ba.force_tile_config(-1)
 
 
+@pytest.mark.parametrize("ti", ["bf16", "f16", "f32"])
+def test_gemm_short_reduction_all_k_tiles(ba, ti):
+    # the 64x64 tile loads a reduction of at most four k-tiles at once; cover
+    # 1..4 k-tiles, ragged tails and the first length past the limit
+    ba.force_tile_config(5)
+    try:
+        bk = 32 if ti == "f32" else 64
+        for j, K in enumerate((0, 1, bk - 3, bk, bk + 1, 3 * bk - 5, 4 * bk, 4 * bk + 1)):
+            M, N = 70 + 37 * j, 130 - 9 * j
+            case = _gcase(M, N, K, ti, "f32", "f32", ACTS[j % 4], 0.1)
+            inp = wl.gen_gemm(case, seed=40 + j)
+            y = values_of(run_gemm(case, inp), "f32")
+            ref, floor = gemm_reference(case, inp)
+            rep = check(y, ref, floor, case)
+            _report(f"short-k {ti} K={K}", rep)
+            assert rep["ok"], rep
+    finally:
+        ba.force_tile_config(-1)
+
+
 def test_gemm_no_bias_and_k_zero(ba):
     case = wl.GemmCase("nobias", 70, 90, 130, "bf16", None, "f32", "relu")
     inp = wl.gen_gemm(case, seed=5)
