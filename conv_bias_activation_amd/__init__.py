@@ -20,6 +20,7 @@ from ._binding import (  # noqa: F401
     conv_out_hw,
     dtypes_code,
     force_halo_variant,
+    last_tile_config,
     force_tile_config,
     gemm_bias_act,
     gemm_bias_act_2k,

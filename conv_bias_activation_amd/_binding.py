@@ -51,6 +51,8 @@ def _load():
     l.conv2d_bias_act_workspace_size.restype = ctypes.c_size_t
     l.biasact_status_string.argtypes = [ctypes.c_int]
     l.biasact_status_string.restype = ctypes.c_char_p
+    l.biasact_last_tile_config.argtypes = [ctypes.c_char_p, ctypes.c_size_t]
+    l.biasact_last_tile_config.restype = ctypes.c_int
     l.biasact_last_hip_error.argtypes = []
     l.biasact_last_hip_error.restype = ctypes.c_int
     l.biasact_last_hip_error_string.argtypes = []
@@ -268,6 +270,13 @@ def conv_tile_config(N, Co, Ho, Wo, K, dtypes: int) -> int:
 
 def force_tile_config(i: int):
     _check(lib.biasact_force_tile_config(int(i)), "force_tile_config")
+
+
+def last_tile_config() -> str:
+    """The kernel and tile the calling thread's last launching call queued."""
+    buf = ctypes.create_string_buffer(128)
+    _check(lib.biasact_last_tile_config(buf, len(buf)), "last_tile_config")
+    return buf.value.decode()
 
 
 def force_halo_variant(v: int):

@@ -14,6 +14,7 @@ using namespace biasact;
 
 namespace biasact {
 thread_local hipError_t t_launch_error = hipSuccess;
+thread_local char t_launch_desc[kLaunchDescBytes] = "none";
 }
 
 namespace {
@@ -215,6 +216,12 @@ int conv2d_bias_act_2k(const void* x, const void* w, const void* bias, void* y, 
 }
 
 const char* biasact_status_string(int status) { return status_string(status); }
+
+int biasact_last_tile_config(char* buf, size_t n) {
+  if (!buf || n == 0) return kErrInvalid;
+  snprintf(buf, n, "%s", t_launch_desc);
+  return kOk;
+}
 
 int biasact_last_hip_error(void) { return (int)t_last_hip; }
 

@@ -418,6 +418,8 @@ __global__ __launch_bounds__(256, (occupancy<BM, KS, SN>())) void conv16_halo_ke
 
 template <int DTI, int DTO, int T, int BM, int KS, int SN>
 inline void launch_conv_halo_t(const HaloArgs& a, hipStream_t s) {
+  note_launch("conv-halo %d taps, %d co x %ux%u positions, %d chunk set%s", T, BM, a.PH, a.PW, KS,
+              KS > 1 ? "s" : "");
   launch_kernel(conv16_halo_kernel<DTI, DTO, T, BM, KS, SN>, dim3(a.blocks), dim3(halo::THREADS), s, a);
 }
 

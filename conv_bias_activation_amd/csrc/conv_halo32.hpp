@@ -269,6 +269,7 @@ __global__ __launch_bounds__(256, 2) void conv32_halo_kernel(HaloArgs a) {
 
 template <int DTO, int BM>
 inline void launch_conv32_halo_t(const HaloArgs& a, hipStream_t s) {
+  note_launch("conv-halo fp32, %d co x %ux%u positions", BM, a.PH, a.PW);
   launch_kernel(conv32_halo_kernel<DTO, BM>, dim3(a.blocks), dim3(halo32::THREADS), s, a);
 }
 

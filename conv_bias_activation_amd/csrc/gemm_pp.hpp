@@ -252,6 +252,7 @@ __global__ __launch_bounds__(512, 1) void gemm16_pp_kernel(GemmArgs a) {
 
 template <int DTI, int DTO>
 inline void launch_gemm_pp(const GemmArgs& a, hipStream_t s) {
+  note_launch("gemm 256x256/2x4 ping-pong");
   launch_kernel(gemm16_pp_kernel<DTI, DTO>, dim3(a.tiles_m * a.tiles_n), dim3(pp::THREADS), s, a);
 }
 

@@ -227,12 +227,15 @@ __global__ __launch_bounds__(256) void act_cast_kernel(const float* ws, void* ou
 template <int DTI, int DTO, class TL, int NK = 0>
 inline void launch_gemm_t(const GemmArgs& a, hipStream_t s) {
   const uint32_t nblk = a.tiles_m * a.tiles_n;
+  note_launch("gemm %dx%d/%dx%d%s", TL::BM, TL::BN, TL::WAVES_M, TL::WAVES_N,
+              NK > 0 ? " all-k" : "");
   launch_kernel(gemm_bias_act_kernel<DTI, DTO, TL, NK>, dim3(nblk), dim3(TL::threads), s, a);
 }
 
 template <int DTI, int DTO, class TL>
 inline void launch_conv_t(const ConvArgs& a, hipStream_t s) {
   const uint32_t nblk = a.tiles_m * a.tiles_n;
+  note_launch("conv %dx%d/%dx%d", TL::BM, TL::BN, TL::WAVES_M, TL::WAVES_N);
   launch_kernel(conv_bias_act_kernel<DTI, DTO, TL>, dim3(nblk), dim3(TL::threads), s, a);
 }
 

@@ -5,6 +5,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
 
 #include <tuple>
 #include <utility>
@@ -14,6 +16,18 @@ namespace biasact {
 // First launch refusal since the calling thread last cleared it (api.hip
 // clears it before each entry point's launches).
 extern thread_local hipError_t t_launch_error;
+
+// Description of the main kernel the calling thread queued last (reported by
+// biasact_last_tile_config).
+constexpr int kLaunchDescBytes = 96;
+extern thread_local char t_launch_desc[kLaunchDescBytes];
+
+inline void note_launch(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(t_launch_desc, sizeof(t_launch_desc), fmt, ap);
+  va_end(ap);
+}
 
 template <class... P, size_t... I>
 inline hipError_t launch_argv(void (*k)(P...), dim3 grid, dim3 block, hipStream_t s,

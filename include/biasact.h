@@ -132,6 +132,14 @@ int biasact_num_tile_configs(void);
 /* Describe tile config `id` ("BMxBN/waves_mxwaves_n") into buf (NUL-terminated,
  * truncated to n bytes); BA_ERR_INVALID for an unknown id. */
 int biasact_tile_config_name(int id, char* buf, size_t n);
+/* Describes into buf (NUL-terminated, truncated to n bytes) the main kernel
+ * that the calling thread queued last (the most recent entry-point call that
+ * launched anything):
+ * its kind and tile, e.g. "gemm 64x64/2x2 all-k", "gemm 256x256/2x4
+ * ping-pong", "conv-halo 9 taps, 64 co x 8x56 positions, 2 chunk sets";
+ * "none" before the first launch.  For a *_2k call it names the first of the
+ * two kernels.  BA_ERR_INVALID for a null buf or n == 0. */
+int biasact_last_tile_config(char* buf, size_t n);
 /* Tile config the library picks for a GEMM / conv problem (no launch). */
 int biasact_gemm_tile_config(int64_t M, int64_t N, int64_t K, uint32_t dtypes);
 int biasact_conv_tile_config(int64_t N, int64_t Co, int64_t Ho, int64_t Wo, int64_t K_total,

@@ -47,6 +47,15 @@ def test_status_strings():
         assert len(L.biasact_status_string(s)) > 0
 
 
+def test_last_tile_config_before_any_launch():
+    buf = ctypes.create_string_buffer(64)
+    assert L.biasact_last_tile_config(buf, 64) == 0 and buf.value == b"none"
+    assert L.biasact_last_tile_config(None, 64) == 1
+    assert L.biasact_last_tile_config(buf, 0) == 1
+    small = ctypes.create_string_buffer(3)
+    assert L.biasact_last_tile_config(small, 3) == 0 and small.value == b"no"
+
+
 def test_last_hip_error_starts_clear():
     # nothing has failed a launch on this thread: hipSuccess and a fixed text
     assert L.biasact_last_hip_error() == 0
