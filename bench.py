@@ -13,7 +13,10 @@ Besides the headline, the line carries:
                 against the dense bf16 MFMA peak;
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
                 workload (a subset of output rows), on this host's cores;
-  others        the other workloads (fused and two-kernel), same protocol.
+  others        every workload, fused and two-kernel: eager back-to-back steps
+                (mean), HIP-graph replays of R steps (median and minimum of 20
+                trials, no host call cost), and for the HBM-bound workloads
+                single steps after a 512 MiB cache flush.
 """
 from __future__ import annotations
 
@@ -35,8 +38,17 @@ PEAK_HBM_GBS = 8000.0
 # carries their hash and is reported only while they are unchanged.
 KERNEL_SOURCES = ["gemm_pp.hpp", "epilogue.hpp", "device_common.hpp", "gemm_args.hpp", "tile_map.hpp"]
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gemm_relu_4096_bf16_hbm_traffic.json")
-# kernels of the specialised tile configs (the other ids run the generic kernels)
-KERNEL_NAMES = {6: "gemm16_pp_kernel", 7: "conv16_halo_kernel"}
+
+
+def kernel_name(desc: str) -> str:
+    """Kernel function behind a last_tile_config() description."""
+    if "ping-pong" in desc:
+        return "gemm16_pp_kernel"
+    if desc.startswith("conv-halo fp32"):
+        return "conv32_halo_kernel"
+    if desc.startswith("conv-halo"):
+        return "conv16_halo_kernel"
+    return "gemm_bias_act_kernel" if desc.startswith("gemm") else "conv_bias_act_kernel"
 
 
 def kernel_fingerprint() -> str:
@@ -145,16 +157,88 @@ def time_steps(step, steps, warmup):
     return e0.elapsed_time(e1) / steps, wall
 
 
+def _rates(case, ms):
+    tf = case.flops / (ms * 1e-3) / 1e12
+    gbs = case.alg_bytes / (ms * 1e-3) / 1e9
+    return {"tflops": round(tf, 2), "frac_mfma": round(tf / PEAK_TFLOPS[case.in_dtype], 4),
+            "alg_GBs": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+
+
+def graph_trials(step, eager_ms, trials=20, min_trial_ms=1.0):
+    """Device throughput without the host's per-call cost: R steps captured in
+    one HIP graph (R chosen so one replay lasts >= min_trial_ms), `trials`
+    replays each timed with HIP events; per-step median and minimum."""
+    import torch
+    R = int(max(1, min(500, -(-min_trial_ms // max(eager_ms, 1e-4)))))
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for _ in range(R):
+                step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g.replay()
+    g.replay()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    times = []
+    for _ in range(trials):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        g.replay()
+        e1.record(s)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / R)
+    del g
+    return R, float(np.median(times)), float(np.min(times))
+
+
+def cold_trials(step, trials=20, flush_bytes=512 << 20):
+    """Single steps after writing a buffer larger than the 256 MB last-level
+    cache (which also evicts the L2s): inputs come from HBM.  The flush kernel
+    is still running while the host queues the step, so the events bracket the
+    step's kernels only."""
+    import torch
+    scratch = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.current_stream()
+    times = []
+    for t in range(trials + 2):
+        scratch.fill_(t & 0xFF)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        step()
+        e1.record(s)
+        torch.cuda.synchronize()
+        if t >= 2:
+            times.append(e0.elapsed_time(e1))
+    del scratch
+    return float(np.median(times)), float(np.min(times))
+
+
+# workloads whose roofline is HBM (or launch latency): also timed from a cold cache
+COLD_WORKLOADS = ("gemm_leaky_1024x640x256_f16", "conv3x3_tanh_8x64x56_f16")
+
+
 def measure_case(case, path, min_ms=200.0):
+    """Eager back-to-back steps (mean, host call cost included), then graph
+    replays (median / min per step, device time), and for the HBM-bound
+    workloads single cold-cache steps."""
     step, nk = make_step(case, 0, path)
     ms1, _ = time_steps(step, 5, 3)
     reps = int(max(10, min(2000, min_ms / max(ms1, 1e-3))))
     ms, _ = time_steps(step, reps, 5)
-    tf = case.flops / (ms * 1e-3) / 1e12
-    gbs = case.alg_bytes / (ms * 1e-3) / 1e9
-    return {"ms": round(ms, 5), "tflops": round(tf, 2),
-            "frac_mfma": round(tf / PEAK_TFLOPS[case.in_dtype], 4),
-            "alg_GBs": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "kernels": nk}
+    import conv_bias_activation_amd as ba
+    out = {"ms": round(ms, 5), **_rates(case, ms), "kernels": nk, "tile": ba.last_tile_config()}
+    R, med, mn = graph_trials(step, ms)
+    out["graph"] = {"steps_per_replay": R, "trials": 20, "median_ms": round(med, 5),
+                    "min_ms": round(mn, 5), **_rates(case, med)}
+    if case.name in COLD_WORKLOADS:
+        cmed, cmn = cold_trials(step)
+        out["cold"] = {"trials": 20, "median_ms": round(cmed, 5), "min_ms": round(cmn, 5),
+                       **_rates(case, cmed)}
+    return out
 
 
 def cpu_baseline(case, target_s):
@@ -219,17 +303,11 @@ def main():
     tflops = case.flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[case.in_dtype]
     if isinstance(case, wl.GemmCase):
-        tile = ba.gemm_tile_config(case.M, case.N, case.K, ba.dtypes_code(case.in_dtype, case.in_dtype,
-                                                                           case.bias_dtype, case.out_dtype))
         cfg = {"workload": case.name, "M": case.M, "N": case.N, "K": case.K,
                "in": case.in_dtype, "bias": case.bias_dtype, "out": case.out_dtype, "act": case.act}
     else:
-        Ho, Wo = case.out_hw()
-        tile = ba.conv_tile_config(case.N, case.Co, Ho, Wo, case.C * case.kh * case.kw,
-                                   ba.dtypes_code(case.in_dtype, case.in_dtype, case.bias_dtype,
-                                                  case.out_dtype))
         cfg = {"workload": case.name, "in": case.in_dtype, "out": case.out_dtype, "act": case.act}
-    cfg["tile"] = ba.tile_config_name(tile)
+    cfg["tile"] = ba.last_tile_config()
     if args.path != "fused":
         cfg["path"] = args.path
     if args.halo_variant >= 0:
@@ -251,8 +329,7 @@ def main():
         "frac_of_peak": round(tflops / peak, 4),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 4), "traffic": measured_traffic(case.name),
-                     "kernel": KERNEL_NAMES.get(tile, "gemm_bias_act_kernel" if isinstance(case, wl.GemmCase)
-                                                else "conv_bias_act_kernel"),
+                     "kernel": kernel_name(cfg["tile"]),
                      "per_launch_flops": case.flops,
                      "mean_launch_ms": round(ms, 5)},
         "wall_s_timed": round(wall, 3),
