@@ -22,7 +22,7 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
-ACT_CODES = {"none": 0, "relu": 1, "leaky_relu": 2, "tanh": 3}
+ACT_CODES = {"none": 0, "relu": 1, "leaky_relu": 2, "tanh": 3, "gelu": 4, "sigmoid": 5}
 
 GCC_FLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared",
              "-std=c11", "-Wall"]

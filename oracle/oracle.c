@@ -99,7 +99,15 @@ int orc_decode(int dtype, const void *src, int64_t n, double *dst)
  * by alpha ([MLR] 概述 and the leaky_relu row of 核心接口).  ReLU keeps
  * positive values and maps the rest to +0 ([FMR] host loop).  tanh is the
  * hyperbolic tangent ([FCT] K2 chain: (e^z - e^-z) / (e^z + e^-z)); libm's
- * tanh is used because the quotient form overflows for |z| > ~709. */
+ * tanh is used because the quotient form overflows for |z| > ~709.
+ * GELU and Sigmoid are the other element-wise activations of the matmul +
+ * activation family ([FMR] ops-nn的融合算子分类与适用场景, first class; Sigmoid
+ * is also the activation of [FCT]'s twin ConvSigmoid operator).  The pages
+ * name them without a formula; the plain definitions are taken:
+ * GELU(z) = z * Phi(z) with Phi the standard normal CDF, Phi(z) =
+ * (1 + erf(z / sqrt 2)) / 2 (the exact form, not the tanh approximation),
+ * and Sigmoid(z) = 1 / (1 + e^-z), written for z < 0 as e^z / (1 + e^z) so
+ * that e^-z never overflows. */
 double orc_act(int act, double z, double alpha)
 {
     switch (act) {
@@ -111,6 +119,11 @@ double orc_act(int act, double z, double alpha)
         return z >= 0.0 ? z : alpha * z;
     case ORC_ACT_TANH:
         return tanh(z);
+    case ORC_ACT_GELU:
+        return z * 0.5 * (1.0 + erf(z / sqrt(2.0)));
+    case ORC_ACT_SIGMOID:
+        if (z >= 0.0) return 1.0 / (1.0 + exp(-z));
+        return exp(z) / (1.0 + exp(z));
     default:
         return NAN;
     }
@@ -123,7 +136,7 @@ void orc_act_array(int act, double alpha, const double *z, double *y, int64_t n)
 
 static int act_ok(int act)
 {
-    return act >= ORC_ACT_NONE && act <= ORC_ACT_TANH;
+    return act >= ORC_ACT_NONE && act <= ORC_ACT_SIGMOID;
 }
 
 /* ---- GEMM -------------------------------------------------------------- */

@@ -30,7 +30,8 @@ extern "C" {
 enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2 };
 
 /* Activation codes. */
-enum { ORC_ACT_NONE = 0, ORC_ACT_RELU = 1, ORC_ACT_LEAKY = 2, ORC_ACT_TANH = 3 };
+enum { ORC_ACT_NONE = 0, ORC_ACT_RELU = 1, ORC_ACT_LEAKY = 2, ORC_ACT_TANH = 3,
+       ORC_ACT_GELU = 4, ORC_ACT_SIGMOID = 5 };
 
 /* Exact decoders, written from the IEEE-754 binary16 / binary32 layouts and
  * from bfloat16 = the upper half of a binary32.  n elements, src packed. */

@@ -132,6 +132,64 @@ def test_tanh_matches_page_formula_and_symmetry():
     assert np.all(np.abs(O.act(np.linspace(-50, 50, 999), "tanh")) <= 1.0)
 
 
+def test_sigmoid_closed_forms_golden():
+    g = _golden("sigmoid_closed_forms.json")
+    z = np.array([math.log(p["ln_of"]) for p in g["points"]])
+    y = O.act(z, "sigmoid")
+    for got, p in zip(y, g["points"]):
+        assert abs(got - p["expect"]) <= 4e-16, (p, got)
+
+
+def test_sigmoid_symmetry_tanh_relation_and_range():
+    z = np.concatenate([np.linspace(-40, 40, 8001), [1e-12, -1e-12, 0.0]])
+    y = O.act(z, "sigmoid")
+    # Sigmoid(z) + Sigmoid(-z) = 1
+    assert np.all(np.abs(y + O.act(-z, "sigmoid") - 1.0) <= 4.5e-16)     # two ulps of 1
+    # Sigmoid(z) = (1 + tanh(z/2)) / 2, against the (separately pinned) tanh
+    assert np.all(np.abs(y - 0.5 * (1.0 + O.act(z / 2.0, "tanh"))) <= 4e-16)
+    # finite and in [0, 1] far out, where e^-z alone would overflow
+    far = O.act(np.array([800.0, -800.0, 1e6, -1e6]), "sigmoid")
+    assert np.array_equal(far, [1.0, 0.0, 1.0, 0.0])
+    assert np.all((y >= 0.0) & (y <= 1.0))
+
+
+def _phi_by_quadrature(z):
+    """Standard normal CDF by composite Simpson integration of the density
+    from 0 to z (2^14 panels; error far below 1e-14 for |z| <= 6): an
+    evaluation that shares nothing with an erf routine."""
+    n = 1 << 14
+    t = np.linspace(0.0, z, n + 1)
+    f = np.exp(-0.5 * t * t) / math.sqrt(2.0 * math.pi)
+    h = z / n
+    return 0.5 + h / 3.0 * (f[0] + f[-1] + 4.0 * f[1:-1:2].sum() + 2.0 * f[2:-1:2].sum())
+
+
+def test_gelu_against_quadrature_of_the_normal_density():
+    # GELU(z) = z * Phi(z), the exact (erf) form
+    zs = np.array([-6.0, -3.0, -2.0, -1.0, -0.5, -0.1, 0.1, 0.5, 1.0, 1.5, 2.0, 3.0, 6.0])
+    y = O.act(zs, "gelu")
+    for z, got in zip(zs, y):
+        want = z * _phi_by_quadrature(z)
+        assert abs(got - want) <= 1e-14 * max(1.0, abs(want)), (z, got, want)
+
+
+def test_gelu_identities_and_limits():
+    z = np.linspace(-8, 8, 1601)
+    y = O.act(z, "gelu")
+    # Phi(z) + Phi(-z) = 1  =>  GELU(z) - GELU(-z) = z
+    assert np.all(np.abs(y - O.act(-z, "gelu") - z) <= 1e-15 * (1 + np.abs(z)))
+    # GELU(z) = z/2 + z^2 / sqrt(2 pi) + O(z^4) near 0
+    h = np.array([1e-3, -1e-3, 1e-4])
+    c2 = (O.act(h, "gelu") - h / 2) / h ** 2
+    assert np.all(np.abs(c2 - 1.0 / math.sqrt(2.0 * math.pi)) <= 2e-6)
+    assert O.act(np.array([0.0]), "gelu")[0] == 0.0
+    # far tails: the identity for large positive z, zero for large negative z
+    far = O.act(np.array([40.0, -40.0]), "gelu")
+    assert far[0] == 40.0 and abs(far[1]) < 1e-300
+    # the minimum of z * Phi(z) lies between -1 and 0 and is about -0.17
+    assert -0.18 < y.min() < -0.16
+
+
 # --------------------------------------------------------------------------
 # GEMM
 # --------------------------------------------------------------------------

@@ -28,7 +28,7 @@ import numpy as np
 
 DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
 DTYPE_SIZES = {"f32": 4, "f16": 2, "bf16": 2}
-ACT_CODES = {"none": 0, "relu": 1, "leaky_relu": 2, "tanh": 3}
+ACT_CODES = {"none": 0, "relu": 1, "leaky_relu": 2, "tanh": 3, "gelu": 4, "sigmoid": 5}
 
 
 # ---------------------------------------------------------------------------
