@@ -105,7 +105,9 @@ int orc_decode(int dtype, const void *src, int64_t n, double *dst)
  * is also the activation of [FCT]'s twin ConvSigmoid operator).  The pages
  * name them without a formula; the plain definitions are taken:
  * GELU(z) = z * Phi(z) with Phi the standard normal CDF, Phi(z) =
- * (1 + erf(z / sqrt 2)) / 2 (the exact form, not the tanh approximation),
+ * (1 + erf(z / sqrt 2)) / 2 = erfc(-z / sqrt 2) / 2 (the exact form, not the
+ * tanh approximation; the erfc form keeps Phi's relative accuracy in the
+ * negative tail, where 1 + erf cancels),
  * and Sigmoid(z) = 1 / (1 + e^-z), written for z < 0 as e^z / (1 + e^z) so
  * that e^-z never overflows. */
 double orc_act(int act, double z, double alpha)
@@ -120,7 +122,7 @@ double orc_act(int act, double z, double alpha)
     case ORC_ACT_TANH:
         return tanh(z);
     case ORC_ACT_GELU:
-        return z * 0.5 * (1.0 + erf(z / sqrt(2.0)));
+        return z * 0.5 * erfc(-z / sqrt(2.0));
     case ORC_ACT_SIGMOID:
         if (z >= 0.0) return 1.0 / (1.0 + exp(-z));
         return exp(z) / (1.0 + exp(z));

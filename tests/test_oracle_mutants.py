@@ -25,12 +25,14 @@ MUTANTS = [
     ("leaky branches swapped", "return z >= 0.0 ? z : alpha * z;", "return z >= 0.0 ? alpha * z : z;"),
     ("relu keeps negatives", "return z > 0.0 ? z : 0.0;", "return z > 0.0 ? z : -z;"),
     ("tanh dropped", "return tanh(z);", "return z;"),
-    ("gelu erf argument unscaled", "return z * 0.5 * (1.0 + erf(z / sqrt(2.0)));",
-     "return z * 0.5 * (1.0 + erf(z));"),
-    ("gelu tanh approximation", "return z * 0.5 * (1.0 + erf(z / sqrt(2.0)));",
+    ("gelu erfc argument unscaled", "return z * 0.5 * erfc(-z / sqrt(2.0));",
+     "return z * 0.5 * erfc(-z);"),
+    ("gelu tanh approximation", "return z * 0.5 * erfc(-z / sqrt(2.0));",
      "return z * 0.5 * (1.0 + tanh(sqrt(2.0 / 3.141592653589793) * (z + 0.044715 * z * z * z)));"),
-    ("gelu cdf of -z", "return z * 0.5 * (1.0 + erf(z / sqrt(2.0)));",
-     "return z * 0.5 * (1.0 - erf(z / sqrt(2.0)));"),
+    ("gelu cdf of -z", "return z * 0.5 * erfc(-z / sqrt(2.0));",
+     "return z * 0.5 * erfc(z / sqrt(2.0));"),
+    ("gelu via 1 + erf (cancels in the tail)", "return z * 0.5 * erfc(-z / sqrt(2.0));",
+     "return z * 0.5 * (1.0 + erf(z / sqrt(2.0)));"),
     ("sigmoid sign", "if (z >= 0.0) return 1.0 / (1.0 + exp(-z));", "if (z >= 0.0) return 1.0 / (1.0 + exp(z));"),
     ("sigmoid negative branch", "return exp(z) / (1.0 + exp(z));", "return 1.0 / (1.0 + exp(z));"),
     ("gemm bias dropped", "double z = acc[j] + (bias ? bias[j] : 0.0);", "double z = acc[j];"),

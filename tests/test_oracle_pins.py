@@ -188,6 +188,13 @@ def test_gelu_identities_and_limits():
     assert far[0] == 40.0 and abs(far[1]) < 1e-300
     # the minimum of z * Phi(z) lies between -1 and 0 and is about -0.17
     assert -0.18 < y.min() < -0.16
+    # relative accuracy in the negative tail, against the quadrature:
+    # Phi(z) = 1/2 - int_z^0 density, and Mills' ratio bounds
+    # phi(z)/|z| * (1 - 1/z^2) < Phi(z) < phi(z)/|z| for z < 0
+    for z in (-8.0, -12.0, -20.0):
+        got = O.act(np.array([z]), "gelu")[0] / z
+        dens = math.exp(-0.5 * z * z) / math.sqrt(2.0 * math.pi)
+        assert dens / abs(z) * (1 - 1 / z ** 2) < got < dens / abs(z), (z, got)
 
 
 # --------------------------------------------------------------------------
