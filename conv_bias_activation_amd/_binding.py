@@ -10,7 +10,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libbiasact.so")
 
 DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
-ACT_CODES = {"none": 0, "relu": 1, "leaky_relu": 2, "tanh": 3}
+ACT_CODES = {"none": 0, "relu": 1, "leaky_relu": 2, "tanh": 3, "gelu": 4, "sigmoid": 5}
 BA_OK, BA_ERR_INVALID, BA_ERR_UNSUPPORTED, BA_ERR_HIP = 0, 1, 2, 3
 
 

@@ -374,7 +374,7 @@ __global__ __launch_bounds__(256, (occupancy<BM, KS, SN>())) void conv16_halo_ke
   const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.y, a.y_bytes);
   const uint32_t howo = G.Ho * G.Wo;
   const uint32_t npos = a.PH * a.PW;
-  auto epilogue = [&](auto act_c) {
+  auto epilogue = [&](auto act_c) __attribute__((always_inline)) {
     constexpr int ACT = decltype(act_c)::value;
 #pragma unroll
     for (int si = 0; si < SN; ++si)
@@ -412,6 +412,8 @@ __global__ __launch_bounds__(256, (occupancy<BM, KS, SN>())) void conv16_halo_ke
     case ACT_RELU: epilogue(std::integral_constant<int, ACT_RELU>{}); break;
     case ACT_LEAKY: epilogue(std::integral_constant<int, ACT_LEAKY>{}); break;
     case ACT_TANH: epilogue(std::integral_constant<int, ACT_TANH>{}); break;
+    case ACT_GELU: epilogue(std::integral_constant<int, ACT_GELU>{}); break;
+    case ACT_SIGMOID: epilogue(std::integral_constant<int, ACT_SIGMOID>{}); break;
     default: epilogue(std::integral_constant<int, ACT_NONE>{}); break;
   }
 }

@@ -12,10 +12,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace biasact {
 
 enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
-enum : int { ACT_NONE = 0, ACT_RELU = 1, ACT_LEAKY = 2, ACT_TANH = 3 };
+enum : int { ACT_NONE = 0, ACT_RELU = 1, ACT_LEAKY = 2, ACT_TANH = 3, ACT_GELU = 4, ACT_SIGMOID = 5 };
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -81,6 +83,11 @@ template <> __device__ __forceinline__ float widen<DT_BF16>(uint32_t w) {
 template <int DT> __device__ __forceinline__ uint32_t narrow(float v);
 template <> __device__ __forceinline__ uint32_t narrow<DT_F32>(float v) { return __float_as_uint(v); }
 template <> __device__ __forceinline__ uint32_t narrow<DT_F16>(float v) {
+  // The opaque copy keeps the compiler from folding a multiply that produced
+  // v into a mixed-precision multiply-add rounding straight to fp16: that
+  // rounds once instead of twice and turns -0 into +0, so whether it fires
+  // would depend on the surrounding kernel.  Every path rounds to fp32 first.
+  asm("" : "+v"(v));
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v);
 }
 template <> __device__ __forceinline__ uint32_t narrow<DT_BF16>(float v) {
@@ -97,10 +104,15 @@ template <> __device__ __forceinline__ uint32_t narrow<DT_BF16>(float v) {
 // exponential gives exactly 1, so large arguments stay finite); below 0.625
 // the odd polynomial x * P(x^2) whose coefficients fit_tanh.py derives.
 // Relative error below 2e-7 everywhere; the sign comes from x, NaN propagates.
+// The activation helpers below turn off implicit multiply-add contraction and
+// state every fused multiply-add they use, so each compiles to the same
+// instruction sequence in every kernel: the fused epilogue and the two-kernel
+// path's act_cast_kernel give bitwise equal results.
 __device__ __forceinline__ float tanh_f32(float x) {
+#pragma clang fp contract(off)
   const float ax = __builtin_fabsf(x);
   const float e = __builtin_amdgcn_exp2f(ax * 2.885390082f);     // e^{2|x|} = 2^{2|x| / ln 2}
-  const float big = 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
+  const float big = __builtin_fmaf(-2.0f, __builtin_amdgcn_rcpf(e + 1.0f), 1.0f);
   const float t = x * x;
   float p = -5.664775148e-03f;
   p = __builtin_fmaf(p, t, 2.059567906e-02f);
@@ -112,20 +124,71 @@ __device__ __forceinline__ float tanh_f32(float x) {
   return __builtin_copysignf(r, x);
 }
 
+// Sigmoid(z) = 1 / (1 + e^-z), with e^-z = 2^(-z log2 e) from the hardware
+// base-2 exponential and the hardware reciprocal: for z -> -inf the
+// exponential overflows to +inf and the reciprocal gives 0; for z -> +inf it
+// gives 1.  Each step is within about an ulp, so the result is within a few
+// fp32 ulps of the definition.
+__device__ __forceinline__ float sigmoid_f32(float z) {
+#pragma clang fp contract(off)
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.442695041f));
+}
+
+// erfc(x) for x >= 0 as t * e^(-x^2 + P(t)), t = 1 / (1 + x/2), P of degree 9:
+// the functional form of the Chebyshev-fitted erfc in Numerical Recipes
+// (section 6.2), with this project's own least-squares coefficients
+// (csrc/fit_erfc.py, which also reports the float32 error: relative
+// 4e-7 on [0, 1], 2e-6 on [1, 4], 8e-6 on [4, 9], the last dominated by the
+// rounding of the exponent's argument).  erfc(-x) = 2 - erfc(x).
+__device__ __forceinline__ float erfc_f32(float x) {
+#pragma clang fp contract(off)
+  const float ax = __builtin_fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.5f, ax, 1.0f));
+  float p = 1.449302137e-01f;
+  p = __builtin_fmaf(p, t, -6.808272004e-01f);
+  p = __builtin_fmaf(p, t, 1.156733751e+00f);
+  p = __builtin_fmaf(p, t, -6.962518692e-01f);
+  p = __builtin_fmaf(p, t, -8.028043061e-02f);
+  p = __builtin_fmaf(p, t, 1.267586369e-03f);
+  p = __builtin_fmaf(p, t, 3.460279852e-02f);
+  p = __builtin_fmaf(p, t, 3.866403997e-01f);
+  p = __builtin_fmaf(p, t, 9.986327887e-01f);
+  p = __builtin_fmaf(p, t, -1.265447974e+00f);
+  const float e = __builtin_fmaf(-ax, ax, p);
+  const float r = t * __builtin_amdgcn_exp2f(e * 1.442695041f);
+  return x < 0.0f ? 2.0f - r : r;
+}
+
+// GELU(z) = z * Phi(z), Phi(z) = erfc(-z / sqrt 2) / 2: the complementary
+// error function keeps Phi's relative accuracy in the negative tail, where
+// the 1 + erf form cancels.
+__device__ __forceinline__ float gelu_f32(float z) {
+#pragma clang fp contract(off)
+  return 0.5f * z * erfc_f32(z * -0.7071067812f);
+}
+
 template <int ACT>
 __device__ __forceinline__ float act_fn(float z, float alpha) {
   if constexpr (ACT == ACT_RELU) return z > 0.0f ? z : 0.0f;
   else if constexpr (ACT == ACT_LEAKY) return z >= 0.0f ? z : alpha * z;
   else if constexpr (ACT == ACT_TANH) return tanh_f32(z);
+  else if constexpr (ACT == ACT_GELU) return gelu_f32(z);
+  else if constexpr (ACT == ACT_SIGMOID) return sigmoid_f32(z);
   else return z;
 }
 
-__device__ __forceinline__ float apply_act(int act, float z, float alpha) {
+// Runs f(std::integral_constant<int, ACT>{}) for the runtime activation code:
+// an epilogue is instantiated once per activation and branches once, not per
+// element.
+template <class F>
+__device__ __forceinline__ void with_act(int act, F&& f) {
   switch (act) {
-    case ACT_RELU:  return act_fn<ACT_RELU>(z, alpha);
-    case ACT_LEAKY: return act_fn<ACT_LEAKY>(z, alpha);
-    case ACT_TANH:  return act_fn<ACT_TANH>(z, alpha);
-    default:        return z;
+    case ACT_RELU: f(std::integral_constant<int, ACT_RELU>{}); break;
+    case ACT_LEAKY: f(std::integral_constant<int, ACT_LEAKY>{}); break;
+    case ACT_TANH: f(std::integral_constant<int, ACT_TANH>{}); break;
+    case ACT_GELU: f(std::integral_constant<int, ACT_GELU>{}); break;
+    case ACT_SIGMOID: f(std::integral_constant<int, ACT_SIGMOID>{}); break;
+    default: f(std::integral_constant<int, ACT_NONE>{}); break;
   }
 }
 

@@ -233,21 +233,23 @@ __global__ __launch_bounds__(512, 1) void gemm16_pp_kernel(GemmArgs a) {
 
   // ---- epilogue: activation, cast, one store per element -----------------
   const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.C, a.c_bytes);
+  with_act(a.act, [&](auto act_c) __attribute__((always_inline)) {
+    constexpr int ACT = decltype(act_c)::value;
 #pragma unroll
-  for (int si = 0; si < 2; ++si)
+    for (int si = 0; si < 2; ++si)
 #pragma unroll
-    for (int sj = 0; sj < 4; ++sj) {
-      const uint32_t m = m0 + wm * 128 + sj * 32 + lrow;
+      for (int sj = 0; sj < 4; ++sj) {
+        const uint32_t m = m0 + wm * 128 + sj * 32 + lrow;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const uint32_t n = n0 + wn * 64 + si * 32 + 8 * g + 4 * half;
-        const float y0 = apply_act(a.act, acc[si][sj][4 * g + 0], a.alpha);
-        const float y1 = apply_act(a.act, acc[si][sj][4 * g + 1], a.alpha);
-        const float y2 = apply_act(a.act, acc[si][sj][4 * g + 2], a.alpha);
-        const float y3 = apply_act(a.act, acc[si][sj][4 * g + 3], a.alpha);
-        store4<DTO>(rc, m * a.N + n, m < a.M && n < a.N, y0, y1, y2, y3);
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t n = n0 + wn * 64 + si * 32 + 8 * g + 4 * half;
+          store4<DTO>(rc, m * a.N + n, m < a.M && n < a.N, act_fn<ACT>(acc[si][sj][4 * g + 0], a.alpha),
+                      act_fn<ACT>(acc[si][sj][4 * g + 1], a.alpha),
+                      act_fn<ACT>(acc[si][sj][4 * g + 2], a.alpha),
+                      act_fn<ACT>(acc[si][sj][4 * g + 3], a.alpha));
+        }
       }
-    }
+  });
 }
 
 template <int DTI, int DTO>

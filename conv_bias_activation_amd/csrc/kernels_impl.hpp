@@ -66,6 +66,8 @@ __global__ __launch_bounds__(TL::threads, 1) void gemm_bias_act_kernel(GemmArgs 
 
   // epilogue: activation, cast, one store per element
   const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.C, a.c_bytes);
+  with_act(a.act, [&](auto act_c) __attribute__((always_inline)) {
+  constexpr int ACT = decltype(act_c)::value;
 #pragma unroll
   for (int si = 0; si < TL::SN; ++si)
 #pragma unroll
@@ -74,10 +76,10 @@ __global__ __launch_bounds__(TL::threads, 1) void gemm_bias_act_kernel(GemmArgs 
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const uint32_t n = n0 + wave_n * TL::WTN + si * 32 + 8 * g + 4 * half;
-        const float y0 = apply_act(a.act, acc[si][sj][4 * g + 0], a.alpha);
-        const float y1 = apply_act(a.act, acc[si][sj][4 * g + 1], a.alpha);
-        const float y2 = apply_act(a.act, acc[si][sj][4 * g + 2], a.alpha);
-        const float y3 = apply_act(a.act, acc[si][sj][4 * g + 3], a.alpha);
+        const float y0 = act_fn<ACT>(acc[si][sj][4 * g + 0], a.alpha);
+        const float y1 = act_fn<ACT>(acc[si][sj][4 * g + 1], a.alpha);
+        const float y2 = act_fn<ACT>(acc[si][sj][4 * g + 2], a.alpha);
+        const float y3 = act_fn<ACT>(acc[si][sj][4 * g + 3], a.alpha);
         if (a.vec_c) {
           store4<DTO>(rc, m * a.N + n, m < a.M && n < a.N, y0, y1, y2, y3);
         } else {
@@ -89,6 +91,7 @@ __global__ __launch_bounds__(TL::threads, 1) void gemm_bias_act_kernel(GemmArgs 
         }
       }
     }
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -133,6 +136,8 @@ __global__ __launch_bounds__(TL::threads, 1) void conv_bias_act_kernel(ConvArgs 
 
   const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.y, a.y_bytes);
   const uint32_t howo = G.Ho * G.Wo;
+  with_act(a.act, [&](auto act_c) __attribute__((always_inline)) {
+  constexpr int ACT = decltype(act_c)::value;
 #pragma unroll
   for (int si = 0; si < TL::SN; ++si)
 #pragma unroll
@@ -142,10 +147,10 @@ __global__ __launch_bounds__(TL::threads, 1) void conv_bias_act_kernel(ConvArgs 
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const uint32_t p = p0 + wave_n * TL::WTN + si * 32 + 8 * g + 4 * half;
-        const float y0 = apply_act(a.act, acc[si][sj][4 * g + 0], a.alpha);
-        const float y1 = apply_act(a.act, acc[si][sj][4 * g + 1], a.alpha);
-        const float y2 = apply_act(a.act, acc[si][sj][4 * g + 2], a.alpha);
-        const float y3 = apply_act(a.act, acc[si][sj][4 * g + 3], a.alpha);
+        const float y0 = act_fn<ACT>(acc[si][sj][4 * g + 0], a.alpha);
+        const float y1 = act_fn<ACT>(acc[si][sj][4 * g + 1], a.alpha);
+        const float y2 = act_fn<ACT>(acc[si][sj][4 * g + 2], a.alpha);
+        const float y3 = act_fn<ACT>(acc[si][sj][4 * g + 3], a.alpha);
         if (a.vec_y) {
           // Ho*Wo % 4 == 0: the four positions lie in one image
           const uint32_t img = fdiv(p, G.div_howo);
@@ -163,6 +168,7 @@ __global__ __launch_bounds__(TL::threads, 1) void conv_bias_act_kernel(ConvArgs 
         }
       }
     }
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -179,7 +185,7 @@ __global__ __launch_bounds__(256) void act_cast_kernel(const float* ws, void* ou
   const __amdgpu_buffer_rsrc_t ri = make_rsrc(ws, n * 4u);
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(out, n * (uint32_t)Elem<DTO>::bytes);
   const uint32_t stride = gridDim.x * blockDim.x * EPT;
-  auto run = [&](auto act_c) {
+  auto run = [&](auto act_c) __attribute__((always_inline)) {
     constexpr int ACT = decltype(act_c)::value;
     for (uint32_t base = (blockIdx.x * blockDim.x + threadIdx.x) * EPT; base < n; base += stride) {
       const bool full = base + EPT <= n;
@@ -217,6 +223,8 @@ __global__ __launch_bounds__(256) void act_cast_kernel(const float* ws, void* ou
     case ACT_RELU: run(std::integral_constant<int, ACT_RELU>{}); break;
     case ACT_LEAKY: run(std::integral_constant<int, ACT_LEAKY>{}); break;
     case ACT_TANH: run(std::integral_constant<int, ACT_TANH>{}); break;
+    case ACT_GELU: run(std::integral_constant<int, ACT_GELU>{}); break;
+    case ACT_SIGMOID: run(std::integral_constant<int, ACT_SIGMOID>{}); break;
     default: run(std::integral_constant<int, ACT_NONE>{}); break;
   }
 }

@@ -86,7 +86,7 @@ struct DenseRowLoader {
   bool vec;
   u32x4 reg[RA];
 
-  __device__ void init(const void* p, uint32_t nbytes, uint32_t rows, uint32_t K_, uint32_t r0,
+  __device__ __forceinline__ void init(const void* p, uint32_t nbytes, uint32_t rows, uint32_t K_, uint32_t r0,
                        bool vec_) {
     rsrc = make_rsrc(p, nbytes);
     K = K_;
@@ -100,7 +100,7 @@ struct DenseRowLoader {
     }
   }
 
-  __device__ void load(int kt) {
+  __device__ __forceinline__ void load(int kt) {
 #pragma unroll
     for (int i = 0; i < RA; ++i) {
       const uint32_t k = (uint32_t)kt * BK + chunk[i] * EPC;
@@ -119,7 +119,7 @@ struct DenseRowLoader {
     }
   }
 
-  __device__ void store(uint8_t* s) const {
+  __device__ __forceinline__ void store(uint8_t* s) const {
 #pragma unroll
     for (int i = 0; i < RA; ++i) {
       const int q = threadIdx.x + i * TL::threads;
@@ -148,7 +148,7 @@ struct DenseColLoader {
   bool vec;
   u32x4 reg[RB][EPC];
 
-  __device__ void init(const void* p, uint32_t nbytes, uint32_t K_, uint32_t N_, uint32_t n0,
+  __device__ __forceinline__ void init(const void* p, uint32_t nbytes, uint32_t K_, uint32_t N_, uint32_t n0,
                        bool vec_) {
     rsrc = make_rsrc(p, nbytes);
     K = K_;
@@ -164,7 +164,7 @@ struct DenseColLoader {
     }
   }
 
-  __device__ void load(int kt) {
+  __device__ __forceinline__ void load(int kt) {
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       if (!active[i]) continue;
@@ -187,7 +187,7 @@ struct DenseColLoader {
     }
   }
 
-  __device__ void store(uint8_t* s) const {
+  __device__ __forceinline__ void store(uint8_t* s) const {
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       if (!active[i]) continue;
@@ -252,7 +252,7 @@ struct ConvGatherLoader {
   uint32_t c0;                  // first chunk index of this wave (wave-uniform)
   u32x4 reg[PPT][CPP];
 
-  __device__ void init(const void* x, uint32_t nbytes, const ConvGeom& geom, uint32_t p0) {
+  __device__ __forceinline__ void init(const void* x, uint32_t nbytes, const ConvGeom& geom, uint32_t p0) {
     rsrc = make_rsrc(x, nbytes);
     g = geom;
 #pragma unroll
@@ -277,7 +277,7 @@ struct ConvGatherLoader {
     c0 = __builtin_amdgcn_readfirstlane((uint32_t)(threadIdx.x / TL::BN));
   }
 
-  __device__ void load(int kt) {
+  __device__ __forceinline__ void load(int kt) {
     const ConvGeom& G = g;
     const uint32_t cstep = TL::threads >= TL::BN ? TL::threads / TL::BN : 1;
 #pragma unroll
@@ -313,7 +313,7 @@ struct ConvGatherLoader {
     }
   }
 
-  __device__ void store(uint8_t* s) const {
+  __device__ __forceinline__ void store(uint8_t* s) const {
     const uint32_t cstep = TL::threads >= TL::BN ? TL::threads / TL::BN : 1;
 #pragma unroll
     for (int u = 0; u < PPT; ++u)

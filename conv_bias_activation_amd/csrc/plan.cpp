@@ -221,7 +221,7 @@ int plan_gemm(const void* A, const void* B, const void* bias, const void* C, int
               int64_t K, uint32_t dtypes, int act, GemmPlan* p) {
   if (!p) return kErrInvalid;
   if (M < 0 || N < 0 || K < 0) return kErrInvalid;
-  if (act < 0 || act > 3) return kErrInvalid;
+  if (act < 0 || act > 5) return kErrInvalid;
   int dti, dto, dtb;
   int rc = decode_dtypes(dtypes, bias != nullptr, &dti, &dto, &dtb);
   if (rc) return rc;
@@ -265,7 +265,7 @@ int plan_conv(const void* x, const void* w, const void* bias, const void* y, int
               ConvPlan* p) {
   if (!p || !strides || !pads || !dilations) return kErrInvalid;
   if (N < 0 || C <= 0 || H <= 0 || W <= 0 || Co <= 0 || kh <= 0 || kw <= 0) return kErrInvalid;
-  if (act < 0 || act > 3) return kErrInvalid;
+  if (act < 0 || act > 5) return kErrInvalid;
   if (act == 2) return kErrUnsupported;                 // no alpha argument on this entry point
   const int32_t sh = strides[0], sw = strides[1], dh = dilations[0], dw = dilations[1];
   const int32_t pt = pads[0], pb = pads[1], pl = pads[2], pr = pads[3];

@@ -70,6 +70,8 @@ extern "C" {
 #define BA_ACT_RELU 1       /* z > 0 ? z : +0 */
 #define BA_ACT_LEAKY_RELU 2 /* z >= 0 ? z : alpha * z */
 #define BA_ACT_TANH 3       /* tanh(z) */
+#define BA_ACT_GELU 4       /* z * Phi(z), Phi the standard normal CDF (exact erf form) */
+#define BA_ACT_SIGMOID 5    /* 1 / (1 + e^-z) */
 
 /* status codes */
 #define BA_OK 0

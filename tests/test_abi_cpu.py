@@ -127,7 +127,7 @@ def gemm(A=P, B=P, bias=P, C=P, M=4, N=4, K=4, dt=_dt(F16, F16, F32, F32), act=2
 @pytest.mark.parametrize("kw,code", [
     (dict(A=NUL), 1), (dict(B=NUL), 1), (dict(C=NUL), 1),
     (dict(M=-1), 1), (dict(N=-2), 1), (dict(K=-3), 1),
-    (dict(act=4), 1), (dict(act=-1), 1),
+    (dict(act=6), 1), (dict(act=-1), 1),
     (dict(dt=_dt(F16, BF16, F32, F32)), 2),           # A and B differ
     (dict(dt=_dt(3, 3, F32, F32)), 2),                # unknown type
     (dict(dt=_dt(F16, F16, BF16, F32)), 2),           # bias neither f32 nor the input type
@@ -189,6 +189,6 @@ def test_python_binding_raises_value_error_on_bad_names():
     with pytest.raises(ValueError):
         ba.dtypes_code("f64", "f64", None, "f32")
     with pytest.raises(ValueError):
-        ba._binding._act("gelu")
+        ba._binding._act("swish")
     assert ba.conv_out_hw(224, 224, 7, 7, (2, 2), (3, 3, 3, 3), (1, 1)) == (112, 112)
     assert ba.conv_out_hw(2, 2, 3, 3, (1, 1), (0, 0, 0, 0), (1, 1)) is None

@@ -47,7 +47,7 @@ GEMM_SHAPES = [(1, 1, 1), (3, 5, 7), (64, 64, 64), (127, 129, 65), (200, 136, 72
                (256, 256, 64), (300, 520, 200), (33, 260, 1000), (520, 8, 24), (16, 1024, 40)]
 GEMM_TYPES = [("bf16", "bf16", "f32"), ("f16", "f32", "f32"), ("f16", "f16", "f16"),
               ("bf16", "f32", "bf16"), ("f32", "f32", "f32"), ("f32", "bf16", "f32")]
-ACTS = ["none", "relu", "leaky_relu", "tanh"]
+ACTS = ["none", "relu", "leaky_relu", "tanh", "gelu", "sigmoid"]
 
 
 @pytest.mark.parametrize("shape", GEMM_SHAPES, ids=lambda s: "x".join(map(str, s)))
@@ -56,7 +56,7 @@ def test_gemm_small_vs_oracle(ba, shape, types):
     M, N, K = shape
     ti, to, tb = types
     s0 = sum(shape) + len(ti)
-    for j, act in enumerate((ACTS[s0 % 4], ACTS[(s0 + 1) % 4])):
+    for j, act in enumerate((ACTS[s0 % 6], ACTS[(s0 + 1) % 6], ACTS[(s0 + 3) % 6])):
         case = _gcase(M, N, K, ti, to, tb, act, alpha=0.1)
         inp = wl.gen_gemm(case, seed=11 + j)
         y = values_of(run_gemm(case, inp), to)
@@ -93,7 +93,7 @@ def test_gemm_short_reduction_all_k_tiles(ba, ti):
         bk = 32 if ti == "f32" else 64
         for j, K in enumerate((0, 1, bk - 3, bk, bk + 1, 3 * bk - 5, 4 * bk, 4 * bk + 1)):
             M, N = 70 + 37 * j, 130 - 9 * j
-            case = _gcase(M, N, K, ti, "f32", "f32", ACTS[j % 4], 0.1)
+            case = _gcase(M, N, K, ti, "f32", "f32", ACTS[j % 6], 0.1)
             inp = wl.gen_gemm(case, seed=40 + j)
             y = values_of(run_gemm(case, inp), "f32")
             ref, floor = gemm_reference(case, inp)
@@ -198,6 +198,45 @@ def test_tanh_sweep_through_k1_gemm(ba):
     assert np.array_equal(neg, -pos)
 
 
+@pytest.mark.parametrize("act", ["gelu", "sigmoid"])
+def test_gelu_sigmoid_sweep_through_k1_gemm(ba, act):
+    # z through an fp32 K = 1 GEMM (A = z, B = 1, no bias): y = act(z) against
+    # the oracle's fp64 value, over the range and the far tails
+    z = np.array([0.0, 1e-8, 1e-6, 1e-3, 0.1, 0.5, 1.0, 2.0, 3.0, 5.0, 8.0, 10.0, 15.0, 20.0,
+                  40.0, 88.0, 89.0, 1e4, 3.4e38], dtype=np.float32)
+    z = np.concatenate([z, -z, np.linspace(-12, 12, 4041, dtype=np.float32)])
+    M = z.size
+    inp = {"A": wl.encode(z.reshape(M, 1), "f32"), "B": wl.encode(np.ones((1, 1), np.float32), "f32"),
+           "bias": None}
+    case = wl.GemmCase(act, M, 1, 1, "f32", None, "f32", act)
+    y = values_of(run_gemm(case, inp), "f32")
+    ref = gemm_reference(case, inp)[0]
+    assert np.all(np.isfinite(y))
+    ulp32 = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
+    zd = np.abs(z.astype(np.float64))
+    if act == "sigmoid":
+        # a few fp32 ulps (hardware exp2 and reciprocal), plus the rounding of
+        # the fp32 exponent argument z*log2(e), which e^-z turns into a
+        # relative error of |z| * 2^-24 (up to ~90 ulps at z = -88); results
+        # below the fp32 normal range may flush to zero
+        assert np.all(np.abs(y - ref) <= np.maximum((4 + 1.5 * zd) * ulp32, 1e-37))
+        assert np.all((y >= 0) & (y <= 1))
+        assert np.all(y[z >= 20] == 1.0)
+    else:
+        # a few fp32 ulps, plus roundings that erfc's tail (~e^-x^2) amplifies
+        # by x^2: of the fp32 argument x = z/sqrt(2) (2 x^2 ulps) and of the
+        # exponent -x^2 + P(t) and its base-2 scaling (about 2 x^2 ulps more);
+        # a float32 emulation of the device evaluation peaks at 0.61 of this
+        # bound (255 ulps at z = -12).  erfc, unlike 1 + erf, adds no
+        # cancellation there.
+        x2 = zd * zd / 2.0
+        small = np.abs(ref) < 1e-30
+        err_ulps = np.abs(y - ref)[~small] / ulp32[~small]
+        assert np.all(err_ulps <= 16 + 6.0 * x2[~small]), np.max(err_ulps)
+        assert np.all(np.abs(y[small]) < 1e-30)
+        assert np.all(y[z >= 10] == z[z >= 10])
+
+
 # ---------------------------------------------------------------------------
 # conv2d
 # ---------------------------------------------------------------------------
@@ -222,7 +261,7 @@ CONV_TYPES = [("f16", "f16", "f16"), ("bf16", "bf16", "bf16"), ("f32", "f32", "f
 def test_conv_small_vs_oracle(ba, shape, types):
     N, C, H, W, Co, kh, kw, st, pd, dl = shape
     ti, to, tb = types
-    for j, act in enumerate(("tanh", "none", "relu")):
+    for j, act in enumerate(("tanh", "none", "relu", "sigmoid", "gelu")):
         case = _ccase(N, C, H, W, Co, kh, kw, st, pd, dl, ti, to, tb, act)
         inp = wl.gen_conv(case, seed=31 + j)
         y = values_of(run_conv(case, inp), to)
@@ -278,7 +317,7 @@ def test_conv_halo_path_vs_oracle(ba, shape, types):
         ba.force_tile_config(tile)
         ba.force_halo_variant(variant)
         try:
-            for j, act in enumerate(("tanh", "relu")):
+            for j, act in enumerate(("tanh", "relu", "gelu" if Co % 2 else "sigmoid")):
                 case = _ccase(N, C, H, W, Co, kh, kw, st, pd, dl, ti, to, tb, act)
                 inp = wl.gen_conv(case, seed=41 + j)
                 y = values_of(run_conv(case, inp), to)
@@ -308,7 +347,7 @@ def test_conv_halo32_path_vs_oracle(ba, shape, to):
     for tile in (-1, 7):
         ba.force_tile_config(tile)
         try:
-            for j, act in enumerate(("tanh", "relu")):
+            for j, act in enumerate(("tanh", "relu", "sigmoid" if Co % 2 else "gelu")):
                 case = _ccase(N, C, H, W, Co, kh, kw, st, pd, dl, "f32", to, "f32", act)
                 inp = wl.gen_conv(case, seed=71 + j)
                 y = values_of(run_conv(case, inp), to)
@@ -360,7 +399,7 @@ def test_gemm_two_kernel_bitwise_equal_fused(ba, types):
 @pytest.mark.parametrize("types", CONV_TYPES, ids=lambda t: "-".join(t))
 def test_conv_two_kernel_bitwise_equal_fused(ba, types):
     ti, to, tb = types
-    for act in ("tanh", "relu", "none"):
+    for act in ("tanh", "relu", "none", "gelu", "sigmoid"):
         case = _ccase(2, 24, 13, 11, 40, 3, 3, (2, 1), (1, 1, 0, 2), (1, 2), ti, to, tb, act)
         inp = wl.gen_conv(case, seed=12)
         a = words_of(run_conv(case, inp, "fused"), to)
