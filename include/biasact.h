@@ -5,8 +5,8 @@
  * Computes, in one kernel and one store per output element,
  *     C = act(A . B + bias)                       (GEMM)
  *     y = act(conv2d(x, w) + bias)                (conv2d as an implicit GEMM)
- * with act in {identity, ReLU, LeakyReLU(alpha), tanh}.  Sources (web pages,
- * cited by title and section):
+ * with act in {identity, ReLU, LeakyReLU(alpha), tanh, GELU, Sigmoid}.  Sources
+ * (web pages, cited by title and section):
  *   - "CANN pyasc MatmulLeakyRelu 融合算子实战" (lshu.cn/news/76032): section
  *     概述 (C = A x B + Bias, then LeakyReLU: non-negative values unchanged,
  *     negative values times alpha), section 样例规格 (operand shapes and types:
@@ -16,6 +16,8 @@
  *     "fused_matmul_relu底层到底做了什么" (fused matmul + ReLU on caller-owned
  *     device buffers, one HBM read of the operands and one write of C; the
  *     two-step matmul-then-activation fallback through a device temporary).
+ *     Section ops-nn的融合算子分类与适用场景: the matmul + activation class
+ *     covers ReLU, GELU, Sigmoid and tanh, all element-wise.
  *   - multimodal-ops "Fused ConvTanh" article (wmrh.cn/news/81139): sections
  *     这个算子到底在算什么 (y = tanh(conv2d(x, filter, bias)) with strides,
  *     pads and dilations), 双 Kernel 是怎么分工的 (implicit GEMM with the

@@ -199,6 +199,15 @@ CASES: Dict[str, object] = {
     "conv3x3d2_tanh_32x128x28_bf16": ConvCase(
         "conv3x3d2_tanh_32x128x28_bf16", 32, 128, 28, 28, 128, 3, 3, (1, 1), (2, 2, 2, 2), (2, 2),
         "bf16", "bf16", "bf16", "tanh", 0.0, U01, U01, U01),
+    # The other element-wise activations of the matmul + activation class
+    # (ops-nn article, 融合算子分类): the 4096^3 GEMM with GELU, and the
+    # ConvSigmoid twin of the fp16 3x3 conv (Fused ConvTanh article, 核心问题).
+    "gemm_gelu_4096_bf16": GemmCase(
+        "gemm_gelu_4096_bf16", 4096, 4096, 4096, "bf16", "f32", "bf16", "gelu", 0.0,
+        ("normal", 1.0 / 64.0), ("normal", 1.0 / 64.0), U01),
+    "conv3x3_sigmoid_8x64x56_f16": ConvCase(
+        "conv3x3_sigmoid_8x64x56_f16", 8, 64, 56, 56, 64, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1),
+        "f16", "f16", "f16", "sigmoid", 0.0, U01, U01, U01),
 }
 
 # Which case each named workload group covers (group 1 is the small spec case,
@@ -209,6 +218,7 @@ GROUPS = {
     3: ["conv3x3_tanh_8x64x56_f16"],
     4: ["conv7x7s2_tanh_16x3x224_f32", "conv1x1s2_tanh_16x256x56_f32"],
     5: ["gemm_leaky_32768x4096x1024_bf16", "conv3x3d2_tanh_32x128x28_bf16"],
+    6: ["gemm_gelu_4096_bf16", "conv3x3_sigmoid_8x64x56_f16"],      # epilogue extensions
 }
 
 
