@@ -48,6 +48,7 @@ def _bind(lib):
     lib.orc_decode.argtypes = [ctypes.c_int, ctypes.c_void_p, i64, _D]
     lib.orc_act_array.argtypes = [ctypes.c_int, ctypes.c_double, _D, _D, i64]
     lib.orc_act_array.restype = None
+    lib.orc_residual_act.argtypes = [_D, _D, _D, i64, ctypes.c_int, ctypes.c_double]
     lib.orc_gemm_bias_act.argtypes = [_D, _D, _D, _D, i64, i64, i64, ctypes.c_int, ctypes.c_double]
     lib.orc_gemm_bias_act_elems.argtypes = [_D, _D, _D, i64, i64, i64, _I64, _I64, i64,
                                             ctypes.c_int, ctypes.c_double, _D]
@@ -127,6 +128,15 @@ class Oracle:
         self.lib.orc_act_array(ACT_CODES[act], float(alpha), _dp(z), _dp(y), z.size)
         return y
 
+    def residual_act(self, z, r, act: str, alpha: float = 0.0) -> np.ndarray:
+        """act(z + r) elementwise; z is a pre-activation (contraction + bias)."""
+        z = _f64(z)
+        r = _f64(r).reshape(z.shape)
+        y = np.empty_like(z)
+        _check(self.lib.orc_residual_act(_dp(z), _dp(r), _dp(y), z.size, ACT_CODES[act],
+                                         float(alpha)), "residual_act")
+        return y
+
     # -- GEMM --------------------------------------------------------------
     def gemm(self, A, B, bias, act: str, alpha: float = 0.0) -> np.ndarray:
         A, B = _f64(A), _f64(B)
@@ -153,6 +163,14 @@ class Oracle:
                                                 ii.size, ACT_CODES[act], float(alpha), _dp(out)),
                "gemm_elems")
         return out
+
+    def gemm_residual(self, A, B, bias, R, act: str, alpha: float = 0.0) -> np.ndarray:
+        """C = act(A.B + bias + R), R of C's shape."""
+        return self.residual_act(self.gemm(A, B, bias, "none"), R, act, alpha)
+
+    def gemm_residual_elems(self, A, B, bias, R_flat_at, ii, jj, act: str, alpha: float = 0.0):
+        """The elements (ii, jj) of act(A.B + bias + R); R_flat_at holds R at those elements."""
+        return self.residual_act(self.gemm_elems(A, B, bias, ii, jj, "none"), R_flat_at, act, alpha)
 
     def gemm_bias_fold(self, A, B, bias, act: str, alpha: float = 0.0) -> np.ndarray:
         A, B = _f64(A), _f64(B)
@@ -210,6 +228,17 @@ class Oracle:
                                                   idx.size, ACT_CODES[act], float(alpha), _dp(out)),
                "conv2d_elems")
         return out
+
+    def conv2d_residual(self, x, w, bias, R, strides, pads, dilations, act: str,
+                        alpha: float = 0.0):
+        """y = act(conv2d(x, w) + bias + R), R of y's shape."""
+        z = self.conv2d(x, w, bias, strides, pads, dilations, "none")
+        return self.residual_act(z, R, act, alpha)
+
+    def conv2d_residual_elems(self, x, w, bias, R_flat_at, strides, pads, dilations, idx,
+                              act: str, alpha: float = 0.0):
+        z = self.conv2d_elems(x, w, bias, strides, pads, dilations, idx, "none")
+        return self.residual_act(z, R_flat_at, act, alpha)
 
     def conv2d_im2col(self, x, w, bias, strides, pads, dilations, act: str, alpha: float = 0.0,
                       fold_bias: bool = False):

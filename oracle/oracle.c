@@ -141,6 +141,16 @@ static int act_ok(int act)
     return act >= ORC_ACT_NONE && act <= ORC_ACT_SIGMOID;
 }
 
+/* The residual joins the sum before the activation: act(A.B + bias + R). */
+int orc_residual_act(const double *z, const double *r, double *y, int64_t n, int act,
+                     double alpha)
+{
+    if (!z || !r || !y || n < 0 || !act_ok(act))
+        return -1;
+    for (int64_t i = 0; i < n; ++i) y[i] = orc_act(act, z[i] + r[i], alpha);
+    return 0;
+}
+
 /* ---- GEMM -------------------------------------------------------------- */
 
 int orc_gemm_bias_act(const double *A, const double *B, const double *bias,

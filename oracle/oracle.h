@@ -40,6 +40,14 @@ double orc_bf16_to_f64(uint16_t h);
 double orc_f32_to_f64(uint32_t u);
 int orc_decode(int dtype, const void *src, int64_t n, double *dst);
 
+/* Residual epilogue: y[i] = act(z[i] + r[i]) for a pre-activation z taken
+ * from the GEMM / conv functions with act = NONE (the contraction plus bias)
+ * and a residual r of the output's shape: the "matmul + add + bias" fusion
+ * of the math class in the ops-nn article (section
+ * ops-nn的融合算子分类与适用场景, residual networks). */
+int orc_residual_act(const double *z, const double *r, double *y, int64_t n, int act,
+                     double alpha);
+
 /* Activation applied to one pre-activation value z (in double). */
 double orc_act(int act, double z, double alpha);
 void orc_act_array(int act, double alpha, const double *z, double *y, int64_t n);

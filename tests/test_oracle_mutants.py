@@ -33,6 +33,12 @@ MUTANTS = [
      "return z * 0.5 * erfc(z / sqrt(2.0));"),
     ("gelu via 1 + erf (cancels in the tail)", "return z * 0.5 * erfc(-z / sqrt(2.0));",
      "return z * 0.5 * (1.0 + erf(z / sqrt(2.0)));"),
+    ("residual dropped", "for (int64_t i = 0; i < n; ++i) y[i] = orc_act(act, z[i] + r[i], alpha);",
+     "for (int64_t i = 0; i < n; ++i) y[i] = orc_act(act, z[i], alpha);"),
+    ("residual after the activation", "for (int64_t i = 0; i < n; ++i) y[i] = orc_act(act, z[i] + r[i], alpha);",
+     "for (int64_t i = 0; i < n; ++i) y[i] = orc_act(act, z[i], alpha) + r[i];"),
+    ("residual subtracted", "for (int64_t i = 0; i < n; ++i) y[i] = orc_act(act, z[i] + r[i], alpha);",
+     "for (int64_t i = 0; i < n; ++i) y[i] = orc_act(act, z[i] - r[i], alpha);"),
     ("sigmoid sign", "if (z >= 0.0) return 1.0 / (1.0 + exp(-z));", "if (z >= 0.0) return 1.0 / (1.0 + exp(z));"),
     ("sigmoid negative branch", "return exp(z) / (1.0 + exp(z));", "return 1.0 / (1.0 + exp(z));"),
     ("gemm bias dropped", "double z = acc[j] + (bias ? bias[j] : 0.0);", "double z = acc[j];"),

@@ -255,6 +255,54 @@ def test_gemm_tiny_integer_bruteforce(M, N, K):
         assert [[Fraction(v) for v in r] for r in got.tolist()] == want, act
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (2, 3, 5), (7, 5, 3), (4, 6, 2)])
+def test_gemm_residual_tiny_integer_bruteforce(M, N, K):
+    # act(A.B + bias + R), the residual joining the sum before the activation
+    # ("matmul + add + bias" of the ops-nn math class), exactly
+    rng = np.random.default_rng(M * 37 + N * 11 + K)
+    A = rng.integers(-2, 3, (M, K)).tolist()
+    B = rng.integers(-2, 3, (K, N)).tolist()
+    bias = rng.integers(-2, 3, N).tolist()
+    R = rng.integers(-3, 4, (M, N)).tolist()
+    for act in ("none", "relu", "leaky_relu"):
+        base = _exact_gemm(A, B, bias, "none", None)
+        want = []
+        for i in range(M):
+            row = []
+            for j in range(N):
+                z = base[i][j] + Fraction(R[i][j])
+                if act == "relu":
+                    z = z if z > 0 else Fraction(0)
+                elif act == "leaky_relu":
+                    z = z if z >= 0 else Fraction(1, 4) * z
+                row.append(z)
+            want.append(row)
+        got = O.gemm_residual(A, B, bias, np.array(R, dtype=np.float64), act, 0.25)
+        assert [[Fraction(v) for v in r] for r in got.tolist()] == want, act
+
+
+def test_residual_special_cases():
+    rng = np.random.default_rng(3)
+    A = rng.standard_normal((6, 9))
+    B = rng.standard_normal((9, 5))
+    bias = rng.standard_normal(5)
+    # R = 0 gives the epilogue without a residual, bit for bit
+    for act in ("none", "relu", "tanh", "gelu", "sigmoid"):
+        assert np.array_equal(O.gemm_residual(A, B, bias, np.zeros((6, 5)), act),
+                              O.gemm(A, B, bias, act))
+    # an empty sum (K = 0) leaves act(bias + R): tanh(ln 2) = 3/5 at z = ln 2
+    R = np.full((3, 5), math.log(2.0)) - np.zeros(5)
+    got = O.gemm_residual(np.zeros((3, 0)), np.zeros((0, 5)), np.zeros(5), R, "tanh")
+    assert np.all(np.abs(got - 0.6) <= 4e-16)
+    # R = -(A.B + bias) cancels the sum: ReLU of it is +0, Sigmoid 1/2
+    z = O.gemm(A, B, bias, "none")
+    assert np.array_equal(O.gemm_residual(A, B, bias, -z, "relu"), np.zeros((6, 5)))
+    assert np.array_equal(O.gemm_residual(A, B, bias, -z, "sigmoid"), np.full((6, 5), 0.5))
+    # the residual is indexed like C (row-major [M, N]), not transposed
+    Rr = np.arange(30, dtype=np.float64).reshape(6, 5)
+    assert np.array_equal(O.gemm_residual(A, B, bias, Rr, "none") - z, Rr)
+
+
 def test_gemm_matches_numpy_matmul():
     rng = np.random.default_rng(1)
     M, N, K = 37, 53, 61                     # all different: a transposed operand cannot fit
@@ -350,6 +398,27 @@ def test_conv_matches_torch_conv2d_float64(shape):
     got = O.conv2d(x, w, b, st, pd, dl, "none")
     assert got.shape == ref.shape
     assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("shape", _CONV_SHAPES[1:4])
+def test_conv_residual_matches_torch_float64(shape):
+    # y = act(conv2d(x, w) + bias + R) with R [N, Co, Ho, Wo], against torch in float64
+    torch = pytest.importorskip("torch")
+    import torch.nn.functional as F
+    N, C, H, W, Co, kh, kw, st, pd, dl = shape
+    rng = np.random.default_rng(sum(shape[:7]) + 5)
+    x = rng.standard_normal((N, C, H, W))
+    w = rng.standard_normal((Co, C, kh, kw))
+    b = rng.standard_normal(Co)
+    xt = F.pad(torch.from_numpy(x), (pd[2], pd[3], pd[0], pd[1]))
+    conv = F.conv2d(xt, torch.from_numpy(w), torch.from_numpy(b), stride=st, dilation=dl)
+    R = rng.standard_normal(tuple(conv.shape))
+    ref = torch.tanh(conv + torch.from_numpy(R)).numpy()
+    got = O.conv2d_residual(x, w, b, R, st, pd, dl, "tanh")
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+    idx = np.arange(0, got.size, 3)
+    assert np.array_equal(O.conv2d_residual_elems(x, w, b, R.ravel()[idx], st, pd, dl, idx, "tanh"),
+                          got.ravel()[idx])
 
 
 @pytest.mark.parametrize("shape", _CONV_SHAPES)
