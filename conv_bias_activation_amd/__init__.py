@@ -23,6 +23,10 @@ from ._binding import (  # noqa: F401
     last_tile_config,
     force_tile_config,
     gemm_bias_act,
+    gemm_bias_add_act,
+    gemm_bias_add_act_2k,
+    conv2d_bias_add_act,
+    conv2d_bias_add_act_2k,
     gemm_bias_act_2k,
     gemm_bias_act_workspace_size,
     gemm_tile_config,

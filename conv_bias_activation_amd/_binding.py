@@ -48,6 +48,16 @@ def _load():
     l.conv2d_bias_act_2k.argtypes = conv + [vp, ctypes.c_size_t, vp]
     l.conv2d_bias_act_2k.restype = ctypes.c_int
     l.conv2d_bias_act_workspace_size.argtypes = [i64] * 7 + [i32p, i32p, i32p]
+    gr = [vp, vp, vp, vp, vp, i64, i64, i64, u32, ctypes.c_int, ctypes.c_float]
+    l.gemm_bias_add_act.argtypes = gr + [vp]
+    l.gemm_bias_add_act.restype = ctypes.c_int
+    l.gemm_bias_add_act_2k.argtypes = gr + [vp, ctypes.c_size_t, vp]
+    l.gemm_bias_add_act_2k.restype = ctypes.c_int
+    cr = [vp, vp, vp, vp, vp] + [i64] * 7 + [i32p, i32p, i32p, u32, ctypes.c_int]
+    l.conv2d_bias_add_act.argtypes = cr + [vp]
+    l.conv2d_bias_add_act.restype = ctypes.c_int
+    l.conv2d_bias_add_act_2k.argtypes = cr + [vp, ctypes.c_size_t, vp]
+    l.conv2d_bias_add_act_2k.restype = ctypes.c_int
     l.conv2d_bias_act_workspace_size.restype = ctypes.c_size_t
     l.biasact_status_string.argtypes = [ctypes.c_int]
     l.biasact_status_string.restype = ctypes.c_char_p
@@ -187,6 +197,37 @@ def gemm_bias_act_2k(A, B, bias, C, act="none", alpha: float = 0.0, workspace=No
     return C
 
 
+def _residual(R, out, name="R"):
+    if R is None:
+        raise ValueError(f"{name} (the residual, shaped and typed like the output) is required")
+    if tuple(R.shape) != tuple(out.shape) or R.dtype != out.dtype:
+        raise ValueError(f"{name} must match the output: {tuple(out.shape)} {out.dtype}, "
+                         f"got {tuple(R.shape)} {R.dtype}")
+    return _dev(R, name)
+
+
+def gemm_bias_add_act(A, B, bias, R, C, act="none", alpha: float = 0.0, stream=None):
+    """C = act(A @ B + bias + R); R like C (may be C itself)."""
+    M, N, K, dt = _gemm_args(A, B, bias, C)
+    rc = lib.gemm_bias_add_act(_dev(A, "A"), _dev(B, "B"), _dev(bias, "bias"), _residual(R, C),
+                               _dev(C, "C"), M, N, K, dt, _act(act), float(alpha), _stream(stream))
+    _check(rc, "gemm_bias_add_act")
+    return C
+
+
+def gemm_bias_add_act_2k(A, B, bias, R, C, act="none", alpha: float = 0.0, workspace=None,
+                         stream=None):
+    M, N, K, dt = _gemm_args(A, B, bias, C)
+    if workspace is None:
+        raise ValueError("workspace (device buffer of gemm_bias_act_workspace_size bytes) is required")
+    nbytes = workspace.numel() * workspace.element_size()
+    rc = lib.gemm_bias_add_act_2k(_dev(A, "A"), _dev(B, "B"), _dev(bias, "bias"), _residual(R, C),
+                                  _dev(C, "C"), M, N, K, dt, _act(act), float(alpha),
+                                  _dev(workspace, "workspace"), nbytes, _stream(stream))
+    _check(rc, "gemm_bias_add_act_2k")
+    return C
+
+
 # -- conv2d ----------------------------------------------------------------
 
 def conv_out_hw(H, W, kh, kw, strides, pads, dilations):
@@ -245,6 +286,33 @@ def conv2d_bias_act_2k(x, w, bias, y, strides=(1, 1), pads=(0, 0, 0, 0), dilatio
                                 _i32x(dilations, 2, "dilations"), dt, _act(act),
                                 _dev(workspace, "workspace"), nbytes, _stream(stream))
     _check(rc, "conv2d_bias_act_2k")
+    return y
+
+
+def conv2d_bias_add_act(x, w, bias, R, y, strides=(1, 1), pads=(0, 0, 0, 0), dilations=(1, 1),
+                        act="tanh", stream=None):
+    """y = act(conv2d(x, w) + bias + R); R like y (may be y itself)."""
+    dims, dt = _conv_args(x, w, bias, y, strides, pads, dilations)
+    rc = lib.conv2d_bias_add_act(_dev(x, "x"), _dev(w, "w"), _dev(bias, "bias"), _residual(R, y),
+                                 _dev(y, "y"), *dims, _i32x(strides, 2, "strides"),
+                                 _i32x(pads, 4, "pads"), _i32x(dilations, 2, "dilations"), dt,
+                                 _act(act), _stream(stream))
+    _check(rc, "conv2d_bias_add_act")
+    return y
+
+
+def conv2d_bias_add_act_2k(x, w, bias, R, y, strides=(1, 1), pads=(0, 0, 0, 0), dilations=(1, 1),
+                           act="tanh", workspace=None, stream=None):
+    dims, dt = _conv_args(x, w, bias, y, strides, pads, dilations)
+    if workspace is None:
+        raise ValueError("workspace (device buffer of conv2d_bias_act_workspace_size bytes) is required")
+    nbytes = workspace.numel() * workspace.element_size()
+    rc = lib.conv2d_bias_add_act_2k(_dev(x, "x"), _dev(w, "w"), _dev(bias, "bias"), _residual(R, y),
+                                    _dev(y, "y"), *dims, _i32x(strides, 2, "strides"),
+                                    _i32x(pads, 4, "pads"), _i32x(dilations, 2, "dilations"), dt,
+                                    _act(act), _dev(workspace, "workspace"), nbytes,
+                                    _stream(stream))
+    _check(rc, "conv2d_bias_add_act_2k")
     return y
 
 

@@ -32,13 +32,18 @@ int launch_status() {
   return kErrHip;
 }
 
+bool aligned_for(const void* p, int dt) {
+  return ((uintptr_t)p % (dt == DT_F32 ? 16u : 8u)) == 0;
+}
+
 int launch_gemm_plan(const GemmPlan& p, const void* A, const void* B, const void* bias, void* C,
-                     int dto, int act, float alpha, hipStream_t s) {
+                     const void* R, int dto, int act, float alpha, hipStream_t s) {
   GemmArgs a;
   a.A = A;
   a.B = B;
   a.bias = bias;
   a.C = C;
+  a.R = R;
   a.M = p.M;
   a.N = p.N;
   a.K = p.K;
@@ -53,7 +58,7 @@ int launch_gemm_plan(const GemmPlan& p, const void* A, const void* B, const void
   a.tiles_n = p.tiles_n;
   a.vec_a = p.vec_a;
   a.vec_b = p.vec_b;
-  a.vec_c = p.N % 4 == 0 && ((uintptr_t)C % (dto == DT_F32 ? 16u : 8u)) == 0;
+  a.vec_c = p.N % 4 == 0 && aligned_for(C, dto) && (!R || aligned_for(R, dto));
   int rc;
   switch (p.dti) {
     case DT_F32: rc = launch_gemm_f32(dto, p.tile, a, s); break;
@@ -66,12 +71,13 @@ int launch_gemm_plan(const GemmPlan& p, const void* A, const void* B, const void
 }
 
 int launch_conv_plan(const ConvPlan& p, const void* x, const void* w, const void* bias, void* y,
-                     int dto, int act, hipStream_t s) {
+                     const void* r, int dto, int act, hipStream_t s) {
   ConvArgs a;
   a.x = x;
   a.w = w;
   a.bias = bias;
   a.y = y;
+  a.r = r;
   ConvGeom& g = a.geom;
   g.N = p.N; g.C = p.C; g.H = p.H; g.W = p.W; g.Co = p.Co; g.kh = p.kh; g.kw = p.kw;
   g.Ho = p.Ho; g.Wo = p.Wo;
@@ -90,7 +96,7 @@ int launch_conv_plan(const ConvPlan& p, const void* x, const void* w, const void
   a.tiles_m = p.tiles_m;
   a.tiles_n = p.tiles_n;
   a.vec_w = p.vec_w;
-  a.vec_y = (p.Ho * p.Wo) % 4 == 0 && ((uintptr_t)y % (dto == DT_F32 ? 16u : 8u)) == 0;
+  a.vec_y = (p.Ho * p.Wo) % 4 == 0 && aligned_for(y, dto) && (!r || aligned_for(r, dto));
   int rc;
   if (p.tile == 7) {
     HaloArgs h;
@@ -98,6 +104,7 @@ int launch_conv_plan(const ConvPlan& p, const void* x, const void* w, const void
     h.w = w;
     h.bias = bias;
     h.y = y;
+    h.r = r;
     h.geom = a.geom;
     h.x_bytes = a.x_bytes;
     h.w_bytes = a.w_bytes;
@@ -115,7 +122,7 @@ int launch_conv_plan(const ConvPlan& p, const void* x, const void* w, const void
     h.w_blocks = p.h_w_blocks;
     h.h_blocks = p.h_h_blocks;
     h.blocks = p.h_blocks;
-    h.vec_y = p.Wo % 4 == 0 && ((uintptr_t)y % (dto == DT_F32 ? 16u : 8u)) == 0;
+    h.vec_y = p.Wo % 4 == 0 && aligned_for(y, dto) && (!r || aligned_for(r, dto));
     h.hrcp = p.h_hrcp;
     h.div_hc = make_fastdiv(p.h_HC ? p.h_HC : 1u);
     h.kstr = p.h_kstr;
@@ -136,10 +143,63 @@ int launch_conv_plan(const ConvPlan& p, const void* x, const void* w, const void
 }
 
 int launch_second_kernel(int dto, const void* ws, void* out, uint64_t n, int act, float alpha,
-                         hipStream_t s) {
-  if (launch_act_cast(dto, static_cast<const float*>(ws), out, (uint32_t)n, act, alpha, s))
+                         const void* res, hipStream_t s) {
+  if (launch_act_cast(dto, static_cast<const float*>(ws), out, (uint32_t)n, act, alpha, res, s))
     return kErrUnsupported;
   return launch_status();
+}
+
+// Shared bodies of the entry points; R / r is the residual or null.
+int gemm_impl(const void* A, const void* B, const void* bias, const void* R, void* C, int64_t M,
+              int64_t N, int64_t K, uint32_t dtypes, int act, float alpha, hipStream_t stream) {
+  GemmPlan p;
+  int rc = plan_gemm(A, B, bias, C, M, N, K, dtypes, act, &p, R);
+  if (rc || p.empty) return rc;
+  return launch_gemm_plan(p, A, B, bias, C, R, p.dto, act, alpha, stream);
+}
+
+int gemm_2k_impl(const void* A, const void* B, const void* bias, const void* R, void* C, int64_t M,
+                 int64_t N, int64_t K, uint32_t dtypes, int act, float alpha, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream) {
+  GemmPlan p;
+  int rc = plan_gemm(A, B, bias, C, M, N, K, dtypes, act, &p, R);
+  if (rc || p.empty) return rc;
+  const uint64_t need = (uint64_t)M * (uint64_t)N * 4u;
+  if (need >= (1ull << 31)) return kErrUnsupported;
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % 16) != 0) return kErrInvalid;
+  // kernel 1: same main loop, fp32 pre-activation (A.B + bias) to the workspace
+  rc = launch_gemm_plan(p, A, B, bias, workspace, nullptr, DT_F32, BA_ACT_NONE, 0.0f, stream);
+  if (rc) return rc;
+  // kernel 2: residual, activation and cast
+  return launch_second_kernel(p.dto, workspace, C, need / 4u, act, alpha, R, stream);
+}
+
+int conv_impl(const void* x, const void* w, const void* bias, const void* r, void* y, int64_t N,
+              int64_t C, int64_t H, int64_t W, int64_t Co, int64_t kh, int64_t kw,
+              const int32_t strides[2], const int32_t pads[4], const int32_t dilations[2],
+              uint32_t dtypes, int act, hipStream_t stream) {
+  ConvPlan p;
+  int rc = plan_conv(x, w, bias, y, N, C, H, W, Co, kh, kw, strides, pads, dilations, dtypes, act,
+                     &p, r);
+  if (rc || p.empty) return rc;
+  return launch_conv_plan(p, x, w, bias, y, r, p.dto, act, stream);
+}
+
+int conv_2k_impl(const void* x, const void* w, const void* bias, const void* r, void* y, int64_t N,
+                 int64_t C, int64_t H, int64_t W, int64_t Co, int64_t kh, int64_t kw,
+                 const int32_t strides[2], const int32_t pads[4], const int32_t dilations[2],
+                 uint32_t dtypes, int act, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream) {
+  ConvPlan p;
+  int rc = plan_conv(x, w, bias, y, N, C, H, W, Co, kh, kw, strides, pads, dilations, dtypes, act,
+                     &p, r);
+  if (rc || p.empty) return rc;
+  const uint64_t need = (uint64_t)p.N * p.Co * p.Ho * p.Wo * 4u;
+  if (need >= (1ull << 31)) return kErrUnsupported;
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % 16) != 0) return kErrInvalid;
+  rc = launch_conv_plan(p, x, w, bias, workspace, nullptr, DT_F32, BA_ACT_NONE, stream);
+  if (rc) return rc;
+  return launch_second_kernel(p.dto, workspace, y, need / 4u, act, 0.0f, r, stream);
 }
 
 }  // namespace
@@ -148,10 +208,7 @@ extern "C" {
 
 int gemm_bias_act(const void* A, const void* B, const void* bias, void* C, int64_t M, int64_t N,
                   int64_t K, uint32_t dtypes, int act, float alpha, hipStream_t stream) {
-  GemmPlan p;
-  int rc = plan_gemm(A, B, bias, C, M, N, K, dtypes, act, &p);
-  if (rc || p.empty) return rc;
-  return launch_gemm_plan(p, A, B, bias, C, p.dto, act, alpha, stream);
+  return gemm_impl(A, B, bias, nullptr, C, M, N, K, dtypes, act, alpha, stream);
 }
 
 size_t gemm_bias_act_workspace_size(int64_t M, int64_t N) {
@@ -162,28 +219,31 @@ size_t gemm_bias_act_workspace_size(int64_t M, int64_t N) {
 int gemm_bias_act_2k(const void* A, const void* B, const void* bias, void* C, int64_t M, int64_t N,
                      int64_t K, uint32_t dtypes, int act, float alpha, void* workspace,
                      size_t workspace_bytes, hipStream_t stream) {
-  GemmPlan p;
-  int rc = plan_gemm(A, B, bias, C, M, N, K, dtypes, act, &p);
-  if (rc || p.empty) return rc;
-  const uint64_t need = (uint64_t)M * (uint64_t)N * 4u;
-  if (need >= (1ull << 31)) return kErrUnsupported;
-  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % 16) != 0) return kErrInvalid;
-  // kernel 1: same main loop, fp32 pre-activation to the workspace
-  rc = launch_gemm_plan(p, A, B, bias, workspace, DT_F32, BA_ACT_NONE, 0.0f, stream);
-  if (rc) return rc;
-  // kernel 2: activation + cast
-  return launch_second_kernel(p.dto, workspace, C, need / 4u, act, alpha, stream);
+  return gemm_2k_impl(A, B, bias, nullptr, C, M, N, K, dtypes, act, alpha, workspace,
+                      workspace_bytes, stream);
+}
+
+int gemm_bias_add_act(const void* A, const void* B, const void* bias, const void* R, void* C,
+                      int64_t M, int64_t N, int64_t K, uint32_t dtypes, int act, float alpha,
+                      hipStream_t stream) {
+  if (!R && M > 0 && N > 0) return kErrInvalid;
+  return gemm_impl(A, B, bias, R, C, M, N, K, dtypes, act, alpha, stream);
+}
+
+int gemm_bias_add_act_2k(const void* A, const void* B, const void* bias, const void* R, void* C,
+                         int64_t M, int64_t N, int64_t K, uint32_t dtypes, int act, float alpha,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!R && M > 0 && N > 0) return kErrInvalid;
+  return gemm_2k_impl(A, B, bias, R, C, M, N, K, dtypes, act, alpha, workspace, workspace_bytes,
+                      stream);
 }
 
 int conv2d_bias_act(const void* x, const void* w, const void* bias, void* y, int64_t N, int64_t C,
                     int64_t H, int64_t W, int64_t Co, int64_t kh, int64_t kw,
                     const int32_t strides[2], const int32_t pads[4], const int32_t dilations[2],
                     uint32_t dtypes, int act, hipStream_t stream) {
-  ConvPlan p;
-  int rc = plan_conv(x, w, bias, y, N, C, H, W, Co, kh, kw, strides, pads, dilations, dtypes, act,
-                     &p);
-  if (rc || p.empty) return rc;
-  return launch_conv_plan(p, x, w, bias, y, p.dto, act, stream);
+  return conv_impl(x, w, bias, nullptr, y, N, C, H, W, Co, kh, kw, strides, pads, dilations,
+                   dtypes, act, stream);
 }
 
 size_t conv2d_bias_act_workspace_size(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Co,
@@ -203,16 +263,27 @@ int conv2d_bias_act_2k(const void* x, const void* w, const void* bias, void* y, 
                        const int32_t strides[2], const int32_t pads[4],
                        const int32_t dilations[2], uint32_t dtypes, int act, void* workspace,
                        size_t workspace_bytes, hipStream_t stream) {
-  ConvPlan p;
-  int rc = plan_conv(x, w, bias, y, N, C, H, W, Co, kh, kw, strides, pads, dilations, dtypes, act,
-                     &p);
-  if (rc || p.empty) return rc;
-  const uint64_t need = (uint64_t)p.N * p.Co * p.Ho * p.Wo * 4u;
-  if (need >= (1ull << 31)) return kErrUnsupported;
-  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % 16) != 0) return kErrInvalid;
-  rc = launch_conv_plan(p, x, w, bias, workspace, DT_F32, BA_ACT_NONE, stream);
-  if (rc) return rc;
-  return launch_second_kernel(p.dto, workspace, y, need / 4u, act, 0.0f, stream);
+  return conv_2k_impl(x, w, bias, nullptr, y, N, C, H, W, Co, kh, kw, strides, pads, dilations,
+                      dtypes, act, workspace, workspace_bytes, stream);
+}
+
+int conv2d_bias_add_act(const void* x, const void* w, const void* bias, const void* r, void* y,
+                        int64_t N, int64_t C, int64_t H, int64_t W, int64_t Co, int64_t kh,
+                        int64_t kw, const int32_t strides[2], const int32_t pads[4],
+                        const int32_t dilations[2], uint32_t dtypes, int act, hipStream_t stream) {
+  if (!r && N > 0) return kErrInvalid;
+  return conv_impl(x, w, bias, r, y, N, C, H, W, Co, kh, kw, strides, pads, dilations, dtypes,
+                   act, stream);
+}
+
+int conv2d_bias_add_act_2k(const void* x, const void* w, const void* bias, const void* r, void* y,
+                           int64_t N, int64_t C, int64_t H, int64_t W, int64_t Co, int64_t kh,
+                           int64_t kw, const int32_t strides[2], const int32_t pads[4],
+                           const int32_t dilations[2], uint32_t dtypes, int act, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  if (!r && N > 0) return kErrInvalid;
+  return conv_2k_impl(x, w, bias, r, y, N, C, H, W, Co, kh, kw, strides, pads, dilations, dtypes,
+                      act, workspace, workspace_bytes, stream);
 }
 
 const char* biasact_status_string(int status) { return status_string(status); }

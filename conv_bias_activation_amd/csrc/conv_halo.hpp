@@ -372,10 +372,12 @@ __global__ __launch_bounds__(256, (occupancy<BM, KS, SN>())) void conv16_halo_ke
     bv[sj] = a.bias_dt == DT_F32 ? __uint_as_float(braw[sj])
              : a.bias_dt == DT_F16 ? widen<DT_F16>(braw[sj]) : widen<DT_BF16>(braw[sj]);
   const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.y, a.y_bytes);
+  const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.r, a.r ? a.y_bytes : 0u);
   const uint32_t howo = G.Ho * G.Wo;
   const uint32_t npos = a.PH * a.PW;
-  auto epilogue = [&](auto act_c) __attribute__((always_inline)) {
+  auto epilogue = [&](auto act_c, auto res_c) __attribute__((always_inline)) {
     constexpr int ACT = decltype(act_c)::value;
+    constexpr bool HAS_R = decltype(res_c)::value;
 #pragma unroll
     for (int si = 0; si < SN; ++si)
 #pragma unroll
@@ -386,15 +388,23 @@ __global__ __launch_bounds__(256, (occupancy<BM, KS, SN>())) void conv16_halo_ke
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const uint32_t q = wave_n * WTN + si * 32 + 8 * g + 4 * half;
-          float v[4];
+          float z[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = act_fn<ACT>(acc[si][sj][4 * g + e] + bv[sj], a.alpha);
+          for (int e = 0; e < 4; ++e) z[e] = acc[si][sj][4 * g + e] + bv[sj];
           if (a.vec_y) {
             // PW % 4 == 0 and Wo % 4 == 0: positions q..q+3 share an output row
             const uint32_t qh = q / a.PW, qw = q - qh * a.PW;
             const uint32_t oh = oh0 + qh, ow = ow0 + qw;
             const bool ok = cok && q < npos && oh < G.Ho && ow < G.Wo;
-            store4<DTO>(ry, ybase + oh * G.Wo + ow, ok, v[0], v[1], v[2], v[3]);
+            if constexpr (HAS_R) {
+              float rv[4];
+              load4<DTO>(rr, ybase + oh * G.Wo + ow, ok, rv);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) z[e] += rv[e];
+            }
+            store4<DTO>(ry, ybase + oh * G.Wo + ow, ok, act_fn<ACT>(z[0], a.alpha),
+                        act_fn<ACT>(z[1], a.alpha), act_fn<ACT>(z[2], a.alpha),
+                        act_fn<ACT>(z[3], a.alpha));
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -402,20 +412,19 @@ __global__ __launch_bounds__(256, (occupancy<BM, KS, SN>())) void conv16_halo_ke
               const uint32_t qh = qe / a.PW, qw = qe - qh * a.PW;
               const uint32_t oh = oh0 + qh, ow = ow0 + qw;
               const bool ok = cok && qe < npos && oh < G.Ho && ow < G.Wo;
-              store1<DTO>(ry, ybase + oh * G.Wo + ow, ok, v[e]);
+              float ze = z[e];
+              if constexpr (HAS_R) ze += load1<DTO>(rr, ybase + oh * G.Wo + ow, ok);
+              store1<DTO>(ry, ybase + oh * G.Wo + ow, ok, act_fn<ACT>(ze, a.alpha));
             }
           }
         }
       }
   };
-  switch (a.act) {
-    case ACT_RELU: epilogue(std::integral_constant<int, ACT_RELU>{}); break;
-    case ACT_LEAKY: epilogue(std::integral_constant<int, ACT_LEAKY>{}); break;
-    case ACT_TANH: epilogue(std::integral_constant<int, ACT_TANH>{}); break;
-    case ACT_GELU: epilogue(std::integral_constant<int, ACT_GELU>{}); break;
-    case ACT_SIGMOID: epilogue(std::integral_constant<int, ACT_SIGMOID>{}); break;
-    default: epilogue(std::integral_constant<int, ACT_NONE>{}); break;
-  }
+  // activation and residual dispatched once per workgroup
+  with_act(a.act, [&](auto act_c) __attribute__((always_inline)) {
+    with_residual(a.r != nullptr,
+                  [&](auto res_c) __attribute__((always_inline)) { epilogue(act_c, res_c); });
+  });
 }
 
 template <int DTI, int DTO, int T, int BM, int KS, int SN>

@@ -47,6 +47,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
 __device__ __forceinline__ u32x4 ld_b128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
+__device__ __forceinline__ u32x2 ld_b64(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+}
 __device__ __forceinline__ uint32_t ld_b32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
@@ -175,6 +178,14 @@ __device__ __forceinline__ float act_fn(float z, float alpha) {
   else if constexpr (ACT == ACT_GELU) return gelu_f32(z);
   else if constexpr (ACT == ACT_SIGMOID) return sigmoid_f32(z);
   else return z;
+}
+
+// Runs f(std::integral_constant<bool, HAS_R>{}): the epilogue with the residual
+// loads and adds, or without them.
+template <class F>
+__device__ __forceinline__ void with_residual(bool has_r, F&& f) {
+  if (has_r) f(std::integral_constant<bool, true>{});
+  else f(std::integral_constant<bool, false>{});
 }
 
 // Runs f(std::integral_constant<int, ACT>{}) for the runtime activation code:

@@ -34,6 +34,30 @@ __device__ __forceinline__ void load_bias_vec(const void* bias, uint32_t nbytes,
   }
 }
 
+// Residual values at four consecutive outputs (the layout of store4), or at
+// one, widened exactly to fp32; 0 where !ok.
+template <int DTO>
+__device__ __forceinline__ void load4(__amdgpu_buffer_rsrc_t r, uint32_t off_elems, bool ok,
+                                      float (&v)[4]) {
+  const uint32_t off = ok ? off_elems * Elem<DTO>::bytes : kOOB;
+  if constexpr (DTO == DT_F32) {
+    const u32x4 w = ld_b128(r, off);
+    v[0] = __uint_as_float(w.x); v[1] = __uint_as_float(w.y);
+    v[2] = __uint_as_float(w.z); v[3] = __uint_as_float(w.w);
+  } else {
+    const u32x2 w = ld_b64(r, off);
+    v[0] = widen<DTO>(w.x & 0xffffu); v[1] = widen<DTO>(w.x >> 16);
+    v[2] = widen<DTO>(w.y & 0xffffu); v[3] = widen<DTO>(w.y >> 16);
+  }
+}
+
+template <int DTO>
+__device__ __forceinline__ float load1(__amdgpu_buffer_rsrc_t r, uint32_t off_elems, bool ok) {
+  const uint32_t off = ok ? off_elems * Elem<DTO>::bytes : kOOB;
+  if constexpr (DTO == DT_F32) return __uint_as_float(ld_b32(r, off));
+  else return widen<DTO>(ld_b16(r, off));
+}
+
 // Store four consecutive outputs (one accumulator register group).
 template <int DTO>
 __device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t r, uint32_t off_elems, bool ok,

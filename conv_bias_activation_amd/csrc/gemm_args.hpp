@@ -11,8 +11,9 @@ struct GemmArgs {
   const void* B;
   const void* bias;
   void* C;
+  const void* R;           // residual [M, N] in C's type, added before the activation; may be null
   uint32_t M, N, K;
-  uint32_t a_bytes, b_bytes, bias_bytes, c_bytes;
+  uint32_t a_bytes, b_bytes, bias_bytes, c_bytes;   // R spans c_bytes too
   int bias_dt;             // DT_* of bias, or -1 without bias
   int act;
   float alpha;

@@ -233,22 +233,33 @@ __global__ __launch_bounds__(512, 1) void gemm16_pp_kernel(GemmArgs a) {
 
   // ---- epilogue: activation, cast, one store per element -----------------
   const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.C, a.c_bytes);
+  const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.R, a.R ? a.c_bytes : 0u);
   with_act(a.act, [&](auto act_c) __attribute__((always_inline)) {
     constexpr int ACT = decltype(act_c)::value;
+    with_residual(a.R != nullptr, [&](auto res_c) __attribute__((always_inline)) {
+      constexpr bool HAS_R = decltype(res_c)::value;
 #pragma unroll
-    for (int si = 0; si < 2; ++si)
+      for (int si = 0; si < 2; ++si)
 #pragma unroll
-      for (int sj = 0; sj < 4; ++sj) {
-        const uint32_t m = m0 + wm * 128 + sj * 32 + lrow;
+        for (int sj = 0; sj < 4; ++sj) {
+          const uint32_t m = m0 + wm * 128 + sj * 32 + lrow;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const uint32_t n = n0 + wn * 64 + si * 32 + 8 * g + 4 * half;
-          store4<DTO>(rc, m * a.N + n, m < a.M && n < a.N, act_fn<ACT>(acc[si][sj][4 * g + 0], a.alpha),
-                      act_fn<ACT>(acc[si][sj][4 * g + 1], a.alpha),
-                      act_fn<ACT>(acc[si][sj][4 * g + 2], a.alpha),
-                      act_fn<ACT>(acc[si][sj][4 * g + 3], a.alpha));
+          for (int g = 0; g < 4; ++g) {
+            const uint32_t n = n0 + wn * 64 + si * 32 + 8 * g + 4 * half;
+            const bool ok = m < a.M && n < a.N;
+            float z[4] = {acc[si][sj][4 * g + 0], acc[si][sj][4 * g + 1], acc[si][sj][4 * g + 2],
+                          acc[si][sj][4 * g + 3]};
+            if constexpr (HAS_R) {
+              float rv[4];
+              load4<DTO>(rr, m * a.N + n, ok, rv);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) z[e] += rv[e];
+            }
+            store4<DTO>(rc, m * a.N + n, ok, act_fn<ACT>(z[0], a.alpha), act_fn<ACT>(z[1], a.alpha),
+                        act_fn<ACT>(z[2], a.alpha), act_fn<ACT>(z[3], a.alpha));
+          }
         }
-      }
+    });
   });
 }
 

@@ -66,8 +66,11 @@ __global__ __launch_bounds__(TL::threads, 1) void gemm_bias_act_kernel(GemmArgs 
 
   // epilogue: activation, cast, one store per element
   const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.C, a.c_bytes);
+  const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.R, a.R ? a.c_bytes : 0u);
   with_act(a.act, [&](auto act_c) __attribute__((always_inline)) {
   constexpr int ACT = decltype(act_c)::value;
+  with_residual(a.R != nullptr, [&](auto res_c) __attribute__((always_inline)) {
+  constexpr bool HAS_R = decltype(res_c)::value;
 #pragma unroll
   for (int si = 0; si < TL::SN; ++si)
 #pragma unroll
@@ -76,14 +79,27 @@ __global__ __launch_bounds__(TL::threads, 1) void gemm_bias_act_kernel(GemmArgs 
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const uint32_t n = n0 + wave_n * TL::WTN + si * 32 + 8 * g + 4 * half;
-        const float y0 = act_fn<ACT>(acc[si][sj][4 * g + 0], a.alpha);
-        const float y1 = act_fn<ACT>(acc[si][sj][4 * g + 1], a.alpha);
-        const float y2 = act_fn<ACT>(acc[si][sj][4 * g + 2], a.alpha);
-        const float y3 = act_fn<ACT>(acc[si][sj][4 * g + 3], a.alpha);
+        const bool mok = m < a.M;
+        float z[4] = {acc[si][sj][4 * g + 0], acc[si][sj][4 * g + 1], acc[si][sj][4 * g + 2],
+                      acc[si][sj][4 * g + 3]};
+        if constexpr (HAS_R) {
+          if (a.vec_c) {
+            float rv[4];
+            load4<DTO>(rr, m * a.N + n, mok && n < a.N, rv);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) z[e] += rv[e];
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) z[e] += load1<DTO>(rr, m * a.N + n + e, mok && n + e < a.N);
+          }
+        }
+        const float y0 = act_fn<ACT>(z[0], a.alpha);
+        const float y1 = act_fn<ACT>(z[1], a.alpha);
+        const float y2 = act_fn<ACT>(z[2], a.alpha);
+        const float y3 = act_fn<ACT>(z[3], a.alpha);
         if (a.vec_c) {
-          store4<DTO>(rc, m * a.N + n, m < a.M && n < a.N, y0, y1, y2, y3);
+          store4<DTO>(rc, m * a.N + n, mok && n < a.N, y0, y1, y2, y3);
         } else {
-          const bool mok = m < a.M;
           store1<DTO>(rc, m * a.N + n + 0, mok && n + 0 < a.N, y0);
           store1<DTO>(rc, m * a.N + n + 1, mok && n + 1 < a.N, y1);
           store1<DTO>(rc, m * a.N + n + 2, mok && n + 2 < a.N, y2);
@@ -91,6 +107,7 @@ __global__ __launch_bounds__(TL::threads, 1) void gemm_bias_act_kernel(GemmArgs 
         }
       }
     }
+  });
   });
 }
 
@@ -135,9 +152,12 @@ __global__ __launch_bounds__(TL::threads, 1) void conv_bias_act_kernel(ConvArgs 
   main_loop<DTI, TL>(acc, la, lb, smem, ktiles, init_acc);
 
   const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.y, a.y_bytes);
+  const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.r, a.r ? a.y_bytes : 0u);
   const uint32_t howo = G.Ho * G.Wo;
   with_act(a.act, [&](auto act_c) __attribute__((always_inline)) {
   constexpr int ACT = decltype(act_c)::value;
+  with_residual(a.r != nullptr, [&](auto res_c) __attribute__((always_inline)) {
+  constexpr bool HAS_R = decltype(res_c)::value;
 #pragma unroll
   for (int si = 0; si < TL::SN; ++si)
 #pragma unroll
@@ -147,46 +167,59 @@ __global__ __launch_bounds__(TL::threads, 1) void conv_bias_act_kernel(ConvArgs 
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const uint32_t p = p0 + wave_n * TL::WTN + si * 32 + 8 * g + 4 * half;
-        const float y0 = act_fn<ACT>(acc[si][sj][4 * g + 0], a.alpha);
-        const float y1 = act_fn<ACT>(acc[si][sj][4 * g + 1], a.alpha);
-        const float y2 = act_fn<ACT>(acc[si][sj][4 * g + 2], a.alpha);
-        const float y3 = act_fn<ACT>(acc[si][sj][4 * g + 3], a.alpha);
+        float z[4] = {acc[si][sj][4 * g + 0], acc[si][sj][4 * g + 1], acc[si][sj][4 * g + 2],
+                      acc[si][sj][4 * g + 3]};
         if (a.vec_y) {
           // Ho*Wo % 4 == 0: the four positions lie in one image
           const uint32_t img = fdiv(p, G.div_howo);
           const uint32_t q = p - img * howo;
-          store4<DTO>(ry, (img * G.Co + co) * howo + q, cok && p < G.P, y0, y1, y2, y3);
+          const uint32_t off = (img * G.Co + co) * howo + q;
+          const bool ok = cok && p < G.P;
+          if constexpr (HAS_R) {
+            float rv[4];
+            load4<DTO>(rr, off, ok, rv);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) z[e] += rv[e];
+          }
+          store4<DTO>(ry, off, ok, act_fn<ACT>(z[0], a.alpha), act_fn<ACT>(z[1], a.alpha),
+                      act_fn<ACT>(z[2], a.alpha), act_fn<ACT>(z[3], a.alpha));
         } else {
-          const float yv[4] = {y0, y1, y2, y3};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const uint32_t pe = p + e;
             const uint32_t img = fdiv(pe, G.div_howo);
             const uint32_t q = pe - img * howo;
-            store1<DTO>(ry, (img * G.Co + co) * howo + q, cok && pe < G.P, yv[e]);
+            const uint32_t off = (img * G.Co + co) * howo + q;
+            const bool ok = cok && pe < G.P;
+            float ze = z[e];
+            if constexpr (HAS_R) ze += load1<DTO>(rr, off, ok);
+            store1<DTO>(ry, off, ok, act_fn<ACT>(ze, a.alpha));
           }
         }
       }
     }
   });
+  });
 }
 
 // ---------------------------------------------------------------------------
-// Second kernel of the two-kernel path: out[i] = cast(act(ws[i])) over a
-// packed fp32 workspace that already holds A.B + bias (GEMM, [M,N]) or
-// conv + bias (conv, NCHW).  Each thread handles 16 consecutive elements per
+// Second kernel of the two-kernel path: out[i] = cast(act(ws[i] (+ res[i])))
+// over a packed fp32 workspace that already holds A.B + bias (GEMM, [M,N]) or
+// conv + bias (conv, NCHW); res, if given, is the residual in out's type.  Each thread handles 16 consecutive elements per
 // pass with four 16-byte loads issued before any is used (64 bytes in flight
 // per lane); grid-stride over the array with a grid that fills every CU.
 // ---------------------------------------------------------------------------
 template <int DTO>
 __global__ __launch_bounds__(256) void act_cast_kernel(const float* ws, void* out, uint32_t n,
-                                                       int act, float alpha) {
+                                                       int act, float alpha, const void* res) {
   constexpr uint32_t EPT = 16;
   const __amdgpu_buffer_rsrc_t ri = make_rsrc(ws, n * 4u);
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(out, n * (uint32_t)Elem<DTO>::bytes);
+  const __amdgpu_buffer_rsrc_t rr = make_rsrc(res, res ? n * (uint32_t)Elem<DTO>::bytes : 0u);
   const uint32_t stride = gridDim.x * blockDim.x * EPT;
-  auto run = [&](auto act_c) __attribute__((always_inline)) {
+  auto run = [&](auto act_c, auto res_c) __attribute__((always_inline)) {
     constexpr int ACT = decltype(act_c)::value;
+    constexpr bool HAS_R = decltype(res_c)::value;
     for (uint32_t base = (blockIdx.x * blockDim.x + threadIdx.x) * EPT; base < n; base += stride) {
       const bool full = base + EPT <= n;
       float z[EPT];
@@ -206,6 +239,21 @@ __global__ __launch_bounds__(256) void act_cast_kernel(const float* ws, void* ou
         for (uint32_t e = 0; e < EPT; ++e)
           z[e] = __uint_as_float(ld_b32(ri, base + e < n ? (base + e) * 4u : kOOB));
       }
+      if constexpr (HAS_R) {
+        // the residual joins the pre-activation (A.B + bias) before act
+        if (full) {
+#pragma unroll
+          for (uint32_t q = 0; q < EPT / 4; ++q) {
+            float rv[4];
+            load4<DTO>(rr, base + 4 * q, true, rv);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) z[4 * q + e] += rv[e];
+          }
+        } else {
+#pragma unroll
+          for (uint32_t e = 0; e < EPT; ++e) z[e] += load1<DTO>(rr, base + e, base + e < n);
+        }
+      }
       float y[EPT];
 #pragma unroll
       for (uint32_t e = 0; e < EPT; ++e) y[e] = act_fn<ACT>(z[e], alpha);
@@ -219,14 +267,10 @@ __global__ __launch_bounds__(256) void act_cast_kernel(const float* ws, void* ou
       }
     }
   };
-  switch (act) {                        // activation dispatched once per thread
-    case ACT_RELU: run(std::integral_constant<int, ACT_RELU>{}); break;
-    case ACT_LEAKY: run(std::integral_constant<int, ACT_LEAKY>{}); break;
-    case ACT_TANH: run(std::integral_constant<int, ACT_TANH>{}); break;
-    case ACT_GELU: run(std::integral_constant<int, ACT_GELU>{}); break;
-    case ACT_SIGMOID: run(std::integral_constant<int, ACT_SIGMOID>{}); break;
-    default: run(std::integral_constant<int, ACT_NONE>{}); break;
-  }
+  // activation and residual dispatched once per thread
+  with_act(act, [&](auto act_c) __attribute__((always_inline)) {
+    with_residual(res != nullptr, [&](auto res_c) __attribute__((always_inline)) { run(act_c, res_c); });
+  });
 }
 
 // ---------------------------------------------------------------------------

@@ -15,6 +15,7 @@ struct ConvArgs {
   const void* w;
   const void* bias;
   void* y;
+  const void* r;            // residual [N, Co, Ho, Wo] in y's type (y_bytes), or null
   ConvGeom geom;
   uint32_t x_bytes, w_bytes, bias_bytes, y_bytes;
   int bias_dt;
@@ -30,6 +31,7 @@ struct HaloArgs {
   const void* w;
   const void* bias;
   void* y;
+  const void* r;            // residual, as in ConvArgs
   ConvGeom geom;
   uint32_t x_bytes, w_bytes, bias_bytes, y_bytes;
   int bias_dt;
@@ -58,6 +60,6 @@ int launch_conv_f16(int dto, int tile, const ConvArgs& a, hipStream_t s);
 int launch_conv_bf16(int dto, int tile, const ConvArgs& a, hipStream_t s);
 int launch_conv_halo(int dti, int dto, int taps, int bm, int ks, int sn, const HaloArgs& a, hipStream_t s);
 int launch_act_cast(int dto, const float* ws, void* out, uint32_t n, int act, float alpha,
-                    hipStream_t s);
+                    const void* res, hipStream_t s);
 
 }  // namespace biasact

@@ -218,7 +218,7 @@ int select_conv_tile(int64_t N, int64_t Co, int64_t Ho, int64_t Wo, int64_t /*K*
 }
 
 int plan_gemm(const void* A, const void* B, const void* bias, const void* C, int64_t M, int64_t N,
-              int64_t K, uint32_t dtypes, int act, GemmPlan* p) {
+              int64_t K, uint32_t dtypes, int act, GemmPlan* p, const void* R) {
   if (!p) return kErrInvalid;
   if (M < 0 || N < 0 || K < 0) return kErrInvalid;
   if (act < 0 || act > 5) return kErrInvalid;
@@ -244,7 +244,8 @@ int plan_gemm(const void* A, const void* B, const void* bias, const void* C, int
   const int epc = chunk_elems(dti);
   p->vec_a = K % epc == 0 && aligned(A, 16);
   p->vec_b = N % epc == 0 && aligned(B, 16);
-  p->vec_c = N % 4 == 0 && aligned(C, 4 * (uintptr_t)elem_bytes(dto));
+  p->vec_c = N % 4 == 0 && aligned(C, 4 * (uintptr_t)elem_bytes(dto)) &&
+             (!R || aligned(R, 4 * (uintptr_t)elem_bytes(dto)));
   p->empty = M == 0 || N == 0;
   int tile = forced_tile();
   if (tile < 0 || tile >= kNumTileConfigs) tile = select_gemm_tile(M, N, K, dti);
@@ -262,7 +263,7 @@ int plan_gemm(const void* A, const void* B, const void* bias, const void* C, int
 int plan_conv(const void* x, const void* w, const void* bias, const void* y, int64_t N, int64_t C,
               int64_t H, int64_t W, int64_t Co, int64_t kh, int64_t kw, const int32_t* strides,
               const int32_t* pads, const int32_t* dilations, uint32_t dtypes, int act,
-              ConvPlan* p) {
+              ConvPlan* p, const void* r) {
   if (!p || !strides || !pads || !dilations) return kErrInvalid;
   if (N < 0 || C <= 0 || H <= 0 || W <= 0 || Co <= 0 || kh <= 0 || kw <= 0) return kErrInvalid;
   if (act < 0 || act > 5) return kErrInvalid;
@@ -302,7 +303,8 @@ int plan_conv(const void* x, const void* w, const void* bias, const void* y, int
   p->bias_bytes = (uint32_t)bias_bytes;
   p->y_bytes = (uint32_t)y_bytes;
   p->vec_w = K % chunk_elems(dti) == 0 && aligned(w, 16);
-  p->vec_y = (Ho * Wo) % 4 == 0 && aligned(y, 4 * (uintptr_t)elem_bytes(dto));
+  p->vec_y = (Ho * Wo) % 4 == 0 && aligned(y, 4 * (uintptr_t)elem_bytes(dto)) &&
+             (!r || aligned(r, 4 * (uintptr_t)elem_bytes(dto)));
   p->empty = N == 0;
   int tile = forced_tile();
   const bool auto_tile = tile < 0 || tile >= kNumTileConfigs;

@@ -50,12 +50,13 @@ struct ConvPlan {
   uint32_t h_hrcp, h_kpad, h_kstr;   // fp32 halo kernel (see plan_halo32)
 };
 
+// R (residual, output's type and shape) only enters the alignment decisions.
 int plan_gemm(const void* A, const void* B, const void* bias, const void* C, int64_t M, int64_t N,
-              int64_t K, uint32_t dtypes, int act, GemmPlan* p);
+              int64_t K, uint32_t dtypes, int act, GemmPlan* p, const void* R = nullptr);
 int plan_conv(const void* x, const void* w, const void* bias, const void* y, int64_t N, int64_t C,
               int64_t H, int64_t W, int64_t Co, int64_t kh, int64_t kw, const int32_t* strides,
               const int32_t* pads, const int32_t* dilations, uint32_t dtypes, int act,
-              ConvPlan* p);
+              ConvPlan* p, const void* r = nullptr);
 
 int select_gemm_tile(int64_t M, int64_t N, int64_t K, int dti);
 int select_conv_tile(int64_t N, int64_t Co, int64_t Ho, int64_t Wo, int64_t K, int dti);

@@ -125,6 +125,35 @@ int conv2d_bias_act_2k(const void* x, const void* w, const void* bias, void* y,
                        uint32_t dtypes, int act, void* workspace, size_t workspace_bytes,
                        hipStream_t stream);
 
+/* Residual epilogue: the same contraction with an extra input R of the
+ * output's type and shape (C's [M,N] row-major, or y's [N,Co,Ho,Wo]) joining
+ * the sum before the activation:
+ *     C = act(A . B + bias + R)        y = act(conv2d(x, w) + bias + R)
+ * the "matmul + add + bias" fusion of residual networks in the ops-nn article
+ * (mlqm.cn/news/1824), section ops-nn的融合算子分类与适用场景 (math class).
+ * R is a device pointer owned by the caller, read once per output element;
+ * it may be the output buffer itself (in place: each element is read before
+ * it is written, by the same thread), but must not overlap it otherwise.
+ * R == NULL with a non-empty output returns BA_ERR_INVALID.  The other
+ * arguments, limits and return codes are those of the entry points above;
+ * the _2k variants add R in their second kernel and match the fused results
+ * bit for bit. */
+int gemm_bias_add_act(const void* A, const void* B, const void* bias, const void* R, void* C,
+                      int64_t M, int64_t N, int64_t K, uint32_t dtypes, int act, float alpha,
+                      hipStream_t stream);
+int gemm_bias_add_act_2k(const void* A, const void* B, const void* bias, const void* R, void* C,
+                         int64_t M, int64_t N, int64_t K, uint32_t dtypes, int act, float alpha,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+int conv2d_bias_add_act(const void* x, const void* w, const void* bias, const void* R, void* y,
+                        int64_t N, int64_t C, int64_t H, int64_t W, int64_t Co, int64_t kh,
+                        int64_t kw, const int32_t strides[2], const int32_t pads[4],
+                        const int32_t dilations[2], uint32_t dtypes, int act, hipStream_t stream);
+int conv2d_bias_add_act_2k(const void* x, const void* w, const void* bias, const void* R, void* y,
+                           int64_t N, int64_t C, int64_t H, int64_t W, int64_t Co, int64_t kh,
+                           int64_t kw, const int32_t strides[2], const int32_t pads[4],
+                           const int32_t dilations[2], uint32_t dtypes, int act, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
 /* Introspection and tuning. */
 const char* biasact_status_string(int status);  /* static string, never NULL */
 /* The hipError_t behind the most recent BA_ERR_HIP returned on the calling

@@ -32,7 +32,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for must in ("gemm_bias_act", "conv2d_bias_act", "gemm_bias_act_2k", "conv2d_bias_act_2k",
                  "gemm_bias_act_workspace_size", "conv2d_bias_act_workspace_size",
-                 "biasact_status_string", "biasact_force_tile_config"):
+                 "biasact_status_string", "biasact_force_tile_config", "gemm_bias_add_act",
+                 "conv2d_bias_add_act", "gemm_bias_add_act_2k", "conv2d_bias_add_act_2k"):
         assert must in names
 
 
@@ -140,6 +141,23 @@ def test_gemm_rejects(kw, code):
 
 def test_gemm_empty_problem_is_ok_without_launch():
     assert gemm(M=0) == 0 and gemm(N=0) == 0
+
+
+def test_residual_entry_points_validate():
+    dt = _dt(BF16, BF16, F32, BF16)
+    # a null residual with a non-empty output is invalid; empty outputs launch nothing
+    assert L.gemm_bias_add_act(P, P, P, NUL, P, 4, 4, 4, dt, 1, 0.0, NUL) == 1
+    assert L.gemm_bias_add_act(P, P, P, NUL, P, 0, 4, 4, dt, 1, 0.0, NUL) == 0
+    assert L.gemm_bias_add_act_2k(P, P, P, NUL, P, 4, 4, 4, dt, 1, 0.0, P, 64, NUL) == 1
+    # the other checks are those of the plain entry point
+    assert L.gemm_bias_add_act(P, P, P, P, P, 4, 4, 4, dt, 6, 0.0, NUL) == 1
+    assert L.gemm_bias_add_act(P, P, P, P, P, 4, 4, 4, _dt(F16, BF16, F32, F32), 1, 0.0, NUL) == 2
+    c = (ctypes.c_int32 * 2)(1, 1), (ctypes.c_int32 * 4)(1, 1, 1, 1), (ctypes.c_int32 * 2)(1, 1)
+    cdt = _dt(F16, F16, F16, F16)
+    assert L.conv2d_bias_add_act(P, P, P, NUL, P, 1, 3, 8, 8, 4, 3, 3, *c, cdt, 3, NUL) == 1
+    assert L.conv2d_bias_add_act(P, P, P, P, P, 1, 3, 8, 8, 4, 3, 3, *c, cdt, 2, NUL) == 2
+    assert L.conv2d_bias_add_act_2k(P, P, P, NUL, P, 1, 3, 8, 8, 4, 3, 3, *c, cdt, 3, P, 4096,
+                                    NUL) == 1
 
 
 def test_gemm_2k_workspace_checks():
