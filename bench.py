@@ -117,10 +117,17 @@ def make_step(case, seed=0, path="fused"):
         bias = None if inp["bias"] is None else to_device(inp["bias"], case.bias_dtype)
         C = torch.empty((case.M, case.N), dtype=tdt[case.out_dtype], device="cuda")
         alpha = float(np.float32(case.alpha))
+        R = None if inp.get("R") is None else to_device(inp["R"].reshape(case.M, case.N),
+                                                        case.out_dtype)
         if path == "fused":
+            if R is not None:
+                return (lambda: ba.gemm_bias_add_act(A, B, bias, R, C, case.act, alpha)), 1
             return (lambda: ba.gemm_bias_act(A, B, bias, C, case.act, alpha)), 1
         ws = torch.empty(ba.gemm_bias_act_workspace_size(case.M, case.N) // 4, dtype=torch.float32,
                          device="cuda")
+        if R is not None:
+            return (lambda: ba.gemm_bias_add_act_2k(A, B, bias, R, C, case.act, alpha,
+                                                    workspace=ws)), 2
         return (lambda: ba.gemm_bias_act_2k(A, B, bias, C, case.act, alpha, workspace=ws)), 2
     inp = wl.gen_conv(case, seed)
     x = to_device(inp["x"].reshape(case.N, case.C, case.H, case.W), case.in_dtype)
@@ -129,11 +136,17 @@ def make_step(case, seed=0, path="fused"):
     Ho, Wo = case.out_hw()
     y = torch.empty((case.N, case.Co, Ho, Wo), dtype=tdt[case.out_dtype], device="cuda")
     args = (case.strides, case.pads, case.dilations, case.act)
+    R = None if inp.get("R") is None else to_device(inp["R"].reshape(case.N, case.Co, Ho, Wo),
+                                                    case.out_dtype)
     if path == "fused":
+        if R is not None:
+            return (lambda: ba.conv2d_bias_add_act(x, w, bias, R, y, *args)), 1
         return (lambda: ba.conv2d_bias_act(x, w, bias, y, *args)), 1
     n = ba.conv2d_bias_act_workspace_size(case.N, case.C, case.H, case.W, case.Co, case.kh, case.kw,
                                           case.strides, case.pads, case.dilations)
     ws = torch.empty(n // 4, dtype=torch.float32, device="cuda")
+    if R is not None:
+        return (lambda: ba.conv2d_bias_add_act_2k(x, w, bias, R, y, *args, workspace=ws)), 2
     return (lambda: ba.conv2d_bias_act_2k(x, w, bias, y, *args, workspace=ws)), 2
 
 

@@ -114,17 +114,29 @@ def gemm_reference(case: wl.GemmCase, inp, idx=None):
     floor = None
     need = _needs_floor(case.in_dtype, case.out_dtype, case.K)
     absb = None if bias is None else np.abs(bias)
+    R = None if inp.get("R") is None else o.decode(inp["R"].ravel(), case.out_dtype)
+    terms = case.K + (R is not None)
     if idx is None:
-        ref = o.gemm(A, B, bias, case.act, alpha).ravel()
+        if R is None:
+            ref = o.gemm(A, B, bias, case.act, alpha).ravel()
+        else:
+            ref = o.gemm_residual(A, B, bias, R.reshape(case.M, case.N), case.act, alpha).ravel()
         if need:
             s = o.gemm(np.abs(A), np.abs(B), absb, "none").ravel()
-            floor = _floor(case.in_dtype, case.out_dtype, case.K, s)
+            if R is not None:
+                s = s + np.abs(R)
+            floor = _floor(case.in_dtype, case.out_dtype, terms, s)
     else:
         ii, jj = idx // case.N, idx % case.N
-        ref = o.gemm_elems(A, B, bias, ii, jj, case.act, alpha)
+        if R is None:
+            ref = o.gemm_elems(A, B, bias, ii, jj, case.act, alpha)
+        else:
+            ref = o.gemm_residual_elems(A, B, bias, R[idx], ii, jj, case.act, alpha)
         if need:
             s = o.gemm_elems(np.abs(A), np.abs(B), absb, ii, jj, "none")
-            floor = _floor(case.in_dtype, case.out_dtype, case.K, s)
+            if R is not None:
+                s = s + np.abs(R[idx])
+            floor = _floor(case.in_dtype, case.out_dtype, terms, s)
     return ref, floor
 
 
@@ -138,16 +150,27 @@ def conv_reference(case: wl.ConvCase, inp, idx=None):
     floor = None
     absb = None if bias is None else np.abs(bias)
     need = _needs_floor(case.in_dtype, case.out_dtype, K)
+    R = None if inp.get("R") is None else o.decode(inp["R"].ravel(), case.out_dtype)
+    terms = K + (R is not None)
     if idx is None:
-        ref = o.conv2d(x, w, bias, *args, case.act, orc.f32(case.alpha)).ravel()
+        if R is None:
+            ref = o.conv2d(x, w, bias, *args, case.act, orc.f32(case.alpha)).ravel()
+        else:
+            z = o.conv2d(x, w, bias, *args, "none").ravel()
+            ref = o.residual_act(z, R, case.act, orc.f32(case.alpha))
         if need:
-            floor = _floor(case.in_dtype, case.out_dtype, K,
-                           o.conv2d(np.abs(x), np.abs(w), absb, *args, "none").ravel())
+            s = o.conv2d(np.abs(x), np.abs(w), absb, *args, "none").ravel()
+            floor = _floor(case.in_dtype, case.out_dtype, terms, s if R is None else s + np.abs(R))
     else:
-        ref = o.conv2d_elems(x, w, bias, *args, idx, case.act, orc.f32(case.alpha))
+        if R is None:
+            ref = o.conv2d_elems(x, w, bias, *args, idx, case.act, orc.f32(case.alpha))
+        else:
+            ref = o.conv2d_residual_elems(x, w, bias, R[idx], *args, idx, case.act,
+                                          orc.f32(case.alpha))
         if need:
-            floor = _floor(case.in_dtype, case.out_dtype, K,
-                           o.conv2d_elems(np.abs(x), np.abs(w), absb, *args, idx, "none"))
+            s = o.conv2d_elems(np.abs(x), np.abs(w), absb, *args, idx, "none")
+            floor = _floor(case.in_dtype, case.out_dtype, terms,
+                           s if R is None else s + np.abs(R[idx]))
     return ref, floor
 
 
@@ -164,12 +187,19 @@ def run_gemm(case: wl.GemmCase, inp, path: str = "fused", out=None):
     C = out if out is not None else torch.empty((case.M, case.N), dtype=torch_dtype(case.out_dtype),
                                                device="cuda")
     alpha = float(np.float32(case.alpha))
+    R = None if inp.get("R") is None else to_dev(inp["R"].reshape(case.M, case.N), case.out_dtype)[0]
     if path == "fused":
-        ba.gemm_bias_act(A, B, bias, C, case.act, alpha)
+        if R is None:
+            ba.gemm_bias_act(A, B, bias, C, case.act, alpha)
+        else:
+            ba.gemm_bias_add_act(A, B, bias, R, C, case.act, alpha)
     else:
         ws = torch.empty(max(1, ba.gemm_bias_act_workspace_size(case.M, case.N) // 4),
                          dtype=torch.float32, device="cuda")
-        ba.gemm_bias_act_2k(A, B, bias, C, case.act, alpha, workspace=ws)
+        if R is None:
+            ba.gemm_bias_act_2k(A, B, bias, C, case.act, alpha, workspace=ws)
+        else:
+            ba.gemm_bias_add_act_2k(A, B, bias, R, C, case.act, alpha, workspace=ws)
     torch.cuda.synchronize()
     return C
 
@@ -183,14 +213,22 @@ def run_conv(case: wl.ConvCase, inp, path: str = "fused", out=None):
     Ho, Wo = case.out_hw()
     y = out if out is not None else torch.empty((case.N, case.Co, Ho, Wo),
                                                dtype=torch_dtype(case.out_dtype), device="cuda")
+    R = None if inp.get("R") is None else to_dev(inp["R"].reshape(case.N, case.Co, Ho, Wo),
+                                                 case.out_dtype)[0]
+    args = (case.strides, case.pads, case.dilations, case.act)
     if path == "fused":
-        ba.conv2d_bias_act(x, w, bias, y, case.strides, case.pads, case.dilations, case.act)
+        if R is None:
+            ba.conv2d_bias_act(x, w, bias, y, *args)
+        else:
+            ba.conv2d_bias_add_act(x, w, bias, R, y, *args)
     else:
         n = ba.conv2d_bias_act_workspace_size(case.N, case.C, case.H, case.W, case.Co, case.kh,
                                               case.kw, case.strides, case.pads, case.dilations)
         ws = torch.empty(max(1, n // 4), dtype=torch.float32, device="cuda")
-        ba.conv2d_bias_act_2k(x, w, bias, y, case.strides, case.pads, case.dilations, case.act,
-                              workspace=ws)
+        if R is None:
+            ba.conv2d_bias_act_2k(x, w, bias, y, *args, workspace=ws)
+        else:
+            ba.conv2d_bias_add_act_2k(x, w, bias, R, y, *args, workspace=ws)
     torch.cuda.synchronize()
     return y
 

@@ -90,6 +90,7 @@ class GemmCase:
     dist_a: Tuple = ("uniform", -1.0, 1.0)
     dist_b: Tuple = ("uniform", -1.0, 1.0)
     dist_bias: Tuple = ("uniform", -1.0, 1.0)
+    dist_r: Optional[Tuple] = None  # residual R [M, N] in out_dtype; None = no residual
 
     @property
     def flops(self) -> int:
@@ -101,6 +102,8 @@ class GemmCase:
         b = (self.M * self.K + self.K * self.N) * s[self.in_dtype] + self.M * self.N * s[self.out_dtype]
         if self.bias_dtype:
             b += self.N * s[self.bias_dtype]
+        if self.dist_r:
+            b += self.M * self.N * s[self.out_dtype]
         return b
 
 
@@ -125,6 +128,7 @@ class ConvCase:
     dist_x: Tuple = ("uniform", -1.0, 1.0)
     dist_w: Tuple = ("uniform", -1.0, 1.0)
     dist_bias: Tuple = ("uniform", -1.0, 1.0)
+    dist_r: Optional[Tuple] = None  # residual R [N, Co, Ho, Wo] in out_dtype; None = no residual
 
     def out_hw(self) -> Tuple[int, int]:
         def od(i, k, s, p0, p1, d):
@@ -150,6 +154,8 @@ class ConvCase:
         b += self.N * self.Co * Ho * Wo * s[self.out_dtype]
         if self.bias_dtype:
             b += self.Co * s[self.bias_dtype]
+        if self.dist_r:
+            b += self.N * self.Co * Ho * Wo * s[self.out_dtype]
         return b
 
 
@@ -208,6 +214,15 @@ CASES: Dict[str, object] = {
     "conv3x3_sigmoid_8x64x56_f16": ConvCase(
         "conv3x3_sigmoid_8x64x56_f16", 8, 64, 56, 56, 64, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1),
         "f16", "f16", "f16", "sigmoid", 0.0, U01, U01, U01),
+    # The residual ("matmul + add + bias", ops-nn article, math class): the
+    # 4096^3 GEMM with a bf16 residual, and the fp16 3x3 conv with an identity
+    # skip (R of y's shape), the shape of a residual block.
+    "gemm_relu_residual_4096_bf16": GemmCase(
+        "gemm_relu_residual_4096_bf16", 4096, 4096, 4096, "bf16", "f32", "bf16", "relu", 0.0,
+        ("normal", 1.0 / 64.0), ("normal", 1.0 / 64.0), U01, U01),
+    "conv3x3_residual_tanh_8x64x56_f16": ConvCase(
+        "conv3x3_residual_tanh_8x64x56_f16", 8, 64, 56, 56, 64, 3, 3, (1, 1), (1, 1, 1, 1),
+        (1, 1), "f16", "f16", "f16", "tanh", 0.0, U01, U01, U01, U01),
 }
 
 # Which case each named workload group covers (group 1 is the small spec case,
@@ -219,11 +234,13 @@ GROUPS = {
     4: ["conv7x7s2_tanh_16x3x224_f32", "conv1x1s2_tanh_16x256x56_f32"],
     5: ["gemm_leaky_32768x4096x1024_bf16", "conv3x3d2_tanh_32x128x28_bf16"],
     6: ["gemm_gelu_4096_bf16", "conv3x3_sigmoid_8x64x56_f16"],      # epilogue extensions
+    7: ["gemm_relu_residual_4096_bf16", "conv3x3_residual_tanh_8x64x56_f16"],
 }
 
 
 def gen_gemm(case: GemmCase, seed: int):
-    """Returns dict(A, B, bias) of encoded words; bias is None without bias."""
+    """Returns dict(A, B, bias[, R]) of encoded words; bias is None without
+    bias; R (drawn last) only for residual cases."""
     rng = np.random.default_rng(seed)
     a = draw(rng, (case.M, case.K), case.dist_a)
     b = draw(rng, (case.K, case.N), case.dist_b)
@@ -231,11 +248,13 @@ def gen_gemm(case: GemmCase, seed: int):
     if case.bias_dtype:
         bias = draw(rng, (case.N,), case.dist_bias)
         out["bias"] = encode(bias, case.bias_dtype)
+    if case.dist_r:
+        out["R"] = encode(draw(rng, (case.M, case.N), case.dist_r), case.out_dtype)
     return out
 
 
 def gen_conv(case: ConvCase, seed: int):
-    """Returns dict(x, w, bias) of encoded words; bias is None without bias."""
+    """Returns dict(x, w, bias[, R]) of encoded words, as gen_gemm."""
     rng = np.random.default_rng(seed)
     x = draw(rng, (case.N, case.C, case.H, case.W), case.dist_x)
     w = draw(rng, (case.Co, case.C, case.kh, case.kw), case.dist_w)
@@ -243,6 +262,9 @@ def gen_conv(case: ConvCase, seed: int):
     if case.bias_dtype:
         bias = draw(rng, (case.Co,), case.dist_bias)
         out["bias"] = encode(bias, case.bias_dtype)
+    if case.dist_r:
+        Ho, Wo = case.out_hw()
+        out["R"] = encode(draw(rng, (case.N, case.Co, Ho, Wo), case.dist_r), case.out_dtype)
     return out
 
 
