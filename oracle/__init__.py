@@ -21,7 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
+DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3, "i32": 4}
 ACT_CODES = {"none": 0, "relu": 1, "leaky_relu": 2, "tanh": 3, "gelu": 4, "sigmoid": 5}
 
 GCC_FLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared",
@@ -113,7 +113,7 @@ class Oracle:
     # -- decoding ----------------------------------------------------------
     def decode(self, words: np.ndarray, dtype: str) -> np.ndarray:
         words = np.ascontiguousarray(words)
-        want = np.uint32 if dtype == "f32" else np.uint16
+        want = {"f32": np.uint32, "i32": np.uint32, "i8": np.uint8}.get(dtype, np.uint16)
         if words.dtype != want:
             raise ValueError(f"{dtype} words must be {np.dtype(want).name}")
         out = np.empty(words.shape, dtype=np.float64)

@@ -15,6 +15,9 @@ The rule:
     result is round(z) with |z - ref| <= E, so |y - ref| <= ulp/2 + E; without
     E an output whose exact value is tiny next to sum |a_k b_k| would demand
     an fp32 sum far more accurate than fp32 itself.
+  * int32 output (int8 operands, int32 bias; every sum exact): bit-exact;
+  * fp32 output, int8 operands: the fp32-input rule (the integer sum is
+    exact; only its conversion to fp32 and the activation round);
   * fp32 output with an error bound E given (used only for shapes outside
     the named workloads, e.g. fp32 inputs with K > 512, where fp32 summation
     error alone exceeds 1e-5 * (1 + |ref|)): max(rule, E).
@@ -51,8 +54,10 @@ def tolerance(ref: np.ndarray, in_dtype: str, out_dtype: str,
               err_floor: Optional[np.ndarray] = None) -> np.ndarray:
     ref = np.asarray(ref, dtype=np.float64)
     e = 0.0 if err_floor is None else np.asarray(err_floor, dtype=np.float64)
+    if out_dtype == "i32":
+        return np.zeros_like(ref)
     if out_dtype == "f32":
-        rel = 1e-5 if in_dtype == "f32" else 1e-3
+        rel = 1e-5 if in_dtype in ("f32", "i8") else 1e-3
         return np.maximum(rel * (1.0 + np.abs(ref)), e)
     return ulp(np.abs(ref), out_dtype) + e
 
@@ -67,6 +72,8 @@ def decode_out(words: np.ndarray, out_dtype: str) -> np.ndarray:
         return w.view(np.float16).astype(np.float64)
     if out_dtype == "bf16":
         return (w.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if out_dtype == "i32":
+        return w.view(np.int32).astype(np.float64)
     raise ValueError(out_dtype)
 
 

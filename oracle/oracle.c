@@ -87,6 +87,15 @@ int orc_decode(int dtype, const void *src, int64_t n, double *dst)
     } else if (dtype == ORC_F32) {
         const uint32_t *s = (const uint32_t *)src;
         for (int64_t i = 0; i < n; ++i) dst[i] = orc_f32_to_f64(s[i]);
+    } else if (dtype == ORC_I8) {
+        /* two's complement: bit 7 weighs -128 */
+        const uint8_t *s = (const uint8_t *)src;
+        for (int64_t i = 0; i < n; ++i) dst[i] = (double)(s[i] & 0x7f) - ((s[i] & 0x80) ? 128.0 : 0.0);
+    } else if (dtype == ORC_I32) {
+        /* two's complement: bit 31 weighs -2^31 */
+        const uint32_t *s = (const uint32_t *)src;
+        for (int64_t i = 0; i < n; ++i)
+            dst[i] = (double)(s[i] & 0x7fffffffu) - ((s[i] & 0x80000000u) ? 2147483648.0 : 0.0);
     } else {
         return -1;
     }

@@ -27,14 +27,16 @@ extern "C" {
 #endif
 
 /* Element-type codes of the encoded inputs. */
-enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2 };
+enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2, ORC_I8 = 3, ORC_I32 = 4 };
 
 /* Activation codes. */
 enum { ORC_ACT_NONE = 0, ORC_ACT_RELU = 1, ORC_ACT_LEAKY = 2, ORC_ACT_TANH = 3,
        ORC_ACT_GELU = 4, ORC_ACT_SIGMOID = 5 };
 
 /* Exact decoders, written from the IEEE-754 binary16 / binary32 layouts and
- * from bfloat16 = the upper half of a binary32.  n elements, src packed. */
+ * from bfloat16 = the upper half of a binary32; int8 and int32 are two's
+ * complement integers (int8 operands with an int32 bias: "CANN pyasc
+ * MatmulLeakyRelu 融合算子实战", section 补充说明).  n elements, src packed. */
 double orc_f16_to_f64(uint16_t h);
 double orc_bf16_to_f64(uint16_t h);
 double orc_f32_to_f64(uint32_t u);

@@ -21,6 +21,9 @@ MUTANTS = [
     ("f16 subnormal scale", "ldexp((double)m, -24)", "ldexp((double)m, -25)"),
     ("bf16 exponent bias", "ldexp((double)(128 + m), e - 134)", "ldexp((double)(128 + m), e - 133)"),
     ("f32 implicit bit dropped", "ldexp((double)(8388608u + m), e - 150)", "ldexp((double)(m), e - 150)"),
+    ("int8 sign bit weight", "((s[i] & 0x80) ? 128.0 : 0.0)", "((s[i] & 0x80) ? 127.0 : 0.0)"),
+    ("int32 read as unsigned", "((s[i] & 0x80000000u) ? 2147483648.0 : 0.0)",
+     "((s[i] & 0x80000000u) ? -2147483648.0 : 0.0)"),
     ("leaky slope dropped", "return z >= 0.0 ? z : alpha * z;", "return z >= 0.0 ? z : z;"),
     ("leaky branches swapped", "return z >= 0.0 ? z : alpha * z;", "return z >= 0.0 ? alpha * z : z;"),
     ("relu keeps negatives", "return z > 0.0 ? z : 0.0;", "return z > 0.0 ? z : -z;"),

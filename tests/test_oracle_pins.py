@@ -197,6 +197,35 @@ def test_gelu_identities_and_limits():
         assert dens / abs(z) * (1 - 1 / z ** 2) < got < dens / abs(z), (z, got)
 
 
+def test_int8_and_int32_decoders():
+    # all 256 int8 patterns and random int32 patterns against numpy's views
+    w8 = np.arange(256, dtype=np.uint8)
+    assert np.array_equal(O.decode(w8, "i8"), w8.view(np.int8).astype(np.float64))
+    w32 = np.random.default_rng(5).integers(0, 2 ** 32, 100000, dtype=np.uint64).astype(np.uint32)
+    w32 = np.concatenate([w32, np.array([0, 1, 0x7FFFFFFF, 0x80000000, 0xFFFFFFFF], np.uint32)])
+    assert np.array_equal(O.decode(w32, "i32"), w32.view(np.int32).astype(np.float64))
+    assert O.decode(np.array([0x80], np.uint8), "i8")[0] == -128.0
+    assert O.decode(np.array([0x80000000], np.uint32), "i32")[0] == -2.0 ** 31
+
+
+def test_int8_gemm_exact_with_int32_bias():
+    # int8 A, B and an int32 bias ([MLR] 补充说明): the sums are integers far
+    # below 2^53, so the double result is the exact integer (Python ints)
+    rng = np.random.default_rng(8)
+    M, N, K = 9, 11, 300
+    A = rng.integers(-128, 128, (M, K))
+    B = rng.integers(-128, 128, (K, N))
+    bias = rng.integers(-2 ** 30, 2 ** 30, N)
+    got = O.gemm(O.decode(workloads.encode(A.astype(np.float32), "i8").reshape(M, K), "i8"),
+                 O.decode(workloads.encode(B.astype(np.float32), "i8").reshape(K, N), "i8"),
+                 O.decode(bias.astype(np.int32).view(np.uint32), "i32"), "none")
+    want = [[sum(int(A[i, k]) * int(B[k, j]) for k in range(K)) + int(bias[j]) for j in range(N)]
+            for i in range(M)]
+    assert got.tolist() == [[float(v) for v in r] for r in want]
+    # the extreme product -128 * -128 summed 131071 times still fits int32
+    assert 131071 * 16384 < 2 ** 31
+
+
 # --------------------------------------------------------------------------
 # GEMM
 # --------------------------------------------------------------------------

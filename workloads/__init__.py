@@ -27,7 +27,7 @@ from typing import Dict, Optional, Tuple
 import numpy as np
 
 DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
-DTYPE_SIZES = {"f32": 4, "f16": 2, "bf16": 2}
+DTYPE_SIZES = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1, "i32": 4}
 ACT_CODES = {"none": 0, "relu": 1, "leaky_relu": 2, "tanh": 3, "gelu": 4, "sigmoid": 5}
 
 
@@ -43,7 +43,8 @@ def _f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
 
 
 def encode(a: np.ndarray, dtype: str) -> np.ndarray:
-    """fp32 array -> packed words of `dtype` (uint16 for 16-bit, uint32 for f32)."""
+    """fp32 array -> packed words of `dtype` (uint16 for 16-bit, uint32 for f32
+    and int32, uint8 for int8; integer types take integer values)."""
     a = np.ascontiguousarray(a, dtype=np.float32)
     if not np.all(np.isfinite(a)):
         raise ValueError("synthetic inputs must be finite")
@@ -53,7 +54,12 @@ def encode(a: np.ndarray, dtype: str) -> np.ndarray:
         return a.astype(np.float16).view(np.uint16).copy()
     if dtype == "bf16":
         return _f32_to_bf16_bits(a)
-    raise ValueError(f"unknown dtype {dtype!r}; supported: f32, f16, bf16")
+    if dtype in ("i8", "i32"):
+        lo, hi, t = (-128, 127, np.int8) if dtype == "i8" else (-2 ** 31, 2 ** 31 - 1, np.int32)
+        if not np.all((a == np.round(a)) & (a >= lo) & (a <= hi)):
+            raise ValueError(f"{dtype} inputs must be integers in [{lo}, {hi}]")
+        return a.astype(np.float64).astype(t).view(np.uint8 if dtype == "i8" else np.uint32).copy()
+    raise ValueError(f"unknown dtype {dtype!r}; supported: f32, f16, bf16, i8, i32")
 
 
 # ---------------------------------------------------------------------------
