@@ -31,7 +31,8 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}   # dense MFMA, MI355X datasheet
+# dense MFMA, MI355X datasheet (int8: TOP/s)
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3, "i8": 5033.2}
 PEAK_HBM_GBS = 8000.0
 
 # Sources that define the headline kernel; the HBM-traffic record in profiles/
@@ -100,6 +101,8 @@ def to_device(words, dt):
     import torch
     if dt == "f32":
         return torch.from_numpy(np.ascontiguousarray(words).view(np.float32)).cuda()
+    if dt in ("i8", "i32"):
+        return torch.from_numpy(np.ascontiguousarray(words).view(np.int8 if dt == "i8" else np.int32)).cuda()
     t = torch.from_numpy(np.ascontiguousarray(words).view(np.int16))
     return t.view({"f16": torch.float16, "bf16": torch.bfloat16}[dt]).cuda()
 
@@ -109,7 +112,7 @@ def make_step(case, seed=0, path="fused"):
     import torch
     import conv_bias_activation_amd as ba
     import workloads as wl
-    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "i32": torch.int32}
     if isinstance(case, wl.GemmCase):
         inp = wl.gen_gemm(case, seed)
         A = to_device(inp["A"].reshape(case.M, case.K), case.in_dtype)
@@ -352,6 +355,9 @@ def main():
         for name, c in wl.CASES.items():
             entry = {}
             for path in ("fused", "2k"):
+                if path == "2k" and c.in_dtype == "i8":
+                    entry[path] = {"skipped": "int8 GEMMs run the fused path only"}
+                    continue
                 try:
                     entry[path] = measure_case(c, path)
                 except Exception as e:  # report, never hide

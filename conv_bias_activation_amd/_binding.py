@@ -9,7 +9,7 @@ from typing import Optional, Sequence
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libbiasact.so")
 
-DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
+DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3, "i32": 4}
 ACT_CODES = {"none": 0, "relu": 1, "leaky_relu": 2, "tanh": 3, "gelu": 4, "sigmoid": 5}
 BA_OK, BA_ERR_INVALID, BA_ERR_UNSUPPORTED, BA_ERR_HIP = 0, 1, 2, 3
 
@@ -126,9 +126,11 @@ def _torch():
 
 def _tname(t) -> str:
     torch = _torch()
-    m = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
+    m = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16", torch.int8: "i8",
+         torch.int32: "i32"}
     if t.dtype not in m:
-        raise ValueError(f"unsupported tensor dtype {t.dtype}; supported: float32, float16, bfloat16")
+        raise ValueError(f"unsupported tensor dtype {t.dtype}; supported: float32, float16, "
+                         "bfloat16, int8 and int32 (int8 GEMMs)")
     return m[t.dtype]
 
 

@@ -29,7 +29,8 @@ ARCH = "gfx950"
 
 _TYPES = ("f32", "f16", "bf16")
 HIP_SOURCES = ["api.hip", "act_cast.hip", "dispatch.hip"] + [
-    f"{op}_{ti}_{to}.hip" for op in ("gemm", "conv") for ti in _TYPES for to in _TYPES]
+    f"{op}_{ti}_{to}.hip" for op in ("gemm", "conv") for ti in _TYPES for to in _TYPES] + [
+    f"gemm_i8_{to}.hip" for to in ("f32", "f16", "bf16", "i32")]
 CPP_SOURCES = ["plan.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC, "-Wall",

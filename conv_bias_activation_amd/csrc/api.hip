@@ -32,9 +32,10 @@ int launch_status() {
   return kErrHip;
 }
 
-bool aligned_for(const void* p, int dt) {
-  return ((uintptr_t)p % (dt == DT_F32 ? 16u : 8u)) == 0;
-}
+int out_bytes(int dt) { return (dt == DT_F32 || dt == DT_I32) ? 4 : 2; }
+
+// aligned for 4-element (16- or 8-byte) accesses of an output-type tensor
+bool aligned_for(const void* p, int dt) { return ((uintptr_t)p % (4u * out_bytes(dt))) == 0; }
 
 int launch_gemm_plan(const GemmPlan& p, const void* A, const void* B, const void* bias, void* C,
                      const void* R, int dto, int act, float alpha, hipStream_t s) {
@@ -50,7 +51,7 @@ int launch_gemm_plan(const GemmPlan& p, const void* A, const void* B, const void
   a.a_bytes = p.a_bytes;
   a.b_bytes = p.b_bytes;
   a.bias_bytes = p.bias_bytes;
-  a.c_bytes = p.M * p.N * (dto == DT_F32 ? 4u : 2u);
+  a.c_bytes = p.M * p.N * (uint32_t)out_bytes(dto);
   a.bias_dt = p.bias_dt;
   a.act = act;
   a.alpha = alpha;
@@ -64,6 +65,7 @@ int launch_gemm_plan(const GemmPlan& p, const void* A, const void* B, const void
     case DT_F32: rc = launch_gemm_f32(dto, p.tile, a, s); break;
     case DT_F16: rc = launch_gemm_f16(dto, p.tile, a, s); break;
     case DT_BF16: rc = launch_gemm_bf16(dto, p.tile, a, s); break;
+    case DT_I8: rc = launch_gemm_i8(dto, p.tile, a, s); break;
     default: return kErrUnsupported;
   }
   if (rc) return kErrUnsupported;
@@ -164,6 +166,7 @@ int gemm_2k_impl(const void* A, const void* B, const void* bias, const void* R, 
   GemmPlan p;
   int rc = plan_gemm(A, B, bias, C, M, N, K, dtypes, act, &p, R);
   if (rc || p.empty) return rc;
+  if (p.dti == DT_I8) return kErrUnsupported;         // int8 runs the fused path only
   const uint64_t need = (uint64_t)M * (uint64_t)N * 4u;
   if (need >= (1ull << 31)) return kErrUnsupported;
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % 16) != 0) return kErrInvalid;

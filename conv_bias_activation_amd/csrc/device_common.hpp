@@ -16,13 +16,15 @@
 
 namespace biasact {
 
-enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_I8 = 3, DT_I32 = 4 };
 enum : int { ACT_NONE = 0, ACT_RELU = 1, ACT_LEAKY = 2, ACT_TANH = 3, ACT_GELU = 4, ACT_SIGMOID = 5 };
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;   // LDS destination of direct loads
@@ -33,11 +35,14 @@ typedef __attribute__((address_space(3))) void lds_void;   // LDS destination of
 constexpr uint32_t kOOB = 0x80000000u;
 
 // Element traits.  A "chunk" is 16 bytes of consecutive reduction-index (k)
-// values: 8 for 16-bit inputs, 4 for fp32.
+// values: 16 for int8, 8 for 16-bit inputs, 4 for fp32.  int32 appears only
+// as a bias and an output type.
 template <int DT> struct Elem;
 template <> struct Elem<DT_F32>  { static constexpr int bytes = 4, epc = 4; };
 template <> struct Elem<DT_F16>  { static constexpr int bytes = 2, epc = 8; };
 template <> struct Elem<DT_BF16> { static constexpr int bytes = 2, epc = 8; };
+template <> struct Elem<DT_I8>   { static constexpr int bytes = 1, epc = 16; };
+template <> struct Elem<DT_I32>  { static constexpr int bytes = 4, epc = 4; };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t nbytes) {
   // dword3 0x00020000: raw (untyped) 32-bit data format for gfx9-family buffers.
@@ -55,6 +60,9 @@ __device__ __forceinline__ uint32_t ld_b32(__amdgpu_buffer_rsrc_t r, uint32_t of
 }
 __device__ __forceinline__ uint16_t ld_b16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ uint8_t ld_b8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
 }
 __device__ __forceinline__ void st_b128(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
@@ -74,6 +82,8 @@ __device__ __forceinline__ void st_b16(__amdgpu_buffer_rsrc_t r, uint32_t off, u
 // Exact widening of one stored element to fp32.
 template <int DT> __device__ __forceinline__ float widen(uint32_t w);
 template <> __device__ __forceinline__ float widen<DT_F32>(uint32_t w) { return __uint_as_float(w); }
+// int32 values travel through the float-typed epilogue as their bit pattern
+template <> __device__ __forceinline__ float widen<DT_I32>(uint32_t w) { return __uint_as_float(w); }
 template <> __device__ __forceinline__ float widen<DT_F16>(uint32_t w) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)w);
 }
@@ -85,6 +95,7 @@ template <> __device__ __forceinline__ float widen<DT_BF16>(uint32_t w) {
 // conversions v_cvt_f16_f32 / v_cvt_pk_bf16_f32 round to nearest even).
 template <int DT> __device__ __forceinline__ uint32_t narrow(float v);
 template <> __device__ __forceinline__ uint32_t narrow<DT_F32>(float v) { return __float_as_uint(v); }
+template <> __device__ __forceinline__ uint32_t narrow<DT_I32>(float v) { return __float_as_uint(v); }
 template <> __device__ __forceinline__ uint32_t narrow<DT_F16>(float v) {
   // The opaque copy keeps the compiler from folding a multiply that produced
   // v into a mixed-precision multiply-add rounding straight to fp16: that
@@ -217,6 +228,13 @@ template <> __device__ __forceinline__ void mfma_chunk<DT_BF16>(f32x16& acc, u32
 template <> __device__ __forceinline__ void mfma_chunk<DT_F16>(f32x16& acc, u32x4 a, u32x4 b) {
   acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
+}
+// int8: one v_mfma_i32_32x32x32_i8 (16 k-values per lane); the int32
+// accumulators live in the float-typed accumulator registers as bit patterns.
+template <> __device__ __forceinline__ void mfma_chunk<DT_I8>(f32x16& acc, u32x4 a, u32x4 b) {
+  acc = __builtin_bit_cast(f32x16, __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                                       __builtin_bit_cast(i32x4, a), __builtin_bit_cast(i32x4, b),
+                                       __builtin_bit_cast(i32x16, acc), 0, 0, 0));
 }
 template <> __device__ __forceinline__ void mfma_chunk<DT_F32>(f32x16& acc, u32x4 a, u32x4 b) {
   acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);

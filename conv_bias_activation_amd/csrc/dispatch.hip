@@ -12,6 +12,10 @@ int launch_gemm_f16_bf16(int tile, const GemmArgs& a, hipStream_t s);
 int launch_gemm_bf16_f32(int tile, const GemmArgs& a, hipStream_t s);
 int launch_gemm_bf16_f16(int tile, const GemmArgs& a, hipStream_t s);
 int launch_gemm_bf16_bf16(int tile, const GemmArgs& a, hipStream_t s);
+int launch_gemm_i8_f32(int tile, const GemmArgs& a, hipStream_t s);
+int launch_gemm_i8_f16(int tile, const GemmArgs& a, hipStream_t s);
+int launch_gemm_i8_bf16(int tile, const GemmArgs& a, hipStream_t s);
+int launch_gemm_i8_i32(int tile, const GemmArgs& a, hipStream_t s);
 int launch_conv_f32_f32(int tile, const ConvArgs& a, hipStream_t s);
 int launch_conv_f32_f16(int tile, const ConvArgs& a, hipStream_t s);
 int launch_conv_f32_bf16(int tile, const ConvArgs& a, hipStream_t s);
@@ -45,6 +49,16 @@ int launch_gemm_bf16(int dto, int tile, const GemmArgs& a, hipStream_t s) {
     case DT_F32: return launch_gemm_bf16_f32(tile, a, s);
     case DT_F16: return launch_gemm_bf16_f16(tile, a, s);
     case DT_BF16: return launch_gemm_bf16_bf16(tile, a, s);
+    default: return -1;
+  }
+}
+
+int launch_gemm_i8(int dto, int tile, const GemmArgs& a, hipStream_t s) {
+  switch (dto) {
+    case DT_F32: return launch_gemm_i8_f32(tile, a, s);
+    case DT_F16: return launch_gemm_i8_f16(tile, a, s);
+    case DT_BF16: return launch_gemm_i8_bf16(tile, a, s);
+    case DT_I32: return launch_gemm_i8_i32(tile, a, s);
     default: return -1;
   }
 }

@@ -19,7 +19,7 @@ __device__ __forceinline__ void load_bias_vec(const void* bias, uint32_t nbytes,
                                               const uint32_t (&idx)[NV], uint32_t lim,
                                               float (&out)[NV]) {
   const __amdgpu_buffer_rsrc_t r = make_rsrc(bias, nbytes);
-  if (dt == DT_F32) {
+  if (dt == DT_F32 || dt == DT_I32) {        // int32: the bit pattern, for int8 GEMMs
 #pragma unroll
     for (int v = 0; v < NV; ++v) out[v] = __uint_as_float(ld_b32(r, idx[v] < lim ? idx[v] * 4u : kOOB));
   } else if (dt == DT_F16) {
@@ -40,7 +40,7 @@ template <int DTO>
 __device__ __forceinline__ void load4(__amdgpu_buffer_rsrc_t r, uint32_t off_elems, bool ok,
                                       float (&v)[4]) {
   const uint32_t off = ok ? off_elems * Elem<DTO>::bytes : kOOB;
-  if constexpr (DTO == DT_F32) {
+  if constexpr (Elem<DTO>::bytes == 4) {
     const u32x4 w = ld_b128(r, off);
     v[0] = __uint_as_float(w.x); v[1] = __uint_as_float(w.y);
     v[2] = __uint_as_float(w.z); v[3] = __uint_as_float(w.w);
@@ -54,8 +54,24 @@ __device__ __forceinline__ void load4(__amdgpu_buffer_rsrc_t r, uint32_t off_ele
 template <int DTO>
 __device__ __forceinline__ float load1(__amdgpu_buffer_rsrc_t r, uint32_t off_elems, bool ok) {
   const uint32_t off = ok ? off_elems * Elem<DTO>::bytes : kOOB;
-  if constexpr (DTO == DT_F32) return __uint_as_float(ld_b32(r, off));
+  if constexpr (Elem<DTO>::bytes == 4) return __uint_as_float(ld_b32(r, off));
   else return widen<DTO>(ld_b16(r, off));
+}
+
+// The value an epilogue stores for one accumulator register z.  With int8
+// operands the register holds the exact int32 sum (bias included): an int32
+// output keeps the integer (ReLU applied on it; the planner admits no other
+// activation there), any other output takes it rounded to fp32 and applies
+// the activation in fp32.
+template <int DTI, int DTO, int ACT>
+__device__ __forceinline__ float out_value(float z, float alpha) {
+  if constexpr (DTI == DT_I8) {
+    const int zi = __float_as_int(z);
+    if constexpr (DTO == DT_I32) return __int_as_float(ACT == ACT_RELU ? (zi > 0 ? zi : 0) : zi);
+    else return act_fn<ACT>((float)zi, alpha);
+  } else {
+    return act_fn<ACT>(z, alpha);
+  }
 }
 
 // Store four consecutive outputs (one accumulator register group).
@@ -63,7 +79,7 @@ template <int DTO>
 __device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t r, uint32_t off_elems, bool ok,
                                        float v0, float v1, float v2, float v3) {
   const uint32_t off = ok ? off_elems * Elem<DTO>::bytes : kOOB;
-  if constexpr (DTO == DT_F32) {
+  if constexpr (Elem<DTO>::bytes == 4) {
     u32x4 o;
     o.x = __float_as_uint(v0); o.y = __float_as_uint(v1);
     o.z = __float_as_uint(v2); o.w = __float_as_uint(v3);
@@ -79,7 +95,7 @@ __device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t r, uint32_t off_el
 template <int DTO>
 __device__ __forceinline__ void store1(__amdgpu_buffer_rsrc_t r, uint32_t off_elems, bool ok, float v) {
   const uint32_t off = ok ? off_elems * Elem<DTO>::bytes : kOOB;
-  if constexpr (DTO == DT_F32) st_b32(r, off, __float_as_uint(v));
+  if constexpr (Elem<DTO>::bytes == 4) st_b32(r, off, __float_as_uint(v));
   else st_b16(r, off, (uint16_t)narrow<DTO>(v));
 }
 

@@ -82,7 +82,7 @@ __global__ __launch_bounds__(TL::threads, 1) void gemm_bias_act_kernel(GemmArgs 
         const bool mok = m < a.M;
         float z[4] = {acc[si][sj][4 * g + 0], acc[si][sj][4 * g + 1], acc[si][sj][4 * g + 2],
                       acc[si][sj][4 * g + 3]};
-        if constexpr (HAS_R) {
+        if constexpr (HAS_R && DTI != DT_I8) {
           if (a.vec_c) {
             float rv[4];
             load4<DTO>(rr, m * a.N + n, mok && n < a.N, rv);
@@ -93,10 +93,10 @@ __global__ __launch_bounds__(TL::threads, 1) void gemm_bias_act_kernel(GemmArgs 
             for (int e = 0; e < 4; ++e) z[e] += load1<DTO>(rr, m * a.N + n + e, mok && n + e < a.N);
           }
         }
-        const float y0 = act_fn<ACT>(z[0], a.alpha);
-        const float y1 = act_fn<ACT>(z[1], a.alpha);
-        const float y2 = act_fn<ACT>(z[2], a.alpha);
-        const float y3 = act_fn<ACT>(z[3], a.alpha);
+        const float y0 = out_value<DTI, DTO, ACT>(z[0], a.alpha);
+        const float y1 = out_value<DTI, DTO, ACT>(z[1], a.alpha);
+        const float y2 = out_value<DTI, DTO, ACT>(z[2], a.alpha);
+        const float y3 = out_value<DTI, DTO, ACT>(z[3], a.alpha);
         if (a.vec_c) {
           store4<DTO>(rc, m * a.N + n, mok && n < a.N, y0, y1, y2, y3);
         } else {
@@ -316,7 +316,7 @@ inline int launch_gemm_tile(int tile, const GemmArgs& a, hipStream_t s) {
         launch_gemm_t<DTI, DTO, T5>(a, s);
       return 0;
     case 6:
-      if constexpr (DTI != DT_F32) {
+      if constexpr (DTI == DT_F16 || DTI == DT_BF16) {
         if (a.vec_a && a.vec_b && a.vec_c) {
           launch_gemm_pp<DTI, DTO>(a, s);
           return 0;

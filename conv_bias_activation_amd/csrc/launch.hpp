@@ -55,6 +55,7 @@ struct HaloArgs {
 int launch_gemm_f32(int dto, int tile, const GemmArgs& a, hipStream_t s);
 int launch_gemm_f16(int dto, int tile, const GemmArgs& a, hipStream_t s);
 int launch_gemm_bf16(int dto, int tile, const GemmArgs& a, hipStream_t s);
+int launch_gemm_i8(int dto, int tile, const GemmArgs& a, hipStream_t s);
 int launch_conv_f32(int dto, int tile, const ConvArgs& a, hipStream_t s);
 int launch_conv_f16(int dto, int tile, const ConvArgs& a, hipStream_t s);
 int launch_conv_bf16(int dto, int tile, const ConvArgs& a, hipStream_t s);

@@ -53,6 +53,11 @@ __device__ __forceinline__ u32x4 pack_chunk(const uint32_t (&w)[Elem<DT>::epc]) 
   u32x4 v;
   if constexpr (Elem<DT>::bytes == 4) {
     v.x = w[0]; v.y = w[1]; v.z = w[2]; v.w = w[3];
+  } else if constexpr (Elem<DT>::bytes == 1) {
+    v.x = (w[0] & 0xffu) | ((w[1] & 0xffu) << 8) | ((w[2] & 0xffu) << 16) | (w[3] << 24);
+    v.y = (w[4] & 0xffu) | ((w[5] & 0xffu) << 8) | ((w[6] & 0xffu) << 16) | (w[7] << 24);
+    v.z = (w[8] & 0xffu) | ((w[9] & 0xffu) << 8) | ((w[10] & 0xffu) << 16) | (w[11] << 24);
+    v.w = (w[12] & 0xffu) | ((w[13] & 0xffu) << 8) | ((w[14] & 0xffu) << 16) | (w[15] << 24);
   } else {
     v.x = (w[0] & 0xffffu) | (w[1] << 16);
     v.y = (w[2] & 0xffffu) | (w[3] << 16);
@@ -65,6 +70,7 @@ __device__ __forceinline__ u32x4 pack_chunk(const uint32_t (&w)[Elem<DT>::epc]) 
 template <int DT>
 __device__ __forceinline__ uint32_t ld_elem(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   if constexpr (Elem<DT>::bytes == 4) return ld_b32(r, off);
+  else if constexpr (Elem<DT>::bytes == 1) return (uint32_t)ld_b8(r, off);
   else return (uint32_t)ld_b16(r, off);
 }
 
@@ -196,6 +202,18 @@ struct DenseColLoader {
         u32x4 o;
         if constexpr (ES == 4) {
           o.x = reg[i][0][j]; o.y = reg[i][1][j]; o.z = reg[i][2][j]; o.w = reg[i][3][j];
+        } else if constexpr (ES == 1) {
+          // byte j % 4 of dword j / 4 of rows 4q .. 4q+3 form dword q of chunk j
+          const int d = j >> 2, b = j & 3;
+          const uint32_t sel = (uint32_t)b | ((uint32_t)(4 + b) << 8) | 0x0c0c0000u;
+          uint32_t q4[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t lo = __builtin_amdgcn_perm(reg[i][4 * q + 1][d], reg[i][4 * q + 0][d], sel);
+            const uint32_t hi = __builtin_amdgcn_perm(reg[i][4 * q + 3][d], reg[i][4 * q + 2][d], sel);
+            q4[q] = lo | (hi << 16);
+          }
+          o.x = q4[0]; o.y = q4[1]; o.z = q4[2]; o.w = q4[3];
         } else {
           // element (row r, column j) is half (j & 1) of dword j/2 of row r
           const int d = j >> 1;

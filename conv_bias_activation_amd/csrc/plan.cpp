@@ -9,12 +9,14 @@ namespace biasact {
 
 namespace {
 
-constexpr int kF32 = 0, kF16 = 1, kBF16 = 2;
+constexpr int kF32 = 0, kF16 = 1, kBF16 = 2, kI8 = 3, kI32 = 4;
 constexpr int64_t kMaxBytes = (int64_t)1 << 31;   // every tensor < 2 GiB (32-bit buffer offsets)
+// int8 GEMMs: K * 128 * 128 < 2^31, so the product sum alone fits int32
+constexpr int64_t kMaxKInt8 = 131071;
 
-int elem_bytes(int dt) { return dt == kF32 ? 4 : 2; }
-int chunk_elems(int dt) { return dt == kF32 ? 4 : 8; }   // 16 bytes of one type
-bool valid_dt(int dt) { return dt == kF32 || dt == kF16 || dt == kBF16; }
+int elem_bytes(int dt) { return dt == kI8 ? 1 : (dt == kF32 || dt == kI32) ? 4 : 2; }
+int chunk_elems(int dt) { return 16 / elem_bytes(dt); }   // 16 bytes of one type
+bool valid_float_dt(int dt) { return dt == kF32 || dt == kF16 || dt == kBF16; }
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 std::atomic<int> g_forced_tile{-1};
@@ -22,13 +24,21 @@ std::atomic<int> g_forced_halo{-1};
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Shared dtype decoding: A/x and B/w share one type; bias is fp32 or that
-// type; the output is any of the three.
+// Shared dtype decoding: A/x and B/w share one type.  Floating-point operands:
+// bias fp32 or the operand type, output fp32, fp16 or bf16.  int8 operands:
+// bias int32 (the only bias type the MatmulLeakyRelu page allows for int8),
+// output int32 or a floating-point type.
 int decode_dtypes(uint32_t dtypes, bool has_bias, int* dti, int* dto, int* dtb) {
   const int a = (int)(dtypes & 0xffu), b = (int)((dtypes >> 8) & 0xffu);
   const int bias = (int)((dtypes >> 16) & 0xffu), out = (int)((dtypes >> 24) & 0xffu);
-  if (!valid_dt(a) || b != a || !valid_dt(out)) return kErrUnsupported;
-  if (has_bias && !(bias == kF32 || bias == a)) return kErrUnsupported;
+  if (b != a) return kErrUnsupported;
+  if (a == kI8) {
+    if (!(valid_float_dt(out) || out == kI32)) return kErrUnsupported;
+    if (has_bias && bias != kI32) return kErrUnsupported;
+  } else {
+    if (!valid_float_dt(a) || !valid_float_dt(out)) return kErrUnsupported;
+    if (has_bias && !(bias == kF32 || bias == a)) return kErrUnsupported;
+  }
   *dti = a;
   *dto = out;
   *dtb = has_bias ? bias : -1;
@@ -201,9 +211,12 @@ int forced_halo_variant() { return g_forced_halo.load(std::memory_order_relaxed)
 void set_forced_halo_variant(int v) { g_forced_halo.store(v, std::memory_order_relaxed); }
 void set_forced_tile(int id) { g_forced_tile.store(id, std::memory_order_relaxed); }
 
-int select_gemm_tile(int64_t M, int64_t N, int64_t /*K*/, int /*dti*/) {
+int select_gemm_tile(int64_t M, int64_t N, int64_t /*K*/, int dti) {
   // Largest tiles first while the grid still covers all 256 compute units.
+  // int8 skips 256x256: its 16x16-byte register transposes of B do not fit
+  // beside 256 accumulators per lane.
   static const int order[] = {0, 1, 2, 3, 5};
+  if (dti == kI8) return pick_tile(order + 1, 4, M, N, 256);
   return pick_tile(order, 5, M, N, 256);
 }
 
@@ -225,6 +238,12 @@ int plan_gemm(const void* A, const void* B, const void* bias, const void* C, int
   int dti, dto, dtb;
   int rc = decode_dtypes(dtypes, bias != nullptr, &dti, &dto, &dtb);
   if (rc) return rc;
+  if (dti == kI8) {
+    if (K > kMaxKInt8) return kErrUnsupported;
+    // an int32 output holds integers: no activation with a non-integer result
+    if (dto == kI32 && act != 0 && act != 1) return kErrUnsupported;
+    if (R) return kErrUnsupported;                      // no residual on int8 GEMMs
+  }
   const int64_t es = elem_bytes(dti);
   const int64_t a_bytes = M * K * es, b_bytes = K * N * es, c_bytes = M * N * elem_bytes(dto);
   const int64_t bias_bytes = bias ? N * elem_bytes(dtb) : 0;
@@ -250,7 +269,7 @@ int plan_gemm(const void* A, const void* B, const void* bias, const void* C, int
   int tile = forced_tile();
   if (tile < 0 || tile >= kNumTileConfigs) tile = select_gemm_tile(M, N, K, dti);
   // the ping-pong kernel takes 16-bit operands with 16-byte aligned rows
-  const bool pp_ok = dti != kF32 && p->vec_a && p->vec_b && p->vec_c;
+  const bool pp_ok = (dti == kF16 || dti == kBF16) && p->vec_a && p->vec_b && p->vec_c;
   if (tile == 0 && pp_ok && forced_tile() < 0) tile = 6;
   if (tile == 6 && !pp_ok) tile = 0;
   if (tile == 7) tile = 2;                              // the halo tile is conv-only
@@ -279,6 +298,7 @@ int plan_conv(const void* x, const void* w, const void* bias, const void* y, int
   int dti, dto, dtb;
   int rc = decode_dtypes(dtypes, bias != nullptr, &dti, &dto, &dtb);
   if (rc) return rc;
+  if (dti == kI8) return kErrUnsupported;              // int8 is a GEMM-only path
   const int64_t es = elem_bytes(dti);
   const int64_t K = C * kh * kw, P = N * Ho * Wo;
   const int64_t x_bytes = N * C * H * W * es, w_bytes = Co * K * es;

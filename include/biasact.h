@@ -54,16 +54,26 @@
 extern "C" {
 #endif
 
-/* element type codes (storage size: 4, 2, 2 bytes) */
+/* element type codes (storage size: 4, 2, 2, 1, 4 bytes) */
 #define BA_F32 0u
 #define BA_F16 1u
 #define BA_BF16 2u
+#define BA_I8 3u            /* two's complement int8: GEMM operands only */
+#define BA_I32 4u           /* two's complement int32: bias / output of int8 GEMMs */
 
 /* dtypes argument: one 8-bit code per operand.
  *   a   : A (GEMM) or x (conv)
  *   b   : B (GEMM) or w (conv)      — must equal a
  *   bias: bias element type         — fp32, or the same type as a (ignored when bias == NULL)
- *   out : C (GEMM) or y (conv)      — fp32, fp16 or bf16 */
+ *   out : C (GEMM) or y (conv)      — fp32, fp16 or bf16
+ * int8 GEMMs ("CANN pyasc MatmulLeakyRelu 融合算子实战", section 补充说明: with
+ * int8 A and B the bias must be int32): a = b = BA_I8, bias BA_I32, out BA_I32
+ * or a floating-point type.  The sum A.B + bias is exact in int32 (K is
+ * limited to 131071 so that the product sum alone fits; the bias must keep
+ * the total in range, else it wraps); an int32 output takes act NONE or RELU
+ * only, a floating-point output the integer rounded to fp32 and then any
+ * activation.  gemm_bias_act only: the conv, two-kernel and residual entry
+ * points return BA_ERR_UNSUPPORTED for int8. */
 #define BA_DTYPES(a, b, bias, out) \
   ((uint32_t)(a) | ((uint32_t)(b) << 8) | ((uint32_t)(bias) << 16) | ((uint32_t)(out) << 24))
 

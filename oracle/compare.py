@@ -92,7 +92,10 @@ def compare(y: np.ndarray, ref: np.ndarray, in_dtype: str, out_dtype: str,
         "n": int(y.size),
         "n_bad": n_bad,
         "max_abs_err": float(np.nanmax(err)) if y.size else 0.0,
-        "max_err_over_tol": float(np.nanmax(err / tol)) if y.size else 0.0,
+        # an exact (zero) tolerance: any error is infinitely over it
+        "max_err_over_tol": float(np.nanmax(np.where(tol > 0, err / np.where(tol > 0, tol, 1.0),
+                                                     np.where(err > 0, np.inf, 0.0))))
+        if y.size else 0.0,
         "n_nonfinite": int((~np.isfinite(y)).sum()),
     }
     if floor is not None:

@@ -21,7 +21,8 @@ def O():
 
 def torch_dtype(dt):
     import torch
-    return {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dt]
+    return {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "i8": torch.int8,
+            "i32": torch.int32}[dt]
 
 
 def to_dev(words: np.ndarray, dt: str, guard: int = 0, fill_word=None):
@@ -32,6 +33,8 @@ def to_dev(words: np.ndarray, dt: str, guard: int = 0, fill_word=None):
     words = np.ascontiguousarray(words)
     if dt == "f32":
         host = torch.from_numpy(words.view(np.float32).copy())
+    elif dt in ("i8", "i32"):
+        host = torch.from_numpy(words.view(np.int8 if dt == "i8" else np.int32).copy())
     else:
         host = torch.from_numpy(words.view(np.int16).copy()).view(torch_dtype(dt))
     if not guard:
@@ -70,7 +73,7 @@ def words_of(t, dt: str) -> np.ndarray:
     """Flat output words of a device tensor."""
     import torch
     c = t.detach().cpu().contiguous().reshape(-1)
-    if dt == "f32":
+    if dt in ("f32", "i32"):
         return c.view(torch.int32).numpy().view(np.uint32).copy()
     return c.view(torch.int16).numpy().view(np.uint16).copy()
 

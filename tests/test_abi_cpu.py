@@ -160,6 +160,30 @@ def test_residual_entry_points_validate():
                                     NUL) == 1
 
 
+I8, I32 = 3, 4
+
+
+def test_int8_type_rules():
+    dt = _dt(I8, I8, I32, I32)
+    # valid int8 problems fail only later, at launch, on this machine; the
+    # planner's rejections come first and need no GPU
+    assert L.gemm_bias_act(P, P, P, P, 4, 4, 4, _dt(I8, I8, F32, F32), 1, 0.0, NUL) == 2  # bias must be int32
+    assert L.gemm_bias_act(P, P, P, P, 4, 4, 4, _dt(I8, F16, I32, I32), 1, 0.0, NUL) == 2
+    assert L.gemm_bias_act(P, P, P, P, 4, 4, 4, _dt(F16, F16, I32, F32), 1, 0.0, NUL) == 2  # int32 bias needs int8
+    assert L.gemm_bias_act(P, P, P, P, 4, 4, 4, _dt(F16, F16, F32, I32), 1, 0.0, NUL) == 2  # int32 out needs int8
+    assert L.gemm_bias_act(P, P, P, P, 4, 4, 4, dt, 3, 0.0, NUL) == 2     # tanh into int32
+    assert L.gemm_bias_act(P, P, P, P, 4, 4, 4, dt, 2, 0.1, NUL) == 2     # leaky into int32
+    assert L.gemm_bias_act(P, P, P, P, 4, 4, 131072, dt, 1, 0.0, NUL) == 2   # K past the int32-safe bound
+    assert L.gemm_bias_act(P, P, P, P, 0, 4, 4, dt, 1, 0.0, NUL) == 0     # empty: nothing launched
+    # the fused GEMM only
+    assert L.gemm_bias_act_2k(P, P, P, P, 4, 4, 4, dt, 1, 0.0, P, 64, NUL) == 2
+    assert L.gemm_bias_add_act(P, P, P, P, P, 4, 4, 4, dt, 1, 0.0, NUL) == 2
+    c = (ctypes.c_int32 * 2)(1, 1), (ctypes.c_int32 * 4)(1, 1, 1, 1), (ctypes.c_int32 * 2)(1, 1)
+    assert L.conv2d_bias_act(P, P, P, P, 1, 3, 8, 8, 4, 3, 3, *c, _dt(I8, I8, I32, I32), 1, NUL) == 2
+    # int8 never takes the 256x256 tile
+    assert ba.gemm_tile_config(4096, 4096, 4096, dt) == 1
+
+
 def test_gemm_2k_workspace_checks():
     dt = _dt(BF16, BF16, F32, BF16)
     assert L.gemm_bias_act_2k(P, P, P, P, 4, 4, 4, dt, 1, 0.0, NUL, 64, NUL) == 1

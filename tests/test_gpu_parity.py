@@ -480,8 +480,9 @@ def test_named_workload_full_size(ba, name):
         _report(f"{name} seed {seed}", rep)
         assert rep["ok"], rep
         assert np.all(np.isfinite(vals))
-        # the two-kernel path gives the same bits at full size
-        if seed == 0:
+        # the two-kernel path gives the same bits at full size (int8 GEMMs
+        # have the fused path only)
+        if seed == 0 and case.in_dtype != "i8":
             y2 = run_gemm(case, inp, "2k") if is_gemm else run_conv(case, inp, "2k")
             assert np.array_equal(words_of(y2, case.out_dtype), words_of(y_t, case.out_dtype))
         del y_t

@@ -226,6 +226,11 @@ CASES: Dict[str, object] = {
     "gemm_relu_residual_4096_bf16": GemmCase(
         "gemm_relu_residual_4096_bf16", 4096, 4096, 4096, "bf16", "f32", "bf16", "relu", 0.0,
         ("normal", 1.0 / 64.0), ("normal", 1.0 / 64.0), U01, U01),
+    # int8 operands with an int32 bias (MatmulLeakyRelu page, 补充说明), exact
+    # int32 output with ReLU, at the 4096^3 shape.
+    "gemm_int8_relu_4096_i32": GemmCase(
+        "gemm_int8_relu_4096_i32", 4096, 4096, 4096, "i8", "i32", "i32", "relu", 0.0,
+        ("ints", -128, 127), ("ints", -128, 127), ("ints", -100000, 100000)),
     "conv3x3_residual_tanh_8x64x56_f16": ConvCase(
         "conv3x3_residual_tanh_8x64x56_f16", 8, 64, 56, 56, 64, 3, 3, (1, 1), (1, 1, 1, 1),
         (1, 1), "f16", "f16", "f16", "tanh", 0.0, U01, U01, U01, U01),
@@ -241,6 +246,7 @@ GROUPS = {
     5: ["gemm_leaky_32768x4096x1024_bf16", "conv3x3d2_tanh_32x128x28_bf16"],
     6: ["gemm_gelu_4096_bf16", "conv3x3_sigmoid_8x64x56_f16"],      # epilogue extensions
     7: ["gemm_relu_residual_4096_bf16", "conv3x3_residual_tanh_8x64x56_f16"],
+    8: ["gemm_int8_relu_4096_i32"],
 }
 
 
