@@ -23,6 +23,12 @@ from ._binding import (  # noqa: F401
     last_tile_config,
     force_tile_config,
     gemm_bias_act,
+    gemm_bias_act_auto,
+    conv2d_bias_act_auto,
+    gemm_path,
+    conv_path,
+    tune_gemm,
+    tune_conv,
     gemm_bias_add_act,
     gemm_bias_add_act_2k,
     conv2d_bias_add_act,

@@ -61,6 +61,20 @@ def _load():
     l.conv2d_bias_act_workspace_size.restype = ctypes.c_size_t
     l.biasact_status_string.argtypes = [ctypes.c_int]
     l.biasact_status_string.restype = ctypes.c_char_p
+    ip = ctypes.POINTER(ctypes.c_int)
+    l.biasact_gemm_path.argtypes = [i64, i64, i64, u32, ctypes.c_int]
+    l.biasact_gemm_path.restype = ctypes.c_int
+    l.biasact_conv_path.argtypes = [i64] * 7 + [i32p, i32p, i32p, u32, ctypes.c_int]
+    l.biasact_conv_path.restype = ctypes.c_int
+    l.biasact_tune_gemm.argtypes = ([vp, vp, vp, vp, i64, i64, i64, u32, ctypes.c_int, ctypes.c_float,
+                                     vp, ctypes.c_size_t, ctypes.c_int, vp, ip])
+    l.biasact_tune_gemm.restype = ctypes.c_int
+    l.biasact_tune_conv.argtypes = conv + [vp, ctypes.c_size_t, ctypes.c_int, vp, ip]
+    l.biasact_tune_conv.restype = ctypes.c_int
+    l.gemm_bias_act_auto.argtypes = l.gemm_bias_act_2k.argtypes
+    l.gemm_bias_act_auto.restype = ctypes.c_int
+    l.conv2d_bias_act_auto.argtypes = l.conv2d_bias_act_2k.argtypes
+    l.conv2d_bias_act_auto.restype = ctypes.c_int
     l.biasact_last_tile_config.argtypes = [ctypes.c_char_p, ctypes.c_size_t]
     l.biasact_last_tile_config.restype = ctypes.c_int
     l.biasact_last_hip_error.argtypes = []
@@ -315,6 +329,80 @@ def conv2d_bias_add_act_2k(x, w, bias, R, y, strides=(1, 1), pads=(0, 0, 0, 0), 
                                     _act(act), _dev(workspace, "workspace"), nbytes,
                                     _stream(stream))
     _check(rc, "conv2d_bias_add_act_2k")
+    return y
+
+
+# -- fused or two-kernel, per problem -------------------------------------------
+
+PATH_NAMES = {0: "fused", 1: "2k"}
+
+
+def gemm_path(M, N, K, dtypes: int, act="none") -> str:
+    return PATH_NAMES[int(lib.biasact_gemm_path(M, N, K, dtypes, _act(act)))]
+
+
+def conv_path(N, C, H, W, Co, kh, kw, strides, pads, dilations, dtypes: int, act="tanh") -> str:
+    rc = int(lib.biasact_conv_path(N, C, H, W, Co, kh, kw, _i32x(strides, 2, "strides"),
+                                   _i32x(pads, 4, "pads"), _i32x(dilations, 2, "dilations"), dtypes,
+                                   _act(act)))
+    if rc < 0:
+        _check(-rc, "conv_path")
+    return PATH_NAMES[rc]
+
+
+def _ws(workspace):
+    if workspace is None:
+        return None, 0
+    return _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+
+
+def tune_gemm(A, B, bias, C, act="none", alpha: float = 0.0, workspace=None, reps: int = 20,
+              stream=None) -> str:
+    """Times both paths on these buffers (synchronising the stream; C is
+    overwritten) and records the faster for this problem."""
+    M, N, K, dt = _gemm_args(A, B, bias, C)
+    ws, nbytes = _ws(workspace)
+    path = ctypes.c_int(-1)
+    rc = lib.biasact_tune_gemm(_dev(A, "A"), _dev(B, "B"), _dev(bias, "bias"), _dev(C, "C"), M, N,
+                               K, dt, _act(act), float(alpha), ws, nbytes, int(reps),
+                               _stream(stream), ctypes.byref(path))
+    _check(rc, "tune_gemm")
+    return PATH_NAMES[path.value]
+
+
+def tune_conv(x, w, bias, y, strides=(1, 1), pads=(0, 0, 0, 0), dilations=(1, 1), act="tanh",
+              workspace=None, reps: int = 20, stream=None) -> str:
+    dims, dt = _conv_args(x, w, bias, y, strides, pads, dilations)
+    ws, nbytes = _ws(workspace)
+    path = ctypes.c_int(-1)
+    rc = lib.biasact_tune_conv(_dev(x, "x"), _dev(w, "w"), _dev(bias, "bias"), _dev(y, "y"), *dims,
+                               _i32x(strides, 2, "strides"), _i32x(pads, 4, "pads"),
+                               _i32x(dilations, 2, "dilations"), dt, _act(act), ws, nbytes,
+                               int(reps), _stream(stream), ctypes.byref(path))
+    _check(rc, "tune_conv")
+    return PATH_NAMES[path.value]
+
+
+def gemm_bias_act_auto(A, B, bias, C, act="none", alpha: float = 0.0, workspace=None, stream=None):
+    """The recorded path for this problem (fused unless tuning chose the
+    two-kernel path and a workspace is given)."""
+    M, N, K, dt = _gemm_args(A, B, bias, C)
+    ws, nbytes = _ws(workspace)
+    rc = lib.gemm_bias_act_auto(_dev(A, "A"), _dev(B, "B"), _dev(bias, "bias"), _dev(C, "C"), M, N,
+                                K, dt, _act(act), float(alpha), ws, nbytes, _stream(stream))
+    _check(rc, "gemm_bias_act_auto")
+    return C
+
+
+def conv2d_bias_act_auto(x, w, bias, y, strides=(1, 1), pads=(0, 0, 0, 0), dilations=(1, 1),
+                         act="tanh", workspace=None, stream=None):
+    dims, dt = _conv_args(x, w, bias, y, strides, pads, dilations)
+    ws, nbytes = _ws(workspace)
+    rc = lib.conv2d_bias_act_auto(_dev(x, "x"), _dev(w, "w"), _dev(bias, "bias"), _dev(y, "y"),
+                                  *dims, _i32x(strides, 2, "strides"), _i32x(pads, 4, "pads"),
+                                  _i32x(dilations, 2, "dilations"), dt, _act(act), ws, nbytes,
+                                  _stream(stream))
+    _check(rc, "conv2d_bias_act_auto")
     return y
 
 

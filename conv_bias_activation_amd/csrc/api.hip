@@ -5,6 +5,10 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <map>
+#include <mutex>
+#include <vector>
+
 #include "biasact.h"
 #include "launch.hpp"
 #include "launch_kernel.hpp"
@@ -205,6 +209,78 @@ int conv_2k_impl(const void* x, const void* w, const void* bias, const void* r, 
   return launch_second_kernel(p.dto, workspace, y, need / 4u, act, 0.0f, r, stream);
 }
 
+// ---- fused-vs-two-kernel selection --------------------------------------
+// Decisions recorded by the tuning calls, per problem (kind, sizes, types,
+// activation); the auto entry points look them up.
+std::mutex g_path_mu;
+std::map<std::vector<int64_t>, int> g_paths;
+
+std::vector<int64_t> gemm_key(int64_t M, int64_t N, int64_t K, uint32_t dtypes, int act) {
+  return {0, M, N, K, (int64_t)dtypes, act};
+}
+
+std::vector<int64_t> conv_key(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Co, int64_t kh,
+                              int64_t kw, const int32_t* st, const int32_t* pd, const int32_t* dl,
+                              uint32_t dtypes, int act) {
+  return {1, N, C, H, W, Co, kh, kw, st[0], st[1], pd[0], pd[1], pd[2], pd[3], dl[0], dl[1],
+          (int64_t)dtypes, act};
+}
+
+int lookup_path(const std::vector<int64_t>& key) {
+  std::lock_guard<std::mutex> g(g_path_mu);
+  auto it = g_paths.find(key);
+  return it == g_paths.end() ? BA_PATH_FUSED : it->second;
+}
+
+void record_path(const std::vector<int64_t>& key, int path) {
+  std::lock_guard<std::mutex> g(g_path_mu);
+  g_paths[key] = path;
+}
+
+// Mean milliseconds per call of `run` over `reps` calls on `stream`, after
+// one untimed call; negative status on a launch or runtime error.
+template <class F>
+int time_calls(F&& run, int reps, hipStream_t stream, float* ms) {
+  int rc = run();
+  if (rc) return rc;
+  hipEvent_t e0, e1;
+  if (hipEventCreate(&e0) != hipSuccess) return kErrHip;
+  if (hipEventCreate(&e1) != hipSuccess) {
+    (void)hipEventDestroy(e0);
+    return kErrHip;
+  }
+  rc = hipEventRecord(e0, stream) == hipSuccess ? kOk : kErrHip;
+  for (int i = 0; i < reps && rc == kOk; ++i) rc = run();
+  if (rc == kOk && hipEventRecord(e1, stream) != hipSuccess) rc = kErrHip;
+  if (rc == kOk && hipEventSynchronize(e1) != hipSuccess) rc = kErrHip;
+  float t = 0.0f;
+  if (rc == kOk && hipEventElapsedTime(&t, e0, e1) != hipSuccess) rc = kErrHip;
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  *ms = t / (float)reps;
+  return rc;
+}
+
+// Times the fused call and, where it runs, the two-kernel call; records and
+// returns the faster path (or a negative-free error status through *path).
+template <class FF, class FT>
+int tune_paths(FF&& fused, FT&& two, bool two_ok, int reps, hipStream_t stream,
+               const std::vector<int64_t>& key, int* path) {
+  if (reps < 1) return kErrInvalid;
+  float t_fused = 0.0f, t_two = 0.0f;
+  int rc = time_calls(fused, reps, stream, &t_fused);
+  if (rc) return rc;
+  int best = BA_PATH_FUSED;
+  if (two_ok) {
+    rc = time_calls(two, reps, stream, &t_two);
+    if (rc) return rc;
+    if (t_two < t_fused) best = BA_PATH_TWO_KERNEL;
+  }
+  record_path(key, best);
+  *path = best;
+  return kOk;
+}
+
 }  // namespace
 
 extern "C" {
@@ -287,6 +363,86 @@ int conv2d_bias_add_act_2k(const void* x, const void* w, const void* bias, const
   if (!r && N > 0) return kErrInvalid;
   return conv_2k_impl(x, w, bias, r, y, N, C, H, W, Co, kh, kw, strides, pads, dilations, dtypes,
                       act, workspace, workspace_bytes, stream);
+}
+
+int biasact_gemm_path(int64_t M, int64_t N, int64_t K, uint32_t dtypes, int act) {
+  return lookup_path(gemm_key(M, N, K, dtypes, act));
+}
+
+int biasact_conv_path(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Co, int64_t kh,
+                      int64_t kw, const int32_t strides[2], const int32_t pads[4],
+                      const int32_t dilations[2], uint32_t dtypes, int act) {
+  if (!strides || !pads || !dilations) return -kErrInvalid;
+  return lookup_path(conv_key(N, C, H, W, Co, kh, kw, strides, pads, dilations, dtypes, act));
+}
+
+int biasact_tune_gemm(const void* A, const void* B, const void* bias, void* C, int64_t M,
+                      int64_t N, int64_t K, uint32_t dtypes, int act, float alpha, void* workspace,
+                      size_t workspace_bytes, int reps, hipStream_t stream, int* path) {
+  if (!path) return kErrInvalid;
+  GemmPlan p;
+  int rc = plan_gemm(A, B, bias, C, M, N, K, dtypes, act, &p);
+  if (rc) return rc;
+  const bool two_ok = p.dti != DT_I8 && workspace &&
+                      workspace_bytes >= (uint64_t)M * (uint64_t)N * 4u;
+  return tune_paths(
+      [&]() { return gemm_impl(A, B, bias, nullptr, C, M, N, K, dtypes, act, alpha, stream); },
+      [&]() {
+        return gemm_2k_impl(A, B, bias, nullptr, C, M, N, K, dtypes, act, alpha, workspace,
+                            workspace_bytes, stream);
+      },
+      two_ok, reps, stream, gemm_key(M, N, K, dtypes, act), path);
+}
+
+int biasact_tune_conv(const void* x, const void* w, const void* bias, void* y, int64_t N,
+                      int64_t C, int64_t H, int64_t W, int64_t Co, int64_t kh, int64_t kw,
+                      const int32_t strides[2], const int32_t pads[4], const int32_t dilations[2],
+                      uint32_t dtypes, int act, void* workspace, size_t workspace_bytes, int reps,
+                      hipStream_t stream, int* path) {
+  if (!path) return kErrInvalid;
+  ConvPlan p;
+  int rc = plan_conv(x, w, bias, y, N, C, H, W, Co, kh, kw, strides, pads, dilations, dtypes, act,
+                     &p);
+  if (rc) return rc;
+  const bool two_ok = workspace && workspace_bytes >= (uint64_t)p.N * p.Co * p.Ho * p.Wo * 4u;
+  return tune_paths(
+      [&]() {
+        return conv_impl(x, w, bias, nullptr, y, N, C, H, W, Co, kh, kw, strides, pads, dilations,
+                         dtypes, act, stream);
+      },
+      [&]() {
+        return conv_2k_impl(x, w, bias, nullptr, y, N, C, H, W, Co, kh, kw, strides, pads,
+                            dilations, dtypes, act, workspace, workspace_bytes, stream);
+      },
+      two_ok, reps, stream, conv_key(N, C, H, W, Co, kh, kw, strides, pads, dilations, dtypes, act),
+      path);
+}
+
+int gemm_bias_act_auto(const void* A, const void* B, const void* bias, void* C, int64_t M,
+                       int64_t N, int64_t K, uint32_t dtypes, int act, float alpha, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  const int path = lookup_path(gemm_key(M, N, K, dtypes, act));
+  if (path == BA_PATH_TWO_KERNEL && workspace && workspace_bytes >= (uint64_t)M * N * 4u)
+    return gemm_2k_impl(A, B, bias, nullptr, C, M, N, K, dtypes, act, alpha, workspace,
+                        workspace_bytes, stream);
+  return gemm_impl(A, B, bias, nullptr, C, M, N, K, dtypes, act, alpha, stream);
+}
+
+int conv2d_bias_act_auto(const void* x, const void* w, const void* bias, void* y, int64_t N,
+                         int64_t C, int64_t H, int64_t W, int64_t Co, int64_t kh, int64_t kw,
+                         const int32_t strides[2], const int32_t pads[4],
+                         const int32_t dilations[2], uint32_t dtypes, int act, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  if (!strides || !pads || !dilations) return kErrInvalid;
+  const int path =
+      lookup_path(conv_key(N, C, H, W, Co, kh, kw, strides, pads, dilations, dtypes, act));
+  if (path == BA_PATH_TWO_KERNEL && workspace &&
+      workspace_bytes >= conv2d_bias_act_workspace_size(N, C, H, W, Co, kh, kw, strides, pads,
+                                                        dilations))
+    return conv_2k_impl(x, w, bias, nullptr, y, N, C, H, W, Co, kh, kw, strides, pads, dilations,
+                        dtypes, act, workspace, workspace_bytes, stream);
+  return conv_impl(x, w, bias, nullptr, y, N, C, H, W, Co, kh, kw, strides, pads, dilations,
+                   dtypes, act, stream);
 }
 
 const char* biasact_status_string(int status) { return status_string(status); }

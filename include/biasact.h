@@ -164,6 +164,49 @@ int conv2d_bias_add_act_2k(const void* x, const void* w, const void* bias, const
                            const int32_t dilations[2], uint32_t dtypes, int act, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
 
+/* Fused or two-kernel path, chosen per problem.  The pages decide at run
+ * time whether to fuse: ops-nn (mlqm.cn/news/1824, section
+ * "fused_matmul_relu底层到底做了什么") checks that the tiles and the
+ * activation's buffer fit the on-chip budget and otherwise runs the two
+ * steps; the Fused ConvTanh article (wmrh.cn/news/81139, section 核心问题)
+ * measures first.  Here the fused epilogue needs no on-chip space beyond the
+ * accumulators, so the static choice is BA_PATH_FUSED; biasact_tune_* measure
+ * both paths on the caller's buffers and record the faster for that problem
+ * (sizes, attributes, dtypes, act), and the *_auto entry points follow the
+ * record.  Both paths give the same bits.
+ *   biasact_gemm_path / biasact_conv_path: the recorded (else static) path;
+ *     negative -BA_ERR_INVALID for null attribute arrays.
+ *   biasact_tune_gemm / biasact_tune_conv: run the fused call once plus
+ *     `reps` timed calls, then the two-kernel call likewise (only with a
+ *     workspace of *_workspace_size bytes, and never for int8), SYNCHRONISING
+ *     `stream` (the only library calls that do); the output buffer is
+ *     overwritten; the chosen path goes to *path.  Returns a status code.
+ *     The record is process-wide and guarded by a lock.
+ *   gemm_bias_act_auto / conv2d_bias_act_auto: the recorded path when its
+ *     workspace is given and large enough, else the fused path. */
+#define BA_PATH_FUSED 0
+#define BA_PATH_TWO_KERNEL 1
+int biasact_gemm_path(int64_t M, int64_t N, int64_t K, uint32_t dtypes, int act);
+int biasact_conv_path(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Co, int64_t kh,
+                      int64_t kw, const int32_t strides[2], const int32_t pads[4],
+                      const int32_t dilations[2], uint32_t dtypes, int act);
+int biasact_tune_gemm(const void* A, const void* B, const void* bias, void* C, int64_t M,
+                      int64_t N, int64_t K, uint32_t dtypes, int act, float alpha, void* workspace,
+                      size_t workspace_bytes, int reps, hipStream_t stream, int* path);
+int biasact_tune_conv(const void* x, const void* w, const void* bias, void* y, int64_t N,
+                      int64_t C, int64_t H, int64_t W, int64_t Co, int64_t kh, int64_t kw,
+                      const int32_t strides[2], const int32_t pads[4], const int32_t dilations[2],
+                      uint32_t dtypes, int act, void* workspace, size_t workspace_bytes, int reps,
+                      hipStream_t stream, int* path);
+int gemm_bias_act_auto(const void* A, const void* B, const void* bias, void* C, int64_t M,
+                       int64_t N, int64_t K, uint32_t dtypes, int act, float alpha, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+int conv2d_bias_act_auto(const void* x, const void* w, const void* bias, void* y, int64_t N,
+                         int64_t C, int64_t H, int64_t W, int64_t Co, int64_t kh, int64_t kw,
+                         const int32_t strides[2], const int32_t pads[4],
+                         const int32_t dilations[2], uint32_t dtypes, int act, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
 /* Introspection and tuning. */
 const char* biasact_status_string(int status);  /* static string, never NULL */
 /* The hipError_t behind the most recent BA_ERR_HIP returned on the calling

@@ -184,6 +184,23 @@ def test_int8_type_rules():
     assert ba.gemm_tile_config(4096, 4096, 4096, dt) == 1
 
 
+def test_path_selection_defaults_to_fused():
+    # nothing tuned: the static rule is the fused path for every problem
+    for M, N, K in ((1, 1, 1), (4096, 4096, 4096), (1024, 640, 256)):
+        assert L.biasact_gemm_path(M, N, K, _dt(BF16, BF16, F32, BF16), 1) == 0
+    c = (ctypes.c_int32 * 2)(1, 1), (ctypes.c_int32 * 4)(1, 1, 1, 1), (ctypes.c_int32 * 2)(1, 1)
+    assert L.biasact_conv_path(8, 64, 56, 56, 64, 3, 3, *c, _dt(F16, F16, F16, F16), 3) == 0
+    assert L.biasact_conv_path(8, 64, 56, 56, 64, 3, 3, None, c[1], c[2], 0, 3) == -1
+    # tuning validates before any launch
+    path = ctypes.c_int(-1)
+    assert L.biasact_tune_gemm(P, P, P, P, 4, 4, 4, _dt(BF16, BF16, F32, BF16), 1, 0.0, NUL, 0, 5,
+                               NUL, None) == 1
+    assert L.biasact_tune_gemm(P, P, P, P, 4, 4, 4, _dt(BF16, BF16, F32, BF16), 9, 0.0, NUL, 0, 5,
+                               NUL, ctypes.byref(path)) == 1
+    assert L.gemm_bias_act_auto(NUL, P, P, P, 4, 4, 4, _dt(BF16, BF16, F32, BF16), 1, 0.0, NUL, 0,
+                                NUL) == 1
+
+
 def test_gemm_2k_workspace_checks():
     dt = _dt(BF16, BF16, F32, BF16)
     assert L.gemm_bias_act_2k(P, P, P, P, 4, 4, 4, dt, 1, 0.0, NUL, 64, NUL) == 1

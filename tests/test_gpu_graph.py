@@ -154,3 +154,54 @@ def test_last_tile_config_names_the_kernel(ba):
     call()
     torch.cuda.synchronize()
     assert m.last_tile_config().startswith("conv-halo fp32"), m.last_tile_config()
+
+
+def test_tuned_path_choice_and_auto_calls(ba):
+    # "measure first": tune both paths on the caller's buffers, record the
+    # faster, and let the auto entry point follow it; the bits are those of
+    # the fused call either way
+    import conv_bias_activation_amd as m
+    for (M, N, K, ti, to, act) in ((1024, 640, 256, "f16", "f32", "leaky_relu"),
+                                   (512, 768, 512, "bf16", "bf16", "relu")):
+        case, inp, _, C, call = _gemm_setup(ba, M, N, K, ti, to, act, "fused")
+        call()
+        torch.cuda.synchronize()
+        want = C.clone()
+        ws = torch.empty(m.gemm_bias_act_workspace_size(M, N) // 4, dtype=torch.float32,
+                         device="cuda")
+        dt = m.dtypes_code(ti, ti, "f32", to)
+        assert m.gemm_path(M, N, K, dt, act) == "fused"          # nothing recorded yet
+        A, B, bias, C2 = _gemm_tensors(case, inp)
+        got = m.tune_gemm(A, B, bias, C2, act=act, alpha=0.05, workspace=ws, reps=5)
+        assert got in ("fused", "2k")
+        assert m.gemm_path(M, N, K, dt, act) == got
+        C2.zero_()
+        m.gemm_bias_act_auto(A, B, bias, C2, act, 0.05, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(C2), _bits(want))
+    # conv: a problem without bias and with zero weights, y = tanh(0) = 0
+    x = torch.randn((4, 64, 28, 28), device="cuda").half()
+    w = torch.zeros((64, 64, 3, 3), dtype=torch.float16, device="cuda")
+    y = torch.empty((4, 64, 28, 28), dtype=torch.float16, device="cuda")
+    n = m.conv2d_bias_act_workspace_size(4, 64, 28, 28, 64, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1))
+    ws = torch.empty(n // 4, dtype=torch.float32, device="cuda")
+    got = m.tune_conv(x, w, None, y, (1, 1), (1, 1, 1, 1), (1, 1), "tanh", workspace=ws, reps=5)
+    assert got in ("fused", "2k")
+    dt = m.dtypes_code("f16", "f16", None, "f16")
+    assert m.conv_path(4, 64, 28, 28, 64, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1), dt, "tanh") == got
+    y.fill_(1.0)
+    m.conv2d_bias_act_auto(x, w, None, y, (1, 1), (1, 1, 1, 1), (1, 1), "tanh", workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(y) == 0
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.element_size() == 2 else t.view(torch.int32)
+
+
+def _gemm_tensors(case, inp):
+    A, _ = to_dev(inp["A"].reshape(case.M, case.K), case.in_dtype)
+    B, _ = to_dev(inp["B"].reshape(case.K, case.N), case.in_dtype)
+    bias, _ = to_dev(inp["bias"], "f32")
+    C = torch.empty((case.M, case.N), dtype=torch_dtype(case.out_dtype), device="cuda")
+    return A, B, bias, C
