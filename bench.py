@@ -16,7 +16,8 @@ Besides the headline, the line carries:
   others        every workload, fused and two-kernel: eager back-to-back steps
                 (mean), HIP-graph replays of R steps (median and minimum of 20
                 trials, no host call cost), and for the HBM-bound workloads
-                single steps after a 512 MiB cache flush.
+                single steps after a 512 MiB cache flush; `tuned_path` is the
+                path the library's own tuner records for the workload.
 """
 from __future__ import annotations
 
@@ -151,6 +152,40 @@ def make_step(case, seed=0, path="fused"):
     if R is not None:
         return (lambda: ba.conv2d_bias_add_act_2k(x, w, bias, R, y, *args, workspace=ws)), 2
     return (lambda: ba.conv2d_bias_act_2k(x, w, bias, y, *args, workspace=ws)), 2
+
+
+def tune_case(case, reps=20):
+    """The library's own fused-vs-two-kernel choice for this workload
+    (biasact_tune_*: both paths timed on these buffers, the faster recorded)."""
+    import torch
+    import conv_bias_activation_amd as ba
+    import workloads as wl
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "i32": torch.int32}
+    if isinstance(case, wl.GemmCase):
+        if case.dist_r:
+            return None                      # the residual entry points are not tuned
+        inp = wl.gen_gemm(case, 0)
+        A = to_device(inp["A"].reshape(case.M, case.K), case.in_dtype)
+        B = to_device(inp["B"].reshape(case.K, case.N), case.in_dtype)
+        bias = None if inp["bias"] is None else to_device(inp["bias"], case.bias_dtype)
+        C = torch.empty((case.M, case.N), dtype=tdt[case.out_dtype], device="cuda")
+        ws = torch.empty(ba.gemm_bias_act_workspace_size(case.M, case.N) // 4, dtype=torch.float32,
+                         device="cuda")
+        return ba.tune_gemm(A, B, bias, C, case.act, float(np.float32(case.alpha)), workspace=ws,
+                            reps=reps)
+    if case.dist_r:
+        return None
+    inp = wl.gen_conv(case, 0)
+    x = to_device(inp["x"].reshape(case.N, case.C, case.H, case.W), case.in_dtype)
+    w = to_device(inp["w"].reshape(case.Co, case.C, case.kh, case.kw), case.in_dtype)
+    bias = None if inp["bias"] is None else to_device(inp["bias"], case.bias_dtype)
+    Ho, Wo = case.out_hw()
+    y = torch.empty((case.N, case.Co, Ho, Wo), dtype=tdt[case.out_dtype], device="cuda")
+    n = ba.conv2d_bias_act_workspace_size(case.N, case.C, case.H, case.W, case.Co, case.kh, case.kw,
+                                          case.strides, case.pads, case.dilations)
+    ws = torch.empty(n // 4, dtype=torch.float32, device="cuda")
+    return ba.tune_conv(x, w, bias, y, case.strides, case.pads, case.dilations, case.act,
+                        workspace=ws, reps=reps)
 
 
 def time_steps(step, steps, warmup):
@@ -362,6 +397,10 @@ def main():
                     entry[path] = measure_case(c, path)
                 except Exception as e:  # report, never hide
                     entry[path] = {"error": repr(e)}
+            try:
+                entry["tuned_path"] = tune_case(c)
+            except Exception as e:  # report, never hide
+                entry["tuned_path"] = {"error": repr(e)}
             others[name] = entry
             torch.cuda.empty_cache()
         line["others"] = others
