@@ -17,7 +17,9 @@ Besides the headline, the line carries:
                 (mean), HIP-graph replays of R steps (median and minimum of 20
                 trials, no host call cost), and for the HBM-bound workloads
                 single steps after a 512 MiB cache flush; `tuned_path` is the
-                path the library's own tuner records for the workload.
+                path the library's own tuner records for the workload;
+                `cpu_oracle` the fp64 oracle's rate on a bounded sample of
+                it, on all host threads (and on one, for the small workloads).
 """
 from __future__ import annotations
 
@@ -292,6 +294,72 @@ def measure_case(case, path, min_ms=200.0):
     return out
 
 
+# workloads whose oracle is also timed on one thread (the small and conv
+# configurations; the large GEMMs only with all threads)
+ONE_THREAD_WORKLOADS = ("gemm_leaky_1024x640x256_f16", "conv3x3_tanh_8x64x56_f16",
+                        "conv7x7s2_tanh_16x3x224_f32", "conv1x1s2_tanh_16x256x56_f32",
+                        "conv3x3d2_tanh_32x128x28_bf16")
+
+
+def _scaled(run, n, limit, target_s):
+    """Grows the sample n (up to limit) until run(n) takes about target_s."""
+    dt, fl = run(n)
+    for _ in range(3):
+        if dt >= 0.5 * target_s or n >= limit:
+            break
+        n = int(min(limit, max(n + 1, n * target_s / max(dt, 1e-6))))
+        dt, fl = run(n)
+    return n, dt, fl
+
+
+def oracle_timing(case, target_s=0.5, threads=None):
+    """The fp64 oracle (contraction + bias + activation) on a bounded sample of
+    the workload: leading output rows (GEMM) or sampled output elements
+    (conv), sized from a short calibration run to take about target_s."""
+    import oracle as orc
+    import workloads as wl
+    O = orc.Oracle()
+    full_threads = O.num_threads()
+    nt = threads or full_threads
+    O.set_num_threads(nt)
+    try:
+        if isinstance(case, wl.GemmCase):
+            inp = wl.gen_gemm(case, 0)
+            B = O.decode(inp["B"], case.in_dtype).reshape(case.K, case.N)
+            bias = O.decode(inp["bias"], case.bias_dtype) if inp["bias"] is not None else None
+            Aw = inp["A"].reshape(case.M, case.K)
+
+            def run(rows):
+                A = O.decode(Aw[:rows], case.in_dtype)
+                t0 = time.perf_counter()
+                O.gemm(A, B, bias, case.act, orc.f32(case.alpha))
+                return time.perf_counter() - t0, 2.0 * rows * case.N * case.K
+
+            rows, dt, fl = _scaled(run, max(1, nt), case.M, target_s)
+            sample = f"{rows} of {case.M} output rows"
+        else:
+            inp = wl.gen_conv(case, 0)
+            x = O.decode(inp["x"], case.in_dtype).reshape(case.N, case.C, case.H, case.W)
+            w = O.decode(inp["w"], case.in_dtype).reshape(case.Co, case.C, case.kh, case.kw)
+            bias = O.decode(inp["bias"], case.bias_dtype) if inp["bias"] is not None else None
+            Ho, Wo = case.out_hw()
+            total = case.N * case.Co * Ho * Wo
+            kflops = 2.0 * case.C * case.kh * case.kw
+
+            def run(n):
+                idx = wl.sample_indices(total, n, 0)
+                t0 = time.perf_counter()
+                O.conv2d_elems(x, w, bias, case.strides, case.pads, case.dilations, idx, case.act)
+                return time.perf_counter() - t0, kflops * idx.size
+
+            n, dt, fl = _scaled(run, 256 * max(1, nt), total, target_s)
+            sample = f"{n} of {total} output elements"
+    finally:
+        O.set_num_threads(full_threads)
+    return {"threads": nt, "seconds": round(dt, 3), "gflops_fp64": round(fl / dt / 1e9, 3),
+            "sample": sample + " (contraction, bias and activation; inputs decoded beforehand)"}
+
+
 def cpu_baseline(case, target_s):
     """The oracle as it stands, on a subset of the workload's output rows."""
     import oracle as orc
@@ -401,6 +469,13 @@ def main():
                 entry["tuned_path"] = tune_case(c)
             except Exception as e:  # report, never hide
                 entry["tuned_path"] = {"error": repr(e)}
+            if not args.no_cpu_baseline:
+                try:
+                    entry["cpu_oracle"] = oracle_timing(c)
+                    if name in ONE_THREAD_WORKLOADS:
+                        entry["cpu_oracle_1thread"] = oracle_timing(c, threads=1)
+                except Exception as e:  # report, never hide
+                    entry["cpu_oracle"] = {"error": repr(e)}
             others[name] = entry
             torch.cuda.empty_cache()
         line["others"] = others

@@ -62,6 +62,8 @@ def _bind(lib):
                                                                     ctypes.c_double, _D]
     lib.orc_conv2d_im2col.argtypes = conv_common + [_D] + shape + [ctypes.c_int, ctypes.c_double,
                                                                    ctypes.c_int]
+    lib.orc_set_num_threads.argtypes = [ctypes.c_int]
+    lib.orc_set_num_threads.restype = None
     lib.orc_num_threads.argtypes = []
     for name in ("orc_decode", "orc_gemm_bias_act", "orc_gemm_bias_act_elems", "orc_gemm_bias_fold",
                  "orc_conv2d_bias_act", "orc_conv2d_bias_act_elems", "orc_conv2d_im2col",
@@ -253,6 +255,9 @@ class Oracle:
 
     def num_threads(self) -> int:
         return int(self.lib.orc_num_threads())
+
+    def set_num_threads(self, n: int) -> None:
+        self.lib.orc_set_num_threads(int(n))
 
 
 def f32(x: float) -> float:

@@ -433,3 +433,14 @@ int orc_num_threads(void)
     return 1;
 #endif
 }
+
+/* Thread count of the following parallel loops (timing only; results do not
+ * depend on it: every output is summed by one thread in index order). */
+void orc_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

@@ -110,6 +110,7 @@ int orc_conv2d_im2col(const double *x, const double *w, const double *bias,
 
 /* Number of OpenMP threads the oracle uses (1 when built without OpenMP). */
 int orc_num_threads(void);
+void orc_set_num_threads(int n);
 
 #ifdef __cplusplus
 }
