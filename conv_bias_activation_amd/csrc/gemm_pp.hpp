@@ -30,6 +30,18 @@
 //            consecutive k of column L%32 that the MFMA expects.
 // Four stages (128 KB of the 160 KB LDS): A0..A3 | B0..B3; stage, subtile and
 // k-step displacements of LDS addresses are instruction immediates.
+//
+// Epilogue.  A 16-bit output tile (256 x 256 x 2 B) fills the LDS exactly, so
+// once the last k-tile is consumed each lane writes its activated, rounded
+// values into LDS (row r = m, 16-byte chunk c of the 512-byte row at slot
+// c ^ (r & 31), which spreads the 32 rows one register group covers over
+// every bank), and the waves then store whole rows: each half-wave writes one
+// 512-byte row with 16-byte stores.  The accumulator layout itself gives only
+// 16 contiguous bytes in each of 32 rows per store instruction, which the
+// memory system drains at about half the rate.  A residual is read the same
+// way (whole rows into LDS, then added in the accumulator layout).  fp32
+// outputs, and C or R not on a 16-byte boundary, store from the accumulator
+// layout directly.
 #pragma once
 
 #include "epilogue.hpp"
@@ -234,6 +246,64 @@ __global__ __launch_bounds__(512, 1) void gemm16_pp_kernel(GemmArgs a) {
   // ---- epilogue: activation, cast, one store per element -----------------
   const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.C, a.c_bytes);
   const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.R, a.R ? a.c_bytes : 0u);
+  bool staged = false;
+  if constexpr (Elem<DTO>::bytes == 2)
+    staged = ((reinterpret_cast<uintptr_t>(a.C) | reinterpret_cast<uintptr_t>(a.R)) & 15u) == 0;
+  if (staged) {
+    __syncthreads();     // every wave's direct loads have landed and its fragment reads are done
+    auto slot = [](int r, int c) { return (uint32_t)(r * 512 + ((c ^ (r & 31)) << 4)); };
+    // rows 16*it + rrow, chunk rchunk; N % 8 == 0 here, so a chunk is wholly inside or outside C
+    const int rrow = 2 * w + (lane >> 5), rchunk = lane & 31;
+    with_act(a.act, [&](auto act_c) __attribute__((always_inline)) {
+      constexpr int ACT = decltype(act_c)::value;
+      with_residual(a.R != nullptr, [&](auto res_c) __attribute__((always_inline)) {
+        constexpr bool HAS_R = decltype(res_c)::value;
+        if constexpr (HAS_R) {
+#pragma unroll
+          for (int it = 0; it < 16; ++it) {
+            const int r = it * 16 + rrow;
+            const uint32_t m = m0 + r, n = n0 + rchunk * 8;
+            *reinterpret_cast<u32x4*>(smem + slot(r, rchunk)) =
+                ld_b128(rr, (m < a.M && n < a.N) ? (m * a.N + n) * 2u : kOOB);
+          }
+          __syncthreads();
+        }
+        // each lane reads (residual) and writes the same 8 bytes: no other lane touches them
+#pragma unroll
+        for (int si = 0; si < 2; ++si)
+#pragma unroll
+          for (int sj = 0; sj < 4; ++sj) {
+            const int r = wm * 128 + sj * 32 + lrow;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              u32x2* p = reinterpret_cast<u32x2*>(smem + slot(r, wn * 8 + si * 4 + g) + half * 8);
+              float z[4] = {acc[si][sj][4 * g + 0], acc[si][sj][4 * g + 1], acc[si][sj][4 * g + 2],
+                            acc[si][sj][4 * g + 3]};
+              if constexpr (HAS_R) {
+                const u32x2 rv = *p;
+                z[0] += widen<DTO>(rv.x & 0xffffu);
+                z[1] += widen<DTO>(rv.x >> 16);
+                z[2] += widen<DTO>(rv.y & 0xffffu);
+                z[3] += widen<DTO>(rv.y >> 16);
+              }
+              u32x2 o;
+              o.x = narrow<DTO>(act_fn<ACT>(z[0], a.alpha)) | (narrow<DTO>(act_fn<ACT>(z[1], a.alpha)) << 16);
+              o.y = narrow<DTO>(act_fn<ACT>(z[2], a.alpha)) | (narrow<DTO>(act_fn<ACT>(z[3], a.alpha)) << 16);
+              *p = o;
+            }
+          }
+      });
+    });
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int r = it * 16 + rrow;
+      const uint32_t m = m0 + r, n = n0 + rchunk * 8;
+      st_b128(rc, (m < a.M && n < a.N) ? (m * a.N + n) * 2u : kOOB,
+              *reinterpret_cast<const u32x4*>(smem + slot(r, rchunk)));
+    }
+    return;
+  }
   with_act(a.act, [&](auto act_c) __attribute__((always_inline)) {
     constexpr int ACT = decltype(act_c)::value;
     with_residual(a.R != nullptr, [&](auto res_c) __attribute__((always_inline)) {

@@ -69,13 +69,16 @@ def _gemm_ref(case, inp, r_words):
     return ref, floor
 
 
-def _run_gemm(ba, case, inp, r_words, path="fused", inplace=False, r_offset=0):
+def _run_gemm(ba, case, inp, r_words, path="fused", inplace=False, r_offset=0, c_offset=0):
     A, _ = to_dev(inp["A"].reshape(case.M, case.K), case.in_dtype)
     B, _ = to_dev(inp["B"].reshape(case.K, case.N), case.in_dtype)
     bias, _ = to_dev(inp["bias"], case.bias_dtype)
     R = _dev_out(r_words.reshape(case.M, case.N), case.out_dtype, r_offset)
-    C = R if inplace else torch.empty((case.M, case.N), dtype=torch_dtype(case.out_dtype),
-                                      device="cuda")
+    if inplace:
+        C = R
+    else:
+        buf = torch.empty(case.M * case.N + c_offset, dtype=torch_dtype(case.out_dtype), device="cuda")
+        C = buf[c_offset:].view(case.M, case.N)
     alpha = float(np.float32(case.alpha))
     if path == "fused":
         ba.gemm_bias_add_act(A, B, bias, R, C, case.act, alpha)
@@ -134,6 +137,41 @@ def test_gemm_residual_misaligned(ba, ti, to):
     b = _run_gemm(ba, case, inp, r, r_offset=1)
     assert check(values_of(b, to), ref, floor, case)["ok"]
     assert np.array_equal(words_of(a, to), words_of(b, to))
+
+
+@pytest.mark.parametrize("to", ["bf16", "f16"])
+def test_pp_row_staged_and_direct_epilogues_agree(ba, to):
+    # The ping-pong kernel writes a 16-bit output through LDS, in whole rows,
+    # when C and R lie on 16-byte boundaries, and straight from the
+    # accumulator layout when one of them lies 8 bytes off (still aligned for
+    # its 4-wide accesses).  Both give the oracle's result and the same bits,
+    # with and without a residual, over ragged M and N (N % 8 == 0).
+    case = _gemm_case(300, 520, 200, "bf16", to, "tanh")
+    inp = wl.gen_gemm(case, seed=66)
+    r = _residual_words((300, 520), to, seed=67)
+    ref, floor = _gemm_ref(case, inp, r)
+    ref0, floor0 = _gemm_ref(case, inp, _residual_words((300, 520), to, seed=0, scale=0.0))
+    ba.force_tile_config(6)
+    try:
+        staged = _run_gemm(ba, case, inp, r)
+        assert check(values_of(staged, to), ref, floor, case)["ok"]
+        for kw in ({"c_offset": 4}, {"r_offset": 4}):
+            direct = _run_gemm(ba, case, inp, r, **kw)
+            assert np.array_equal(words_of(staged, to), words_of(direct, to)), kw
+        plain = []
+        for off in (0, 4):                       # no residual: the plain entry point
+            A, _ = to_dev(inp["A"].reshape(300, 200), "bf16")
+            B, _ = to_dev(inp["B"].reshape(200, 520), "bf16")
+            bias, _ = to_dev(inp["bias"], "f32")
+            buf = torch.empty(300 * 520 + off, dtype=torch_dtype(to), device="cuda")
+            C = buf[off:].view(300, 520)
+            ba.gemm_bias_act(A, B, bias, C, case.act, float(np.float32(case.alpha)))
+            torch.cuda.synchronize()
+            plain.append(C)
+        assert check(values_of(plain[0], to), ref0, floor0, case)["ok"]
+        assert np.array_equal(words_of(plain[0], to), words_of(plain[1], to))
+    finally:
+        ba.force_tile_config(-1)
 
 
 def test_gemm_residual_zero_equals_plain(ba):
