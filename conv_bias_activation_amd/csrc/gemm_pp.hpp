@@ -1,11 +1,12 @@
 // gemm_pp.hpp — the large-tile fused GEMM + bias + activation for fp16 / bf16
-// operands on gfx950 ("ping-pong" kernel).
+// and int8 operands on gfx950 ("ping-pong" kernel).
 //
 //   C[M,N] = act(A[M,K] . B[K,N] + bias[N])   ([MLR] 概述 / 样例规格; [FMR]
 //   fused_matmul_relu: the intermediate never leaves the chip, one HBM read of
 //   the operands and one write of C)
 //
-// Workgroup: 512 threads = 8 waves, output tile 256 (m) x 256 (n), k-tile 32.
+// Workgroup: 512 threads = 8 waves, output tile 256 (m) x 256 (n), k-tile of
+// 64 bytes per row of A (32 16-bit values, 64 int8 values).
 // Waves 0-3 form cluster 0 and waves 4-7 cluster 1; wave w owns the 128 (m) x
 // 64 (n) sub-tile at m = 128*(w/4), n = 64*(w%4), i.e. 4 x 2 accumulator
 // blocks of 32x32 (128 fp32 values per lane).  Each SIMD runs one wave of
@@ -28,6 +29,16 @@
 //            addresses row 8*(L/32) + (L%16)/4 (+4 for the second read),
 //            columns 16*((L/16)%2) + 4*(L%4) .. +3, and receives the 8
 //            consecutive k of column L%32 that the MFMA expects.
+//   int8 B:  64 rows (k) x 256 B, chunk c of row k at slot c ^ 2*(k & 7) (the
+//            32 reads of a half-wave cover all 64 banks); ds_read_b64_tr_b8
+//            (in each 16-lane group, lane i receives byte i%8 of the 8-byte
+//            rows addressed by lanes i/8 + 2r, r = 0..7): lane L addresses row
+//            16*(L/32) + (L%16)/2 (+8 for the second read), columns
+//            16*((L/16)%2) + 8*(L%2) .. +7, and receives 8 consecutive k of
+//            column L%32; with the A chunk of the same 16 k this feeds
+//            v_mfma_i32_32x32x32_i8, whose int32 sums (bias included) are exact.
+//            The LDS displacements of the second read (+2048) and of the next
+//            k-step (+8192) are the 16-bit kernel's.
 // Four stages (128 KB of the 160 KB LDS): A0..A3 | B0..B3; stage, subtile and
 // k-step displacements of LDS addresses are instruction immediates.
 //
@@ -37,11 +48,11 @@
 // c ^ (r & 31), which spreads the 32 rows one register group covers over
 // every bank), and the waves then store whole rows: each half-wave writes one
 // 512-byte row with 16-byte stores.  The accumulator layout itself gives only
-// 16 contiguous bytes in each of 32 rows per store instruction, which the
-// memory system drains at about half the rate.  A residual is read the same
-// way (whole rows into LDS, then added in the accumulator layout).  fp32
-// outputs, and C or R not on a 16-byte boundary, store from the accumulator
-// layout directly.
+// 16 contiguous bytes in each of 32 rows per store instruction; stored that
+// way a 4096^3 bf16 output costs 1.56x its size in HBM writes.  A residual is
+// read the same way (whole rows into LDS, then added in the accumulator
+// layout).  32-bit outputs (fp32, int32) leave in two passes of 128 rows.  C
+// or R not on a 16-byte boundary store from the accumulator layout directly.
 #pragma once
 
 #include "epilogue.hpp"
@@ -55,9 +66,9 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 namespace pp {
-constexpr int BM = 256, BN = 256, BK = 32, THREADS = 512, STAGES = 4;
-constexpr int A_STAGE = BM * BK * 2;         // 16 KB
-constexpr int B_STAGE = BK * BN * 2;         // 16 KB
+constexpr int BM = 256, BN = 256, THREADS = 512, STAGES = 4;
+constexpr int A_STAGE = BM * 64;             // 16 KB: 64 bytes of k per row
+constexpr int B_STAGE = BN * 64;             // 16 KB: 32 rows of 16-bit n, or 64 rows of int8 n
 constexpr int A_OFF = 0, B_OFF = STAGES * A_STAGE;
 constexpr int LDS_BYTES = STAGES * (A_STAGE + B_STAGE);
 constexpr int LOADS_PER_TILE = 4;            // direct loads per wave per k-tile
@@ -68,6 +79,7 @@ constexpr int wait_vm(int n) { return 0x0F70 | (n & 0xF) | ((n >> 4) << 14); }
 
 __device__ __forceinline__ int swz_a(int row) { return (row >> 2) & 3; }
 __device__ __forceinline__ int swz_b(int k) { return 4 * (k & 3); }
+__device__ __forceinline__ int swz_b8(int k) { return 2 * (k & 7); }
 
 // Transposing 8-byte LDS read (see the header comment for the lane layout).
 // Issued as inline assembly: the compiler cannot tell that it does not touch
@@ -80,13 +92,41 @@ __device__ __forceinline__ u32x2 ds_read_tr16_b64(uint32_t lds_addr) {
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(lds_addr), "i"(OFFSET));
   return v;
 }
+template <int OFFSET>
+__device__ __forceinline__ u32x2 ds_read_tr8_b64(uint32_t lds_addr) {
+  u32x2 v;
+  asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(v) : "v"(lds_addr), "i"(OFFSET));
+  return v;
+}
+// B fragment of k-step KS of the stage at lds_addr (16 k per lane: two transposing reads)
+template <int DTI, int KS>
+__device__ __forceinline__ u32x4 read_b_frag(uint32_t lds_addr) {
+  u32x2 lo, hi;
+  if constexpr (DTI == DT_I8) {
+    lo = ds_read_tr8_b64<KS * 8192>(lds_addr);
+    hi = ds_read_tr8_b64<KS * 8192 + 2048>(lds_addr);
+  } else {
+    lo = ds_read_tr16_b64<KS * 8192>(lds_addr);
+    hi = ds_read_tr16_b64<KS * 8192 + 2048>(lds_addr);
+  }
+  u32x4 f;
+  f.x = lo.x;
+  f.y = lo.y;
+  f.z = hi.x;
+  f.w = hi.y;
+  return f;
+}
 
 }  // namespace pp
 
 template <int DTI, int DTO>
 __global__ __launch_bounds__(512, 1) void gemm16_pp_kernel(GemmArgs a) {
-  static_assert(DTI == DT_F16 || DTI == DT_BF16, "16-bit operands only");
+  static_assert(DTI == DT_F16 || DTI == DT_BF16 || DTI == DT_I8, "16-bit or int8 operands");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[pp::LDS_BYTES];
+  constexpr uint32_t ES = Elem<DTI>::bytes, EPC = Elem<DTI>::epc;   // bytes per value, values per chunk
+  constexpr uint32_t BK = 64 / ES;                                   // k values per k-tile
+  constexpr int BRPI = DTI == DT_I8 ? 4 : 2;                         // B rows per 1 KB direct load
+  constexpr int BCPR = 64 / BRPI;                                    // 16-byte chunks per B row
 
   uint32_t tm, tn;
   map_tile(blockIdx.x, gridDim.x, a.tiles_m, a.tiles_n, tm, tn);
@@ -119,7 +159,7 @@ __global__ __launch_bounds__(512, 1) void gemm16_pp_kernel(GemmArgs a) {
 
   // ---- per-lane global offsets of this wave's direct loads --------------
   // A: instruction i covers stage rows (2w + i)*16 .. +16 (16 rows x 64 B);
-  // B: instruction i covers stage rows (k) (2w + i)*2 .. +2 (2 rows x 512 B).
+  // B: instruction i covers stage rows (k) (2w + i)*BRPI .. +BRPI (1 KB).
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.A, a.a_bytes);
   const __amdgpu_buffer_rsrc_t rbm = make_rsrc(a.B, a.b_bytes);
   uint32_t a_off[2], a_k[2], b_off[2], b_k[2];
@@ -128,25 +168,26 @@ __global__ __launch_bounds__(512, 1) void gemm16_pp_kernel(GemmArgs a) {
     const int row = (2 * w + i) * 16 + (lane >> 2);
     const int c = (lane & 3) ^ pp::swz_a(row);               // logical k-chunk for slot lane&3
     const uint32_t gm = m0 + row;
-    a_off[i] = gm < a.M ? (gm * a.K + c * 8) * 2 : kOOB;
-    a_k[i] = c * 8;
-    const int k = (2 * w + i) * 2 + (lane >> 5);
-    const int cb = (lane & 31) ^ pp::swz_b(k);               // logical n-chunk for slot lane&31
-    const uint32_t gn = n0 + cb * 8;
-    b_off[i] = (gn < a.N && (uint32_t)k < a.K) ? ((uint32_t)k * a.N + gn) * 2 : kOOB;
+    a_off[i] = gm < a.M ? (gm * a.K + c * EPC) * ES : kOOB;
+    a_k[i] = c * EPC;
+    const int k = (2 * w + i) * BRPI + lane / BCPR;
+    const int slot = lane % BCPR;
+    const int cb = slot ^ (DTI == DT_I8 ? pp::swz_b8(k) : pp::swz_b(k));   // logical n-chunk for the slot
+    const uint32_t gn = n0 + cb * EPC;
+    b_off[i] = (gn < a.N && (uint32_t)k < a.K) ? ((uint32_t)k * a.N + gn) * ES : kOOB;
     b_k[i] = k;
   }
-  const uint32_t b_kstep = (uint32_t)pp::BK * a.N * 2u;     // bytes of B per k-tile
+  const uint32_t b_kstep = BK * a.N * ES;                   // bytes of B per k-tile
 
   // One direct load j (0..3) of k-tile kt: even j = A rows, odd j = B rows.
   // K-tiles at or beyond K read as zeros (every offset fails the K test), so
   // the loop can issue its loads unconditionally into the stage it frees.
   auto issue_one = [&](int kt, int j) {
     const int stage = kt & (pp::STAGES - 1);
-    const uint32_t kk = (uint32_t)kt * pp::BK;
+    const uint32_t kk = (uint32_t)kt * BK;
     const int i = j >> 1;
     if ((j & 1) == 0) {
-      const uint32_t ao = (a_off[i] != kOOB && kk + a_k[i] < a.K) ? a_off[i] + kk * 2u : kOOB;
+      const uint32_t ao = (a_off[i] != kOOB && kk + a_k[i] < a.K) ? a_off[i] + kk * ES : kOOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           ra, (lds_void*)(smem + pp::A_OFF + stage * pp::A_STAGE + (2 * w + i) * 1024), 16, ao, 0, 0, 0);
     } else {
@@ -163,17 +204,26 @@ __global__ __launch_bounds__(512, 1) void gemm16_pp_kernel(GemmArgs a) {
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
     a_rd[ks] = pp::A_OFF + (wm * 128 + lrow) * 64 + (((2 * ks + half) ^ xa) * 16);
-  // B (n side): k = 8*half + (lane%16)/4 (+ 16*ks + 4*q), n = wn*64 + si*32 + 16*((lane/16)%2) + 4*(lane%4)
+  // B (n side), 16-bit: k = 8*half + (lane%16)/4 (+ 16*ks + 4*q),
+  //   n = wn*64 + si*32 + 16*((lane/16)%2) + 4*(lane%4);
+  // int8: k = 16*half + (lane%16)/2 (+ 32*ks + 8*q), n = wn*64 + si*32 + 16*((lane/16)%2) + 8*(lane%2)
   uint32_t b_rd[2];
 #pragma unroll
   for (int si = 0; si < 2; ++si) {
-    const int k = 8 * half + ((lane & 15) >> 2);
-    const int n = wn * 64 + si * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    const int phys = (n >> 3) ^ pp::swz_b(k);
-    b_rd[si] = pp::B_OFF + k * 512 + phys * 16 + (n & 7) * 2;
+    if constexpr (DTI == DT_I8) {
+      const int k = 16 * half + ((lane & 15) >> 1);
+      const int n = wn * 64 + si * 32 + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
+      const int phys = (n >> 4) ^ pp::swz_b8(k);
+      b_rd[si] = pp::B_OFF + k * 256 + phys * 16 + (n & 15);
+    } else {
+      const int k = 8 * half + ((lane & 15) >> 2);
+      const int n = wn * 64 + si * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      const int phys = (n >> 3) ^ pp::swz_b(k);
+      b_rd[si] = pp::B_OFF + k * 512 + phys * 16 + (n & 7) * 2;
+    }
   }
 
-  const int ktiles = (int)((a.K + pp::BK - 1) / pp::BK);
+  const int ktiles = (int)((a.K + BK - 1) / BK);
   // LDS byte address of smem (an address-space-3 pointer converts to its offset)
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)smem;
 
@@ -212,15 +262,7 @@ __global__ __launch_bounds__(512, 1) void gemm16_pp_kernel(GemmArgs a) {
 #pragma unroll
       for (int si = 0; si < 2; ++si) {
         const uint32_t base = lds_base + b_rd[si] + stage * pp::B_STAGE;
-        const u32x2 lo = ks == 0 ? pp::ds_read_tr16_b64<0>(base) : pp::ds_read_tr16_b64<16 * 512>(base);
-        const u32x2 hi = ks == 0 ? pp::ds_read_tr16_b64<4 * 512>(base)
-                                 : pp::ds_read_tr16_b64<16 * 512 + 4 * 512>(base);
-        u32x4 f;
-        f.x = lo.x;
-        f.y = lo.y;
-        f.z = hi.x;
-        f.w = hi.y;
-        fb[si][ks] = f;
+        fb[si][ks] = ks == 0 ? pp::read_b_frag<DTI, 0>(base) : pp::read_b_frag<DTI, 1>(base);
       }
     }
     // k-tile kt+1 landed for this wave (k-tiles kt+2 and kt+3 may be in flight)
@@ -258,7 +300,7 @@ __global__ __launch_bounds__(512, 1) void gemm16_pp_kernel(GemmArgs a) {
       constexpr int ACT = decltype(act_c)::value;
       with_residual(a.R != nullptr, [&](auto res_c) __attribute__((always_inline)) {
         constexpr bool HAS_R = decltype(res_c)::value;
-        if constexpr (HAS_R) {
+        if constexpr (HAS_R && DTI != DT_I8) {     // int8 GEMMs take no residual
 #pragma unroll
           for (int it = 0; it < 16; ++it) {
             const int r = it * 16 + rrow;
@@ -279,7 +321,7 @@ __global__ __launch_bounds__(512, 1) void gemm16_pp_kernel(GemmArgs a) {
               u32x2* p = reinterpret_cast<u32x2*>(smem + slot(r, wn * 8 + si * 4 + g) + half * 8);
               float z[4] = {acc[si][sj][4 * g + 0], acc[si][sj][4 * g + 1], acc[si][sj][4 * g + 2],
                             acc[si][sj][4 * g + 3]};
-              if constexpr (HAS_R) {
+              if constexpr (HAS_R && DTI != DT_I8) {
                 const u32x2 rv = *p;
                 z[0] += widen<DTO>(rv.x & 0xffffu);
                 z[1] += widen<DTO>(rv.x >> 16);
@@ -287,8 +329,11 @@ __global__ __launch_bounds__(512, 1) void gemm16_pp_kernel(GemmArgs a) {
                 z[3] += widen<DTO>(rv.y >> 16);
               }
               u32x2 o;
-              o.x = narrow<DTO>(act_fn<ACT>(z[0], a.alpha)) | (narrow<DTO>(act_fn<ACT>(z[1], a.alpha)) << 16);
-              o.y = narrow<DTO>(act_fn<ACT>(z[2], a.alpha)) | (narrow<DTO>(act_fn<ACT>(z[3], a.alpha)) << 16);
+              float v[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] = out_value<DTI, DTO, ACT>(z[e], a.alpha);
+              o.x = narrow<DTO>(v[0]) | (narrow<DTO>(v[1]) << 16);
+              o.y = narrow<DTO>(v[2]) | (narrow<DTO>(v[3]) << 16);
               *p = o;
             }
           }
@@ -302,6 +347,73 @@ __global__ __launch_bounds__(512, 1) void gemm16_pp_kernel(GemmArgs a) {
       st_b128(rc, (m < a.M && n < a.N) ? (m * a.N + n) * 2u : kOOB,
               *reinterpret_cast<const u32x4*>(smem + slot(r, rchunk)));
     }
+    return;
+  }
+  bool staged32 = false;
+  if constexpr (Elem<DTO>::bytes == 4)
+    staged32 = ((reinterpret_cast<uintptr_t>(a.C) | reinterpret_cast<uintptr_t>(a.R)) & 15u) == 0;
+  if (staged32) {
+    // 32-bit outputs: the 256 KB tile leaves in two passes of 128 rows (one
+    // cluster's rows each) through 128 KB of LDS: 1 KB rows, 16-byte chunk c
+    // of row r at slot c ^ 2*(r & 31); each wave then stores whole rows.
+    auto slot = [](int r, int c) { return (uint32_t)(r * 1024 + ((c ^ (2 * (r & 31))) << 4)); };
+    with_act(a.act, [&](auto act_c) __attribute__((always_inline)) {
+      constexpr int ACT = decltype(act_c)::value;
+      with_residual(a.R != nullptr, [&](auto res_c) __attribute__((always_inline)) {
+        constexpr bool HAS_R = decltype(res_c)::value && DTI != DT_I8;   // int8 GEMMs take no residual
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+          // pass 0: every direct load has landed and every fragment read is done;
+          // pass 1: the rows of pass 0 have left LDS
+          __syncthreads();
+          if constexpr (HAS_R) {
+#pragma unroll
+            for (int it = 0; it < 16; ++it) {
+              const int r = it * 8 + w;
+              const uint32_t m = m0 + pass * 128 + r, n = n0 + lane * 4;
+              *reinterpret_cast<u32x4*>(smem + slot(r, lane)) =
+                  ld_b128(rr, (m < a.M && n < a.N) ? (m * a.N + n) * 4u : kOOB);
+            }
+            __syncthreads();
+          }
+          if (wm == pass) {
+#pragma unroll
+            for (int si = 0; si < 2; ++si)
+#pragma unroll
+              for (int sj = 0; sj < 4; ++sj) {
+                const int r = sj * 32 + lrow;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                  u32x4* p = reinterpret_cast<u32x4*>(smem + slot(r, wn * 16 + si * 8 + 2 * g + half));
+                  float z[4] = {acc[si][sj][4 * g + 0], acc[si][sj][4 * g + 1], acc[si][sj][4 * g + 2],
+                                acc[si][sj][4 * g + 3]};
+                  if constexpr (HAS_R) {
+                    const u32x4 rv = *p;
+                    z[0] += __uint_as_float(rv.x);
+                    z[1] += __uint_as_float(rv.y);
+                    z[2] += __uint_as_float(rv.z);
+                    z[3] += __uint_as_float(rv.w);
+                  }
+                  u32x4 o;
+                  o.x = narrow<DTO>(out_value<DTI, DTO, ACT>(z[0], a.alpha));
+                  o.y = narrow<DTO>(out_value<DTI, DTO, ACT>(z[1], a.alpha));
+                  o.z = narrow<DTO>(out_value<DTI, DTO, ACT>(z[2], a.alpha));
+                  o.w = narrow<DTO>(out_value<DTI, DTO, ACT>(z[3], a.alpha));
+                  *p = o;
+                }
+              }
+          }
+          __syncthreads();
+#pragma unroll
+          for (int it = 0; it < 16; ++it) {
+            const int r = it * 8 + w;
+            const uint32_t m = m0 + pass * 128 + r, n = n0 + lane * 4;   // N % 8 == 0: 4 values all in or out
+            st_b128(rc, (m < a.M && n < a.N) ? (m * a.N + n) * 4u : kOOB,
+                    *reinterpret_cast<const u32x4*>(smem + slot(r, lane)));
+          }
+        }
+      });
+    });
     return;
   }
   with_act(a.act, [&](auto act_c) __attribute__((always_inline)) {
@@ -319,14 +431,16 @@ __global__ __launch_bounds__(512, 1) void gemm16_pp_kernel(GemmArgs a) {
             const bool ok = m < a.M && n < a.N;
             float z[4] = {acc[si][sj][4 * g + 0], acc[si][sj][4 * g + 1], acc[si][sj][4 * g + 2],
                           acc[si][sj][4 * g + 3]};
-            if constexpr (HAS_R) {
+            if constexpr (HAS_R && DTI != DT_I8) {
               float rv[4];
               load4<DTO>(rr, m * a.N + n, ok, rv);
 #pragma unroll
               for (int e = 0; e < 4; ++e) z[e] += rv[e];
             }
-            store4<DTO>(rc, m * a.N + n, ok, act_fn<ACT>(z[0], a.alpha), act_fn<ACT>(z[1], a.alpha),
-                        act_fn<ACT>(z[2], a.alpha), act_fn<ACT>(z[3], a.alpha));
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = out_value<DTI, DTO, ACT>(z[e], a.alpha);
+            store4<DTO>(rc, m * a.N + n, ok, v[0], v[1], v[2], v[3]);
           }
         }
     });
@@ -335,7 +449,7 @@ __global__ __launch_bounds__(512, 1) void gemm16_pp_kernel(GemmArgs a) {
 
 template <int DTI, int DTO>
 inline void launch_gemm_pp(const GemmArgs& a, hipStream_t s) {
-  note_launch("gemm 256x256/2x4 ping-pong");
+  note_launch(DTI == DT_I8 ? "gemm 256x256/2x4 ping-pong int8" : "gemm 256x256/2x4 ping-pong");
   launch_kernel(gemm16_pp_kernel<DTI, DTO>, dim3(a.tiles_m * a.tiles_n), dim3(pp::THREADS), s, a);
 }
 

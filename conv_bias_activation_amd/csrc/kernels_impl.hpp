@@ -316,7 +316,7 @@ inline int launch_gemm_tile(int tile, const GemmArgs& a, hipStream_t s) {
         launch_gemm_t<DTI, DTO, T5>(a, s);
       return 0;
     case 6:
-      if constexpr (DTI == DT_F16 || DTI == DT_BF16) {
+      if constexpr (DTI == DT_F16 || DTI == DT_BF16 || DTI == DT_I8) {
         if (a.vec_a && a.vec_b && a.vec_c) {
           launch_gemm_pp<DTI, DTO>(a, s);
           return 0;

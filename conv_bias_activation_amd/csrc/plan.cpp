@@ -146,7 +146,12 @@ bool plan_halo(ConvPlan* p, const void* x, const void* w) {
     c.PW = p->Wo < bn ? p->Wo : bn;
     c.PH = bn / c.PW < p->Ho ? bn / c.PW : p->Ho;            // rows of one image only
     c.HR = (c.PH - 1) * p->sh + (p->kh - 1) * p->dh + 1;
-    c.HC = (c.PW - 1) * p->sw + (p->kw - 1) * p->dw + 2;     // +1 column of parity shift
+    // a patch whose first input column ow0*sw - pl is odd starts one column
+    // into its (even-aligned) halo: one more column; when every patch starts
+    // on an even column (pl even, and one column block or an even PW*sw) none
+    const uint32_t wblk = (p->Wo + c.PW - 1) / c.PW;
+    const bool even_starts = p->pl % 2 == 0 && (wblk == 1 || (c.PW * p->sw) % 2 == 0);
+    c.HC = (c.PW - 1) * p->sw + (p->kw - 1) * p->dw + (even_starts ? 1 : 2);
     c.HC += c.HC & 1;
     // the kernel's occupancy rule: two workgroups per CU (80 KB of LDS each)
     // when a wave holds at most two fragment sets and two accumulator tiles
@@ -268,10 +273,13 @@ int plan_gemm(const void* A, const void* B, const void* bias, const void* C, int
   p->empty = M == 0 || N == 0;
   int tile = forced_tile();
   if (tile < 0 || tile >= kNumTileConfigs) tile = select_gemm_tile(M, N, K, dti);
-  // the ping-pong kernel takes 16-bit operands with 16-byte aligned rows
-  const bool pp_ok = (dti == kF16 || dti == kBF16) && p->vec_a && p->vec_b && p->vec_c;
-  if (tile == 0 && pp_ok && forced_tile() < 0) tile = 6;
-  if (tile == 6 && !pp_ok) tile = 0;
+  // the ping-pong kernel takes 16-bit or int8 operands with 16-byte aligned
+  // rows; int8 takes it wherever its 256x256 grid still covers every CU
+  const bool pp_ok = (dti == kF16 || dti == kBF16 || dti == kI8) && p->vec_a && p->vec_b && p->vec_c;
+  if (pp_ok && forced_tile() < 0 &&
+      (tile == 0 || (dti == kI8 && ceil_div(M, 256) * ceil_div(N, 256) >= 256)))
+    tile = 6;
+  if (tile == 6 && !pp_ok) tile = dti == kI8 ? 1 : 0;
   if (tile == 7) tile = 2;                              // the halo tile is conv-only
   p->tile = tile;
   p->tiles_m = (uint32_t)ceil_div(M, kTiles[tile].bm);

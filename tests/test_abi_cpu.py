@@ -180,8 +180,11 @@ def test_int8_type_rules():
     assert L.gemm_bias_add_act(P, P, P, P, P, 4, 4, 4, dt, 1, 0.0, NUL) == 2
     c = (ctypes.c_int32 * 2)(1, 1), (ctypes.c_int32 * 4)(1, 1, 1, 1), (ctypes.c_int32 * 2)(1, 1)
     assert L.conv2d_bias_act(P, P, P, P, 1, 3, 8, 8, 4, 3, 3, *c, _dt(I8, I8, I32, I32), 1, NUL) == 2
-    # int8 never takes the 256x256 tile
-    assert ba.gemm_tile_config(4096, 4096, 4096, dt) == 1
+    # int8 takes the 256x256 ping-pong kernel where K and N are multiples of 16
+    # and its grid covers every CU; otherwise a tiled kernel, never the tiled 256x256
+    assert ba.gemm_tile_config(4096, 4096, 4096, dt) == 6
+    assert ba.gemm_tile_config(4096, 4096, 4104, dt) == 1
+    assert ba.gemm_tile_config(1024, 1024, 1024, dt) not in (0, 6)
 
 
 def test_path_selection_defaults_to_fused():

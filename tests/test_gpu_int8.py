@@ -57,7 +57,9 @@ def test_int8_gemm_vs_oracle(ba, shape, to, acts):
 
 @pytest.mark.parametrize("tile", range(8))
 def test_int8_every_tile_config(ba, tile):
-    # ids 6 and 7 fall back to generic tiles for int8
+    # id 6 is the int8 ping-pong kernel only where K and N are multiples of
+    # 16 (none of these shapes): here it, and the conv-only id 7, fall back
+    # to generic tiles
     ba.force_tile_config(tile)
     try:
         for (M, N, K), to in (((300, 520, 200), "i32"), ((513, 264, 1032), "i32"),
@@ -100,3 +102,31 @@ def test_int8_no_bias_and_relu_invariant(ba):
     rcase = _case(190, 264, 333, "i32", "relu", bias=None)
     r = words_of(run_gemm(rcase, inp), "i32").view(np.int32)
     assert np.array_equal(r, np.maximum(z, 0))
+
+
+PP_SHAPES = [(300, 528, 208), (257, 272, 1040), (1, 16, 16), (520, 784, 64), (256, 256, 4096)]
+
+
+@pytest.mark.parametrize("shape", PP_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("to,acts", [("i32", ("none", "relu")), ("f32", ("leaky_relu", "tanh")),
+                                     ("bf16", ("gelu", "relu")), ("f16", ("sigmoid", "tanh"))])
+def test_int8_ping_pong_vs_oracle(ba, shape, to, acts):
+    # the 256x256 ping-pong kernel with int8 operands (transposing byte reads
+    # of B, v_mfma_i32_32x32x32_i8): ragged M and N, K tails inside a 64-deep
+    # k-tile, every output type, with and without a bias
+    M, N, K = shape
+    ba.force_tile_config(6)
+    try:
+        for j, act in enumerate(acts):
+            case = _case(M, N, K, to, act, bias=BIAS if j == 0 else None)
+            inp = wl.gen_gemm(case, seed=120 + j)
+            y = run_gemm(case, inp)
+            assert "ping-pong int8" in ba.last_tile_config(), ba.last_tile_config()
+            ref, floor = gemm_reference(case, inp)
+            if to == "i32":
+                assert np.array_equal(words_of(y, "i32").view(np.int32).astype(np.float64), ref), act
+            else:
+                rep = check(values_of(y, to), ref, floor, case)
+                assert rep["ok"], (act, rep)
+    finally:
+        ba.force_tile_config(-1)

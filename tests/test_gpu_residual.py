@@ -96,6 +96,7 @@ GEMM_CASES = [
     (257, 264, 136, "f16", "f32", "gelu", -1),
     (1024, 640, 256, "f16", "f32", "leaky_relu", 5),       # short reduction, all k-tiles at once
     (512, 768, 192, "bf16", "bf16", "tanh", 6),            # ping-pong kernel
+    (264, 520, 136, "f16", "f32", "gelu", 6),              # ping-pong kernel, 32-bit output in two passes
     (520, 384, 640, "f16", "f16", "sigmoid", 2),
     (200, 136, 72, "f32", "f32", "tanh", -1),
     (33, 260, 1000, "f32", "bf16", "none", -1),
