@@ -22,10 +22,11 @@
 // both by direct loads: one wave instruction moves 64 consecutive floats of
 // one channel's halo, or of the weight block (padding, rows
 // past Co, channels past C and positions outside the image arrive as zeros).
-// Chunks alternate between two LDS arrays, so the next chunk's copy overlaps
-// the multiply of the current one and the multiply's reads carry no wait on
-// it; two buffers and the offset table fit 80 KB, so two workgroups share a
-// CU.  A table of the halo offset of every reduction index of a chunk lets a
+// Chunks alternate between the two halves of one LDS array, so the next
+// chunk's copy overlaps the multiply of the current one and the multiply's
+// reads carry no wait on it; when all C channels form one chunk (a shallow
+// stem: C = 3), that chunk may fill the whole array.  The array and the offset
+// table fit 80 KB, so two workgroups share a CU.  A table of the halo offset of every reduction index of a chunk lets a
 // lane fetch the offsets of 4 steps with one read.
 #pragma once
 
@@ -49,8 +50,10 @@ constexpr int WTN = 64;                     // positions per wave (two 32-wide M
 template <int DTO, int BM>
 __global__ __launch_bounds__(256, 2) void conv32_halo_kernel(HaloArgs a) {
   constexpr int WTM = BM / 2, SM = WTM / 32, SN = halo32::WTN / 32;
-  __shared__ __attribute__((aligned(16))) float s_buf0[halo32::BUF_FLOATS];
-  __shared__ __attribute__((aligned(16))) float s_buf1[halo32::BUF_FLOATS];
+  // the two chunk buffers, contiguous: a reduction that is one chunk may fill both
+  __shared__ __attribute__((aligned(16))) float s_buf[2 * halo32::BUF_FLOATS];
+  float* const s_buf0 = s_buf;
+  float* const s_buf1 = s_buf + halo32::BUF_FLOATS;
   __shared__ __attribute__((aligned(16))) uint32_t s_koff[halo32::KOFF_MAX];
   const ConvGeom& G = a.geom;
 

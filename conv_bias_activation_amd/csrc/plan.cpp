@@ -63,10 +63,11 @@ int pick_tile(const int* order, int n_order, int64_t rows_j, int64_t rows_i, int
 }
 
 // Halo-kernel parameters for an fp32 conv (any filter larger than 1x1, any
-// stride, padding and dilation): the channel chunk is the widest whose halo (HR x HC positions
-// per channel, rounded up to 64) and weight block (bm rows of 2 kpad + 4
-// floats) fit one of two chunk buffers, evened out over the chunks it takes.  Returns false when a single
-// channel does not fit.
+// stride, padding and dilation).  All C channels form one chunk when their
+// halo (HR x HC positions per channel, rounded up to 64) and weight block (bm
+// rows of 2 kpad + 4 floats) fit both chunk buffers together; otherwise the
+// chunk is the widest that fits one buffer, evened out over the chunks it
+// takes.  Returns false when a single channel does not fit.
 bool plan_halo32(ConvPlan* p, const void* x, const void* w) {
   // A 1x1 filter is a strided GEMM: the generic kernel stages exactly the
   // operands it reads and measures faster there.
@@ -83,18 +84,24 @@ bool plan_halo32(ConvPlan* p, const void* x, const void* w) {
   const uint64_t limit = (80 * 1024 - 256 * 4) / 8;          // floats per buffer (two + offset table)
   auto kpad = [&](uint64_t b) { return ((b * T + 1) / 2 + 3) / 4 * 4; };
   auto kstr = [&](uint64_t b) { return 2 * kpad(b) + 4; };
-  auto fits = [&](uint64_t b) {
-    return kpad(b) <= 128 && b * HRCP + (bm * kstr(b) + 63) / 64 * 64 <= limit;
+  auto fits = [&](uint64_t b, uint64_t lim) {
+    return kpad(b) <= 128 && b * HRCP + (bm * kstr(b) + 63) / 64 * 64 <= lim;
   };
-  if (!fits(1)) return false;
-  uint64_t lo = 1, hi = p->C;                                  // largest chunk that fits
-  while (lo < hi) {
-    const uint64_t mid = (lo + hi + 1) / 2;
-    if (fits(mid)) lo = mid;
-    else hi = mid - 1;
+  uint64_t lo;
+  if (fits(p->C, 2 * limit)) {
+    lo = p->C;                     // one chunk: nothing to double-buffer, it may use both buffers
+  } else {
+    if (!fits(1, limit)) return false;
+    lo = 1;
+    uint64_t hi = p->C;            // largest chunk that fits one buffer
+    while (lo < hi) {
+      const uint64_t mid = (lo + hi + 1) / 2;
+      if (fits(mid, limit)) lo = mid;
+      else hi = mid - 1;
+    }
+    const uint64_t n = (p->C + lo - 1) / lo;                  // same chunk count, even split
+    lo = (p->C + n - 1) / n;
   }
-  const uint64_t n = (p->C + lo - 1) / lo;                    // same chunk count, even split
-  lo = (p->C + n - 1) / n;
   p->h_bm = bm;
   p->h_ks = 0;
   p->h_sn = 2;

@@ -331,7 +331,8 @@ def test_conv_halo_path_vs_oracle(ba, shape, types):
 
 
 HALO32_SHAPES = [
-    (2, 3, 20, 22, 64, 7, 7, (2, 2), (3, 3, 3, 3), (1, 1)),       # stem-like: C = 3, two chunks
+    (2, 3, 20, 22, 64, 7, 7, (2, 2), (3, 3, 3, 3), (1, 1)),       # stem-like: C = 3, one chunk in both buffers
+    (1, 3, 30, 40, 64, 11, 11, (2, 2), (5, 5, 5, 5), (1, 1)),     # C = 3 in three chunks (128 k-pairs at most)
     (1, 5, 13, 9, 70, 5, 5, (1, 1), (2, 1, 0, 2), (1, 1)),        # odd C, asymmetric pads, 128-row block
     (2, 40, 9, 11, 33, 1, 3, (1, 2), (0, 0, 1, 1), (1, 3)),       # 1x3 filter, dilation 3, odd chunk K
     (1, 300, 6, 7, 20, 3, 3, (1, 1), (1, 1, 1, 1), (2, 1)),       # many chunks, the last partial
