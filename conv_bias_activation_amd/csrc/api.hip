@@ -134,6 +134,7 @@ int launch_conv_plan(const ConvPlan& p, const void* x, const void* w, const void
     h.kstr = p.h_kstr;
     h.kpad = p.h_kpad;
     h.div_kstr = make_fastdiv(p.h_kstr ? p.h_kstr : 1u);
+    h.groups = p.h_groups;
     rc = launch_conv_halo(p.dti, dto, (int)(p.kh * p.kw), (int)p.h_bm, (int)p.h_ks, (int)p.h_sn, h, s);
     if (rc) return kErrUnsupported;
     return launch_status();

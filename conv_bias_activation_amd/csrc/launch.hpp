@@ -41,6 +41,7 @@ struct HaloArgs {
   uint32_t HR, HC;          // halo rows / columns staged per channel chunk (HC even)
   uint32_t bkc;             // channels per chunk (8, 16, 32 or 64)
   uint32_t co_blocks, w_blocks, h_blocks, blocks;
+  uint32_t groups;          // fp32 kernel: workgroups of a resident-filter grid (0: one patch each)
   bool vec_y;               // Wo % 4 == 0 and y aligned for 4-element stores
   // fp32 kernel only
   uint32_t hrcp;            // halo floats per channel (HR * HC rounded up to 64)

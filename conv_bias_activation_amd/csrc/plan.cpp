@@ -64,10 +64,10 @@ int pick_tile(const int* order, int n_order, int64_t rows_j, int64_t rows_i, int
 
 // Halo-kernel parameters for an fp32 conv (any filter larger than 1x1, any
 // stride, padding and dilation).  All C channels form one chunk when their
-// halo (HR x HC positions per channel, rounded up to 64) and weight block (bm
-// rows of 2 kpad + 4 floats) fit both chunk buffers together; otherwise the
-// chunk is the widest that fits one buffer, evened out over the chunks it
-// takes.  Returns false when a single channel does not fit.
+// halo (HR x HC positions per channel, rounded up to 64) and their weight
+// block (bm rows of 2 kpad + 4 floats) each fit a chunk buffer; otherwise the
+// chunk is the widest whose halo and weights share one buffer, evened out over
+// the chunks it takes.  Returns false when a single channel does not fit.
 bool plan_halo32(ConvPlan* p, const void* x, const void* w) {
   // A 1x1 filter is a strided GEMM: the generic kernel stages exactly the
   // operands it reads and measures faster there.
@@ -81,22 +81,24 @@ bool plan_halo32(ConvPlan* p, const void* x, const void* w) {
   const uint64_t HR = (uint64_t)(PH - 1) * p->sh + (uint64_t)(p->kh - 1) * p->dh + 1;
   const uint64_t HC = (uint64_t)(PW - 1) * p->sw + (uint64_t)(p->kw - 1) * p->dw + 1;
   const uint64_t HRCP = (HR * HC + 63) / 64 * 64;
-  const uint64_t limit = (80 * 1024 - 256 * 4) / 8;          // floats per buffer (two + offset table)
+  // LDS layouts of conv32_halo_kernel (80 KB each, with the 256-entry offset
+  // table): two chunk buffers of 10108 floats, or (resident filter) a
+  // 10240-float weight block and two 4992-float halo buffers
+  const uint64_t limit = 10108, res_w = 10240, res_h = 4992;
   auto kpad = [&](uint64_t b) { return ((b * T + 1) / 2 + 3) / 4 * 4; };
   auto kstr = [&](uint64_t b) { return 2 * kpad(b) + 4; };
-  auto fits = [&](uint64_t b, uint64_t lim) {
-    return kpad(b) <= 128 && b * HRCP + (bm * kstr(b) + 63) / 64 * 64 <= lim;
-  };
+  auto wsz = [&](uint64_t b) { return (bm * kstr(b) + 63) / 64 * 64; };
+  auto fits = [&](uint64_t b) { return kpad(b) <= 128 && b * HRCP + wsz(b) <= limit; };
   uint64_t lo;
-  if (fits(p->C, 2 * limit)) {
-    lo = p->C;                     // one chunk: nothing to double-buffer, it may use both buffers
+  if (kpad(p->C) <= 128 && p->C * HRCP <= limit && wsz(p->C) <= limit) {
+    lo = p->C;                     // one chunk: its halo in one buffer, its weights in the other
   } else {
-    if (!fits(1, limit)) return false;
+    if (!fits(1)) return false;
     lo = 1;
-    uint64_t hi = p->C;            // largest chunk that fits one buffer
+    uint64_t hi = p->C;            // largest chunk whose halo and weights share one buffer
     while (lo < hi) {
       const uint64_t mid = (lo + hi + 1) / 2;
-      if (fits(mid, limit)) lo = mid;
+      if (fits(mid)) lo = mid;
       else hi = mid - 1;
     }
     const uint64_t n = (p->C + lo - 1) / lo;                  // same chunk count, even split
@@ -119,6 +121,17 @@ bool plan_halo32(ConvPlan* p, const void* x, const void* w) {
   const uint64_t blocks = (uint64_t)p->h_co_blocks * p->h_w_blocks * p->h_h_blocks * p->N;
   if (blocks >= (1u << 31)) return false;
   p->h_blocks = (uint32_t)blocks;
+  // Resident filter: with one chunk and one co block every patch multiplies
+  // the same weight block.  When it fits the resident layout's weight block
+  // and a patch's halo its halo buffers, and there are more patches than
+  // workgroup slots (two per CU on 256 CUs), 512 workgroups each stage the
+  // weights once and stream their patches' halos through the two buffers.
+  constexpr uint64_t kSlots = 512;
+  p->h_groups = 0;
+  if (lo == p->C && p->h_co_blocks == 1 && wsz(lo) <= res_w && lo * HRCP <= res_h && blocks > kSlots) {
+    p->h_groups = (uint32_t)kSlots;
+    p->h_blocks = (uint32_t)kSlots;
+  }
   return true;
 }
 
@@ -129,6 +142,7 @@ bool plan_halo(ConvPlan* p, const void* x, const void* w) {
   p->h_hrcp = 0;
   p->h_kpad = 0;
   p->h_kstr = 0;
+  p->h_groups = 0;
   if (p->dti == kF32) return plan_halo32(p, x, w);
   if (p->C % 8 != 0 || p->W % 2 != 0) return false;
   const uint32_t T = p->kh * p->kw;

@@ -360,6 +360,30 @@ def test_conv_halo32_path_vs_oracle(ba, shape, to):
             ba.force_tile_config(-1)
 
 
+RESIDENT_SHAPES = [
+    (1, 3, 300, 130, 64, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1)),       # 600 patches, ragged second column block
+    (2, 4, 600, 70, 40, 5, 5, (2, 1), (2, 2, 2, 2), (1, 2)),        # stride 2 rows, dilation 2 columns
+]
+
+
+@pytest.mark.parametrize("shape", RESIDENT_SHAPES, ids=lambda s: "x".join(map(str, s[:7])))
+@pytest.mark.parametrize("to", ["f32", "bf16"])
+def test_conv_halo32_resident_filter_vs_oracle(ba, shape, to):
+    # one channel chunk, one output-channel block and more patches than the
+    # 512 workgroup slots: each workgroup stages the filter once and streams
+    # two or one patches' halos through its two halo buffers
+    N, C, H, W, Co, kh, kw, st, pd, dl = shape
+    for j, act in enumerate(("tanh", "none")):
+        case = _ccase(N, C, H, W, Co, kh, kw, st, pd, dl, "f32", to, "f32", act)
+        inp = wl.gen_conv(case, seed=81 + j)
+        y = values_of(run_conv(case, inp), to)
+        assert "resident filter" in ba.last_tile_config(), ba.last_tile_config()
+        ref, floor = conv_reference(case, inp)
+        rep = check(y, ref, floor, case)
+        _report(f"halo32 resident {shape} {to} {act}", rep)
+        assert rep["ok"], rep
+
+
 def test_conv_no_bias(ba):
     case = _ccase(2, 8, 10, 10, 16, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1), "bf16", "f32", None, "none")
     inp = wl.gen_conv(case, seed=2)
