@@ -29,8 +29,8 @@
 // output-channel block, a resident-filter grid of 512 workgroups stages the
 // weight block once per workgroup and streams its patches' halos through two
 // halo arrays.  Either layout and the offset table fit 80 KB, so two
-// workgroups share a CU.  A table of the halo offset of every reduction index of a chunk lets a
-// lane fetch the offsets of 4 steps with one read.
+// workgroups share a CU.  A table of the halo offset of every reduction index
+// of a chunk lets a lane fetch the offsets of 4 steps with one read.
 #pragma once
 
 #include <utility>
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256, 2) void conv32_halo_kernel(HaloArgs a) {
   const uint32_t HR = a.HR, HC = a.HC, HRC = a.hrcp;       // halo rows, columns, floats per channel
   const uint32_t T = G.kh * G.kw, KSTR = a.kstr, BKC = a.bkc;
   const uint32_t KPAD = a.kpad;                             // k-pairs per chunk, multiple of 4
-  const uint32_t wofs = BKC * HRC;                          // weights follow the halo (one patch)
+  const uint32_t wofs = BKC * HRC;                          // several chunks: weights follow the halo
   const uint32_t nchunks = (G.C + BKC - 1) / BKC;
 
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, a.x_bytes);
