@@ -146,7 +146,34 @@ __global__ __launch_bounds__(512, 1) void gemm16_pp_kernel(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         idx[si * 16 + r] = n0 + wn * 64 + si * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-    load_bias_vec<32>(a.bias, a.bias_bytes, a.bias_dt, idx, a.N, bv);
+    // 4 consecutive columns per (si, r / 4), all in or all out (N % 8 == 0):
+    // one 16-byte (32-bit bias) or 8-byte (16-bit bias) load each when the
+    // bias is aligned for it, so the 8 loads are in flight together
+    const int bbytes = a.bias_dt == DT_F32 || a.bias_dt == DT_I32 ? 4 : 2;
+    if (a.bias_dt >= 0 && (reinterpret_cast<uintptr_t>(a.bias) & (4u * bbytes - 1u)) == 0) {
+      const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.bias, a.bias_bytes);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const uint32_t n = idx[4 * q];
+        const bool ok = n < a.N;
+        if (bbytes == 4) {
+          const u32x4 v = ld_b128(rb, ok ? n * 4u : kOOB);
+          bv[4 * q + 0] = __uint_as_float(v.x);
+          bv[4 * q + 1] = __uint_as_float(v.y);
+          bv[4 * q + 2] = __uint_as_float(v.z);
+          bv[4 * q + 3] = __uint_as_float(v.w);
+        } else {
+          const u32x2 v = ld_b64(rb, ok ? n * 2u : kOOB);
+          const bool f16 = a.bias_dt == DT_F16;
+          bv[4 * q + 0] = f16 ? widen<DT_F16>(v.x & 0xffffu) : widen<DT_BF16>(v.x & 0xffffu);
+          bv[4 * q + 1] = f16 ? widen<DT_F16>(v.x >> 16) : widen<DT_BF16>(v.x >> 16);
+          bv[4 * q + 2] = f16 ? widen<DT_F16>(v.y & 0xffffu) : widen<DT_BF16>(v.y & 0xffffu);
+          bv[4 * q + 3] = f16 ? widen<DT_F16>(v.y >> 16) : widen<DT_BF16>(v.y >> 16);
+        }
+      }
+    } else {
+      load_bias_vec<32>(a.bias, a.bias_bytes, a.bias_dt, idx, a.N, bv);
+    }
 #pragma unroll
     for (int si = 0; si < 2; ++si) {
       f32x16 b;

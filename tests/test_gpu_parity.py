@@ -84,6 +84,41 @@ def test_gemm_every_tile_config(ba, tile):
         ba.force_tile_config(-1)
 
 
+@pytest.mark.parametrize("tb", ["f32", "bf16"])
+def test_pp_bias_vector_and_element_loads_agree(ba, tb):
+    # The ping-pong kernel reads each lane's bias as runs of 4 columns (one
+    # 16- or 8-byte load each) when the bias is aligned for it, and element by
+    # element otherwise: bias one element into its buffer gives the same bits
+    M, N, K = 300, 520, 200
+    case = _gcase(M, N, K, "bf16", "bf16", tb, "gelu")
+    inp = wl.gen_gemm(case, seed=23)
+    ref, floor = gemm_reference(case, inp)
+    A, _ = to_dev(inp["A"].reshape(M, K), "bf16")
+    B, _ = to_dev(inp["B"].reshape(K, N), "bf16")
+    bias0, _ = to_dev(inp["bias"], tb)
+    outs = []
+    ba.force_tile_config(6)
+    try:
+        for off in (0, 1):
+            if off:
+                buf = torch.empty(N + off, dtype=bias0.dtype, device="cuda")
+                bias = buf[off:]
+                bias.copy_(bias0)
+            else:
+                bias = bias0
+            C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            ba.gemm_bias_act(A, B, bias, C, "gelu", 0.0)
+            torch.cuda.synchronize()
+            assert "ping-pong" in ba.last_tile_config()
+            outs.append(C)
+    finally:
+        ba.force_tile_config(-1)
+    rep = check(values_of(outs[0], "bf16"), ref, floor, case)
+    _report(f"pp bias {tb}", rep)
+    assert rep["ok"], rep
+    assert np.array_equal(words_of(outs[0], "bf16"), words_of(outs[1], "bf16"))
+
+
 @pytest.mark.parametrize("ti", ["bf16", "f16", "f32"])
 def test_gemm_short_reduction_all_k_tiles(ba, ti):
     # the 64x64 tile loads a reduction of at most four k-tiles at once; cover
