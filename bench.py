@@ -19,7 +19,9 @@ Besides the headline, the line carries:
                 single steps after a 512 MiB cache flush; `tuned_path` is the
                 path the library's own tuner records for the workload;
                 `cpu_oracle` the fp64 oracle's rate on a bounded sample of
-                it, on all host threads (and on one, for the small workloads).
+                it, on all host threads (and on one, for the small workloads);
+  path_rule     the static fused-vs-two-kernel rule's case (the 4096^3 GEMM
+                with a misaligned output): fused, two-kernel and auto calls.
 """
 from __future__ import annotations
 
@@ -38,14 +40,27 @@ sys.path.insert(0, ROOT)
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3, "i8": 5033.2}
 PEAK_HBM_GBS = 8000.0
 
-# Sources that define the headline kernel; the HBM-traffic record in profiles/
-# carries their hash and is reported only while they are unchanged.
-KERNEL_SOURCES = ["gemm_pp.hpp", "epilogue.hpp", "device_common.hpp", "gemm_args.hpp", "tile_map.hpp"]
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gemm_relu_4096_bf16_hbm_traffic.json")
+# Sources that define each kernel; a committed HBM-traffic record carries
+# their hash and is reported only while they are unchanged.
+KERNEL_SOURCES = {
+    "gemm16_pp_kernel": ["gemm_pp.hpp", "epilogue.hpp", "device_common.hpp", "gemm_args.hpp",
+                         "tile_map.hpp"],
+    "conv16_halo_kernel": ["conv_halo.hpp", "device_common.hpp", "mfma_core.hpp"],
+    "conv32_halo_kernel": ["conv_halo32.hpp", "device_common.hpp", "mfma_core.hpp"],
+    "gemm_bias_act_kernel": ["kernels_impl.hpp", "mfma_core.hpp", "epilogue.hpp",
+                             "device_common.hpp", "tile_map.hpp"],
+    "conv_bias_act_kernel": ["kernels_impl.hpp", "mfma_core.hpp", "epilogue.hpp",
+                             "device_common.hpp", "tile_map.hpp"],
+}
+TRAFFIC_RECORDS = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+TWO_KERNEL = "two-kernel: "
 
 
 def kernel_name(desc: str) -> str:
-    """Kernel function behind a last_tile_config() description."""
+    """Kernel function behind a last_tile_config() description (the first
+    kernel of a two-kernel call)."""
+    if desc.startswith(TWO_KERNEL):
+        desc = desc[len(TWO_KERNEL):]
     if "ping-pong" in desc:
         return "gemm16_pp_kernel"
     if desc.startswith("conv-halo fp32"):
@@ -55,27 +70,44 @@ def kernel_name(desc: str) -> str:
     return "gemm_bias_act_kernel" if desc.startswith("gemm") else "conv_bias_act_kernel"
 
 
-def kernel_fingerprint() -> str:
+def kernel_fingerprint(kernel: str = "gemm16_pp_kernel") -> str:
     import hashlib
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "conv_bias_activation_amd", "csrc", name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch from the committed counter record (FETCH_SIZE and
-    WRITE_SIZE scaled by a plain copy of known size), or None if absent or
-    taken on other kernel sources."""
+def measured_traffic(workload: str, tile: str, path: str):
+    """HBM bytes per launch from the committed counter records (FETCH_SIZE and
+    WRITE_SIZE scaled by a plain copy of known size) for this workload, kernel
+    and tile (its last_tile_config() description) and path, or None if there
+    is no such record or it was taken on other kernel sources."""
     try:
-        with open(TRAFFIC_RECORD) as f:
-            rec = json.load(f)
+        with open(TRAFFIC_RECORDS) as f:
+            recs = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("workload") != workload or rec.get("kernel_sources_sha256") != kernel_fingerprint():
-        return None
-    return rec.get("bytes_per_launch")
+    kernel = kernel_name(tile)
+    for rec in recs:
+        if (rec.get("workload") == workload and rec.get("tile") == tile and
+                rec.get("path", "fused") == path and rec.get("kernel") == kernel and
+                rec.get("kernel_sources_sha256") == kernel_fingerprint(kernel)):
+            return rec.get("bytes_per_launch")
+    return None
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def _parse():
@@ -92,7 +124,8 @@ def _parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle sample time")
     ap.add_argument("--tile", type=int, default=-1, help="force a tile config (tuning)")
-    ap.add_argument("--fingerprint", action="store_true", help="print the headline kernel's source hash")
+    ap.add_argument("--fingerprint", default=None, metavar="KERNEL",
+                    help="print the source hash of a kernel (e.g. gemm16_pp_kernel) and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a device copy of 256 MiB (read 256 MiB + write 256 MiB) --steps "
                          "times; its FETCH_SIZE / WRITE_SIZE counters scale the kernel's counters "
@@ -294,6 +327,38 @@ def measure_case(case, path, min_ms=200.0):
     return out
 
 
+def path_rule_case():
+    """The static fused-vs-two-kernel rule's case: the 4096^3 bf16 GEMM + ReLU
+    with C two bytes off its allocation (not aligned for 4-element accesses).
+    Device time per call (graph replays) of the fused call, the two-kernel
+    call and the auto call (which applies the rule), with the kernel each
+    launched."""
+    import torch
+    import conv_bias_activation_amd as ba
+    import workloads as wl
+    case = wl.CASES["gemm_relu_4096_bf16"]
+    inp = wl.gen_gemm(case, 0)
+    A = to_device(inp["A"].reshape(case.M, case.K), "bf16")
+    B = to_device(inp["B"].reshape(case.K, case.N), "bf16")
+    bias = to_device(inp["bias"], "f32")
+    buf = torch.empty(case.M * case.N + 1, dtype=torch.bfloat16, device="cuda")
+    C = buf[1:].view(case.M, case.N)
+    ws = torch.empty(case.M * case.N, dtype=torch.float32, device="cuda")
+    calls = {"fused": lambda: ba.gemm_bias_act(A, B, bias, C, "relu"),
+             "2k": lambda: ba.gemm_bias_act_2k(A, B, bias, C, "relu", workspace=ws),
+             "auto": lambda: ba.gemm_bias_act_auto(A, B, bias, C, "relu", workspace=ws)}
+    out = {"workload": case.name + ", C misaligned by 2 bytes",
+           "static_path": ba.gemm_static_path(A, B, bias, C, "relu", workspace=ws)}
+    for name, step in calls.items():
+        ms, _ = time_steps(step, 20, 5)
+        out[name] = {"tile": ba.last_tile_config()}
+        R, med, mn = graph_trials(step, ms)
+        out[name].update({"graph_median_ms": round(med, 5), "graph_min_ms": round(mn, 5),
+                          **_rates(case, med)})
+    del buf, ws
+    return out
+
+
 # workloads whose oracle is also timed on one thread (the small and conv
 # configurations; the large GEMMs only with all threads)
 ONE_THREAD_WORKLOADS = ("gemm_leaky_1024x640x256_f16", "conv3x3_tanh_8x64x56_f16",
@@ -385,13 +450,13 @@ def cpu_baseline(case, target_s):
             "kind": "oracle",
             "sample": f"{rows} of {case.M} output rows of {case.name} (full K and N), fp64, "
                       f"{dt:.1f} s wall; inputs decoded beforehand",
-            "host_cpus": os.cpu_count()}
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
 
 
 def main():
     args = _parse()
     if args.fingerprint:
-        print(kernel_fingerprint())
+        print(kernel_fingerprint(args.fingerprint))
         return
     if args.gpus != 1:
         print(json.dumps({"error": f"--gpus {args.gpus}: this benchmark runs on exactly one GPU; "
@@ -447,7 +512,8 @@ def main():
         "config": cfg,
         "frac_of_peak": round(tflops / peak, 4),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(tflops / peak, 4), "traffic": measured_traffic(case.name),
+                     "frac": round(tflops / peak, 4),
+                     "traffic": measured_traffic(case.name, cfg["tile"], args.path),
                      "kernel": kernel_name(cfg["tile"]),
                      "per_launch_flops": case.flops,
                      "mean_launch_ms": round(ms, 5)},
@@ -479,6 +545,10 @@ def main():
             others[name] = entry
             torch.cuda.empty_cache()
         line["others"] = others
+        try:
+            line["path_rule"] = path_rule_case()
+        except Exception as e:  # report, never hide
+            line["path_rule"] = {"error": repr(e)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     print(json.dumps(line), flush=True)

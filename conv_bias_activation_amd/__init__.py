@@ -26,6 +26,9 @@ from ._binding import (  # noqa: F401
     gemm_bias_act_auto,
     conv2d_bias_act_auto,
     gemm_path,
+    gemm_static_path,
+    set_gemm_path,
+    set_conv_path,
     conv_path,
     tune_gemm,
     tune_conv,

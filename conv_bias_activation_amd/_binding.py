@@ -66,6 +66,16 @@ def _load():
     l.biasact_gemm_path.restype = ctypes.c_int
     l.biasact_conv_path.argtypes = [i64] * 7 + [i32p, i32p, i32p, u32, ctypes.c_int]
     l.biasact_conv_path.restype = ctypes.c_int
+    l.biasact_set_gemm_path.argtypes = [i64, i64, i64, u32, ctypes.c_int, ctypes.c_int]
+    l.biasact_set_gemm_path.restype = ctypes.c_int
+    l.biasact_set_conv_path.argtypes = [i64] * 7 + [i32p, i32p, i32p, u32, ctypes.c_int, ctypes.c_int]
+    l.biasact_set_conv_path.restype = ctypes.c_int
+    l.biasact_gemm_static_path.argtypes = [vp, vp, vp, vp, i64, i64, i64, u32, ctypes.c_int, vp,
+                                           ctypes.c_size_t]
+    l.biasact_gemm_static_path.restype = ctypes.c_int
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    l.conv2d_bias_act_out_dims.argtypes = [i64] * 4 + [i32p, i32p, i32p, i64p, i64p]
+    l.conv2d_bias_act_out_dims.restype = ctypes.c_int
     l.biasact_tune_gemm.argtypes = ([vp, vp, vp, vp, i64, i64, i64, u32, ctypes.c_int, ctypes.c_float,
                                      vp, ctypes.c_size_t, ctypes.c_int, vp, ip])
     l.biasact_tune_gemm.restype = ctypes.c_int
@@ -247,15 +257,15 @@ def gemm_bias_add_act_2k(A, B, bias, R, C, act="none", alpha: float = 0.0, works
 # -- conv2d ----------------------------------------------------------------
 
 def conv_out_hw(H, W, kh, kw, strides, pads, dilations):
-    """Output size with zero padding, floor rounding (None when empty)."""
-    sh, sw = strides
-    pt, pb, pl, pr = pads
-    dh, dw = dilations
-    span_h = H + pt + pb - dh * (kh - 1) - 1
-    span_w = W + pl + pr - dw * (kw - 1) - 1
-    if span_h < 0 or span_w < 0:
+    """(Ho, Wo) from the library's own output-size rule (None when the
+    output would be empty or the attributes are invalid)."""
+    ho, wo = ctypes.c_int64(0), ctypes.c_int64(0)
+    rc = lib.conv2d_bias_act_out_dims(int(H), int(W), int(kh), int(kw), _i32x(strides, 2, "strides"),
+                                      _i32x(pads, 4, "pads"), _i32x(dilations, 2, "dilations"),
+                                      ctypes.byref(ho), ctypes.byref(wo))
+    if rc != BA_OK:
         return None
-    return span_h // sh + 1, span_w // sw + 1
+    return ho.value, wo.value
 
 
 def _conv_args(x, w, bias, y, strides, pads, dilations):
@@ -350,6 +360,29 @@ def conv_path(N, C, H, W, Co, kh, kw, strides, pads, dilations, dtypes: int, act
     return PATH_NAMES[rc]
 
 
+def set_gemm_path(M, N, K, dtypes: int, act="none", path="fused"):
+    """Record the path for a GEMM problem (None forgets the record)."""
+    code = -1 if path is None else {v: k for k, v in PATH_NAMES.items()}[path]
+    _check(lib.biasact_set_gemm_path(M, N, K, dtypes, _act(act), code), "set_gemm_path")
+
+
+def set_conv_path(N, C, H, W, Co, kh, kw, strides, pads, dilations, dtypes: int, act="tanh",
+                  path="fused"):
+    code = -1 if path is None else {v: k for k, v in PATH_NAMES.items()}[path]
+    _check(lib.biasact_set_conv_path(N, C, H, W, Co, kh, kw, _i32x(strides, 2, "strides"),
+                                     _i32x(pads, 4, "pads"), _i32x(dilations, 2, "dilations"),
+                                     dtypes, _act(act), code), "set_conv_path")
+
+
+def gemm_static_path(A, B, bias, C, act="none", workspace=None) -> str:
+    """The library's static choice for these buffers (no launch)."""
+    M, N, K, dt = _gemm_args(A, B, bias, C)
+    ws, nbytes = _ws(workspace)
+    return PATH_NAMES[int(lib.biasact_gemm_static_path(_dev(A, "A"), _dev(B, "B"), _dev(bias, "bias"),
+                                                        _dev(C, "C"), M, N, K, dt, _act(act), ws,
+                                                        nbytes))]
+
+
 def _ws(workspace):
     if workspace is None:
         return None, 0
@@ -384,8 +417,8 @@ def tune_conv(x, w, bias, y, strides=(1, 1), pads=(0, 0, 0, 0), dilations=(1, 1)
 
 
 def gemm_bias_act_auto(A, B, bias, C, act="none", alpha: float = 0.0, workspace=None, stream=None):
-    """The recorded path for this problem (fused unless tuning chose the
-    two-kernel path and a workspace is given)."""
+    """The recorded path for this problem, else the library's static rule
+    (the two-kernel path only with a large enough workspace)."""
     M, N, K, dt = _gemm_args(A, B, bias, C)
     ws, nbytes = _ws(workspace)
     rc = lib.gemm_bias_act_auto(_dev(A, "A"), _dev(B, "B"), _dev(bias, "bias"), _dev(C, "C"), M, N,

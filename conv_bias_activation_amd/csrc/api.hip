@@ -165,6 +165,17 @@ int gemm_impl(const void* A, const void* B, const void* bias, const void* R, voi
   return launch_gemm_plan(p, A, B, bias, C, R, p.dto, act, alpha, stream);
 }
 
+// dtypes with the output code replaced by fp32 (kernel 1 of the two-kernel
+// path writes the fp32 workspace)
+uint32_t with_f32_out(uint32_t dtypes) { return (dtypes & 0x00ffffffu) | (BA_F32 << 24); }
+
+// The description of the call's first kernel, marked as the two-kernel path.
+void note_two_kernel() {
+  char first[kLaunchDescBytes];
+  snprintf(first, sizeof(first), "%s", t_launch_desc);
+  note_launch("two-kernel: %s", first);
+}
+
 int gemm_2k_impl(const void* A, const void* B, const void* bias, const void* R, void* C, int64_t M,
                  int64_t N, int64_t K, uint32_t dtypes, int act, float alpha, void* workspace,
                  size_t workspace_bytes, hipStream_t stream) {
@@ -175,9 +186,15 @@ int gemm_2k_impl(const void* A, const void* B, const void* bias, const void* R, 
   const uint64_t need = (uint64_t)M * (uint64_t)N * 4u;
   if (need >= (1ull << 31)) return kErrUnsupported;
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % 16) != 0) return kErrInvalid;
-  // kernel 1: same main loop, fp32 pre-activation (A.B + bias) to the workspace
-  rc = launch_gemm_plan(p, A, B, bias, workspace, nullptr, DT_F32, BA_ACT_NONE, 0.0f, stream);
+  // kernel 1: the contraction, fp32 pre-activation (A.B + bias) to the
+  // workspace; its tile is planned for the buffer it writes (the output's and
+  // the residual's alignment only concern kernel 2)
+  GemmPlan p1;
+  rc = plan_gemm(A, B, bias, workspace, M, N, K, with_f32_out(dtypes), BA_ACT_NONE, &p1);
   if (rc) return rc;
+  rc = launch_gemm_plan(p1, A, B, bias, workspace, nullptr, DT_F32, BA_ACT_NONE, 0.0f, stream);
+  if (rc) return rc;
+  note_two_kernel();
   // kernel 2: residual, activation and cast
   return launch_second_kernel(p.dto, workspace, C, need / 4u, act, alpha, R, stream);
 }
@@ -207,6 +224,7 @@ int conv_2k_impl(const void* x, const void* w, const void* bias, const void* r, 
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % 16) != 0) return kErrInvalid;
   rc = launch_conv_plan(p, x, w, bias, workspace, nullptr, DT_F32, BA_ACT_NONE, stream);
   if (rc) return rc;
+  note_two_kernel();
   return launch_second_kernel(p.dto, workspace, y, need / 4u, act, 0.0f, r, stream);
 }
 
@@ -235,7 +253,37 @@ int lookup_path(const std::vector<int64_t>& key) {
 
 void record_path(const std::vector<int64_t>& key, int path) {
   std::lock_guard<std::mutex> g(g_path_mu);
-  g_paths[key] = path;
+  if (path < 0) g_paths.erase(key);
+  else g_paths[key] = path;
+}
+
+// The static choice for a GEMM nobody has tuned.  The fused kernel's
+// epilogue must leave from the registers that hold the accumulators; the
+// 256x256 ping-pong kernel's epilogue (whole 16-byte rows through LDS, or
+// 4-wide stores) needs an output (and residual) aligned for 4-element
+// accesses, and without it the fused call drops to a slower main loop.  The
+// two-kernel path keeps the ping-pong main loop, writing its own aligned fp32
+// workspace, and moves the misaligned accesses into the element-wise second
+// kernel: chosen when that is the case and a large enough workspace is given.
+int static_gemm_path(const void* A, const void* B, const void* bias, const void* C, int64_t M,
+                     int64_t N, int64_t K, uint32_t dtypes, int act, const void* workspace,
+                     size_t workspace_bytes) {
+  GemmPlan pf, p1;
+  if (plan_gemm(A, B, bias, C, M, N, K, dtypes, act, &pf) || pf.empty) return BA_PATH_FUSED;
+  if (pf.tile == 6 || pf.dti == DT_I8) return BA_PATH_FUSED;
+  if (!workspace || workspace_bytes < (uint64_t)M * (uint64_t)N * 4u ||
+      ((uintptr_t)workspace % 16) != 0)
+    return BA_PATH_FUSED;
+  if (plan_gemm(A, B, bias, workspace, M, N, K, with_f32_out(dtypes), BA_ACT_NONE, &p1))
+    return BA_PATH_FUSED;
+  return p1.tile == 6 ? BA_PATH_TWO_KERNEL : BA_PATH_FUSED;
+}
+
+// The recorded path, or -1.
+int recorded_path(const std::vector<int64_t>& key) {
+  std::lock_guard<std::mutex> g(g_path_mu);
+  auto it = g_paths.find(key);
+  return it == g_paths.end() ? -1 : it->second;
 }
 
 // Mean milliseconds per call of `run` over `reps` calls on `stream`, after
@@ -377,6 +425,33 @@ int biasact_conv_path(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Co, in
   return lookup_path(conv_key(N, C, H, W, Co, kh, kw, strides, pads, dilations, dtypes, act));
 }
 
+int biasact_set_gemm_path(int64_t M, int64_t N, int64_t K, uint32_t dtypes, int act, int path) {
+  if (path < -1 || path > BA_PATH_TWO_KERNEL) return kErrInvalid;
+  record_path(gemm_key(M, N, K, dtypes, act), path);
+  return kOk;
+}
+
+int biasact_set_conv_path(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Co, int64_t kh,
+                          int64_t kw, const int32_t strides[2], const int32_t pads[4],
+                          const int32_t dilations[2], uint32_t dtypes, int act, int path) {
+  if (!strides || !pads || !dilations) return kErrInvalid;
+  if (path < -1 || path > BA_PATH_TWO_KERNEL) return kErrInvalid;
+  record_path(conv_key(N, C, H, W, Co, kh, kw, strides, pads, dilations, dtypes, act), path);
+  return kOk;
+}
+
+int biasact_gemm_static_path(const void* A, const void* B, const void* bias, const void* C,
+                             int64_t M, int64_t N, int64_t K, uint32_t dtypes, int act,
+                             const void* workspace, size_t workspace_bytes) {
+  return static_gemm_path(A, B, bias, C, M, N, K, dtypes, act, workspace, workspace_bytes);
+}
+
+int conv2d_bias_act_out_dims(int64_t H, int64_t W, int64_t kh, int64_t kw, const int32_t strides[2],
+                             const int32_t pads[4], const int32_t dilations[2], int64_t* Ho,
+                             int64_t* Wo) {
+  return conv_out_dims(H, W, kh, kw, strides, pads, dilations, Ho, Wo);
+}
+
 int biasact_tune_gemm(const void* A, const void* B, const void* bias, void* C, int64_t M,
                       int64_t N, int64_t K, uint32_t dtypes, int act, float alpha, void* workspace,
                       size_t workspace_bytes, int reps, hipStream_t stream, int* path) {
@@ -422,7 +497,9 @@ int biasact_tune_conv(const void* x, const void* w, const void* bias, void* y, i
 int gemm_bias_act_auto(const void* A, const void* B, const void* bias, void* C, int64_t M,
                        int64_t N, int64_t K, uint32_t dtypes, int act, float alpha, void* workspace,
                        size_t workspace_bytes, hipStream_t stream) {
-  const int path = lookup_path(gemm_key(M, N, K, dtypes, act));
+  int path = recorded_path(gemm_key(M, N, K, dtypes, act));
+  if (path < 0)
+    path = static_gemm_path(A, B, bias, C, M, N, K, dtypes, act, workspace, workspace_bytes);
   if (path == BA_PATH_TWO_KERNEL && workspace && workspace_bytes >= (uint64_t)M * N * 4u)
     return gemm_2k_impl(A, B, bias, nullptr, C, M, N, K, dtypes, act, alpha, workspace,
                         workspace_bytes, stream);

@@ -138,14 +138,30 @@ __device__ __forceinline__ float tanh_f32(float x) {
   return __builtin_copysignf(r, x);
 }
 
-// Sigmoid(z) = 1 / (1 + e^-z), with e^-z = 2^(-z log2 e) from the hardware
-// base-2 exponential and the hardware reciprocal: for z -> -inf the
-// exponential overflows to +inf and the reciprocal gives 0; for z -> +inf it
-// gives 1.  Each step is within about an ulp, so the result is within a few
-// fp32 ulps of the definition.
+// 2^s in fp32, subnormal results included.  The hardware base-2 exponential
+// returns 0 for results below the smallest normal (2^-126), which bf16
+// outputs would see as an error of up to 2^7 of their subnormal spacing;
+// there the exponent is raised by 64 and the result scaled back by an exact
+// power of two, whose multiply rounds once onto the subnormal grid.
+__device__ __forceinline__ float exp2_f32(float s) {
+#pragma clang fp contract(off)
+  const bool tiny = s < -126.0f;
+  const float r = __builtin_amdgcn_exp2f(tiny ? s + 64.0f : s);
+  return tiny ? r * 0x1p-64f : r;
+}
+
+// Sigmoid(z) = 1 / (1 + e^-z), evaluated as s(|z|) = 1 / (1 + u) with
+// u = e^-|z| in (0, 1] (the hardware base-2 exponential and reciprocal), and
+// s(z) = u * s(|z|) = e^z / (1 + e^z) for negative z: nothing overflows, and
+// far-negative results that fall below the fp32 normal range keep their
+// subnormal value.  Each step is within about an ulp, so the result is
+// within a few fp32 ulps of the definition (plus the rounding of the
+// exponent's argument, |z| * 2^-24 relative).
 __device__ __forceinline__ float sigmoid_f32(float z) {
 #pragma clang fp contract(off)
-  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.442695041f));
+  const float u = exp2_f32(__builtin_fabsf(z) * -1.442695041f);
+  const float r = __builtin_amdgcn_rcpf(1.0f + u);
+  return z < 0.0f ? u * r : r;
 }
 
 // erfc(x) for x >= 0 as t * e^(-x^2 + P(t)), t = 1 / (1 + x/2), P of degree 9:
@@ -169,7 +185,12 @@ __device__ __forceinline__ float erfc_f32(float x) {
   p = __builtin_fmaf(p, t, 9.986327887e-01f);
   p = __builtin_fmaf(p, t, -1.265447974e+00f);
   const float e = __builtin_fmaf(-ax, ax, p);
-  const float r = t * __builtin_amdgcn_exp2f(e * 1.442695041f);
+  // below 2^-126 the product is formed at 2^64 times its size, then scaled
+  // back exactly (see exp2_f32): one rounding onto the subnormal grid
+  const float s = e * 1.442695041f;
+  const bool tiny = s < -126.0f;
+  float r = t * __builtin_amdgcn_exp2f(tiny ? s + 64.0f : s);
+  r = tiny ? r * 0x1p-64f : r;
   return x < 0.0f ? 2.0f - r : r;
 }
 

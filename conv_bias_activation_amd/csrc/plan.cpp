@@ -308,6 +308,24 @@ int plan_gemm(const void* A, const void* B, const void* bias, const void* C, int
   return kOk;
 }
 
+int conv_out_dims(int64_t H, int64_t W, int64_t kh, int64_t kw, const int32_t* strides,
+                  const int32_t* pads, const int32_t* dilations, int64_t* Ho, int64_t* Wo) {
+  if (!strides || !pads || !dilations || !Ho || !Wo) return kErrInvalid;
+  if (H <= 0 || W <= 0 || kh <= 0 || kw <= 0) return kErrInvalid;
+  if (H >= kMaxBytes || W >= kMaxBytes || kh >= kMaxBytes || kw >= kMaxBytes) return kErrUnsupported;
+  const int32_t sh = strides[0], sw = strides[1], dh = dilations[0], dw = dilations[1];
+  const int32_t pt = pads[0], pb = pads[1], pl = pads[2], pr = pads[3];
+  if (sh < 1 || sw < 1 || dh < 1 || dw < 1) return kErrInvalid;
+  if (pt < 0 || pb < 0 || pl < 0 || pr < 0) return kErrInvalid;
+  // floor((in + pad_lo + pad_hi - dil * (k - 1) - 1) / stride) + 1 per axis
+  const int64_t span_h = H + pt + pb - (int64_t)dh * (kh - 1) - 1;
+  const int64_t span_w = W + pl + pr - (int64_t)dw * (kw - 1) - 1;
+  if (span_h < 0 || span_w < 0) return kErrInvalid;  // empty output
+  *Ho = span_h / sh + 1;
+  *Wo = span_w / sw + 1;
+  return kOk;
+}
+
 int plan_conv(const void* x, const void* w, const void* bias, const void* y, int64_t N, int64_t C,
               int64_t H, int64_t W, int64_t Co, int64_t kh, int64_t kw, const int32_t* strides,
               const int32_t* pads, const int32_t* dilations, uint32_t dtypes, int act,
@@ -318,12 +336,9 @@ int plan_conv(const void* x, const void* w, const void* bias, const void* y, int
   if (act == 2) return kErrUnsupported;                 // no alpha argument on this entry point
   const int32_t sh = strides[0], sw = strides[1], dh = dilations[0], dw = dilations[1];
   const int32_t pt = pads[0], pb = pads[1], pl = pads[2], pr = pads[3];
-  if (sh < 1 || sw < 1 || dh < 1 || dw < 1) return kErrInvalid;
-  if (pt < 0 || pb < 0 || pl < 0 || pr < 0) return kErrInvalid;
-  const int64_t span_h = H + pt + pb - (int64_t)dh * (kh - 1) - 1;
-  const int64_t span_w = W + pl + pr - (int64_t)dw * (kw - 1) - 1;
-  if (span_h < 0 || span_w < 0) return kErrInvalid;  // empty output
-  const int64_t Ho = span_h / sh + 1, Wo = span_w / sw + 1;
+  int64_t Ho, Wo;
+  const int dims_rc = conv_out_dims(H, W, kh, kw, strides, pads, dilations, &Ho, &Wo);
+  if (dims_rc) return dims_rc;
   int dti, dto, dtb;
   int rc = decode_dtypes(dtypes, bias != nullptr, &dti, &dto, &dtb);
   if (rc) return rc;

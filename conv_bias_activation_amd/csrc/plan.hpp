@@ -59,6 +59,11 @@ int plan_conv(const void* x, const void* w, const void* bias, const void* y, int
               const int32_t* pads, const int32_t* dilations, uint32_t dtypes, int act,
               ConvPlan* p, const void* r = nullptr);
 
+// Output size of conv2d with zero padding (floor rounding); kErrInvalid for
+// bad strides / pads / dilations or an empty output.
+int conv_out_dims(int64_t H, int64_t W, int64_t kh, int64_t kw, const int32_t* strides,
+                  const int32_t* pads, const int32_t* dilations, int64_t* Ho, int64_t* Wo);
+
 int select_gemm_tile(int64_t M, int64_t N, int64_t K, int dti);
 int select_conv_tile(int64_t N, int64_t Co, int64_t Ho, int64_t Wo, int64_t K, int dti);
 

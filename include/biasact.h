@@ -113,12 +113,29 @@ int conv2d_bias_act(const void* x, const void* w, const void* bias, void* y,
                     const int32_t pads[4], const int32_t dilations[2],
                     uint32_t dtypes, int act, hipStream_t stream);
 
-/* Two-kernel variants (the ablation of the fused path): kernel 1 runs the same
- * main loop and stores the fp32 pre-activation (A.B + bias, or conv + bias) to
- * `workspace` ([M,N], or NCHW for conv); kernel 2 reads it back and applies the
- * activation and the output cast.  Results are bitwise identical to the fused
- * entry points.  `workspace` is a caller-owned device buffer of at least
- * *_workspace_size() bytes (BA_ERR_INVALID otherwise). */
+/* Output size of conv2d_bias_act for an H x W input and a kh x kw filter
+ * (the output-size formula of "PyAsc與Ascend-C算子開發實戰", section 3.1,
+ * with dilation): Ho = floor((H + top + bottom - dh*(kh-1) - 1) / sh) + 1,
+ * likewise Wo.  strides, pads, dilations as for conv2d_bias_act (HOST int32
+ * pointers); *Ho and *Wo are host pointers written on success.  Returns
+ * BA_ERR_INVALID for null pointers, H, W, kh or kw < 1, a stride or dilation
+ * < 1, a pad < 0 or an empty output; BA_ERR_UNSUPPORTED for a dimension of
+ * 2^31 or more. */
+int conv2d_bias_act_out_dims(int64_t H, int64_t W, int64_t kh, int64_t kw,
+                             const int32_t strides[2], const int32_t pads[4],
+                             const int32_t dilations[2], int64_t* Ho, int64_t* Wo);
+
+/* Two-kernel variants (the ablation of the fused path): kernel 1 runs the
+ * contraction and stores the fp32 pre-activation (A.B + bias, or conv + bias)
+ * to `workspace` ([M,N], or NCHW for conv); kernel 2 reads it back and applies
+ * the residual (if any), the activation and the output cast.  Kernel 1's tile
+ * is planned for the workspace it writes, so a GEMM whose output or residual
+ * is not aligned for 4-element accesses still runs the 256x256 ping-pong main
+ * loop here.  With the same main loop (aligned outputs) the results are
+ * bitwise identical to the fused entry points; across main loops each result
+ * is still one rounding of an fp32 sum in ascending k.  `workspace` is a
+ * caller-owned, 16-byte aligned device buffer of at least *_workspace_size()
+ * bytes (BA_ERR_INVALID otherwise). */
 size_t gemm_bias_act_workspace_size(int64_t M, int64_t N);
 int gemm_bias_act_2k(const void* A, const void* B, const void* bias, void* C,
                      int64_t M, int64_t N, int64_t K, uint32_t dtypes,
@@ -165,31 +182,51 @@ int conv2d_bias_add_act_2k(const void* x, const void* w, const void* bias, const
                            size_t workspace_bytes, hipStream_t stream);
 
 /* Fused or two-kernel path, chosen per problem.  The pages decide at run
- * time whether to fuse: ops-nn (mlqm.cn/news/1824, section
- * "fused_matmul_relu底层到底做了什么") checks that the tiles and the
- * activation's buffer fit the on-chip budget and otherwise runs the two
- * steps; the Fused ConvTanh article (wmrh.cn/news/81139, section 核心问题)
- * measures first.  Here the fused epilogue needs no on-chip space beyond the
- * accumulators, so the static choice is BA_PATH_FUSED; biasact_tune_* measure
- * both paths on the caller's buffers and record the faster for that problem
- * (sizes, attributes, dtypes, act), and the *_auto entry points follow the
- * record.  Both paths give the same bits.
- *   biasact_gemm_path / biasact_conv_path: the recorded (else static) path;
- *     negative -BA_ERR_INVALID for null attribute arrays.
+ * time whether to fuse: ops-nn (mlqm.cn/news/1824, sections
+ * "fused_matmul_relu底层到底做了什么" and 融合不是万能的) checks that the
+ * tiles and the activation's buffer fit the on-chip budget and otherwise runs
+ * the two steps; the Fused ConvTanh article (wmrh.cn/news/81139, section
+ * 核心问题) measures first.  Here the fused epilogue needs no on-chip space
+ * beyond the accumulators, but the 256x256 ping-pong GEMM's epilogue needs
+ * an output (and residual) aligned for 4-element accesses.  The static rule
+ * for a problem nobody tuned: the two-kernel path when the fused call would
+ * lose the ping-pong main loop to the output's alignment while kernel 1,
+ * writing the aligned workspace, keeps it (and a workspace is given);
+ * otherwise fused.  Convs are always fused statically.  biasact_tune_*
+ * measure both paths on the caller's buffers and record the faster for that
+ * problem (sizes, attributes, dtypes, act); biasact_set_*_path record a
+ * choice directly (e.g. from an earlier tuning run; -1 forgets it); the
+ * *_auto entry points follow the record, else the static rule.
+ *   biasact_gemm_path / biasact_conv_path: the recorded path, else
+ *     BA_PATH_FUSED (the static choice for aligned buffers); negative
+ *     -BA_ERR_INVALID for null attribute arrays.
+ *   biasact_gemm_static_path: the static rule for these buffers (no launch;
+ *     BA_PATH_FUSED for invalid arguments).
+ *   biasact_set_gemm_path / biasact_set_conv_path: record `path`
+ *     (BA_PATH_FUSED, BA_PATH_TWO_KERNEL, or -1 to forget); BA_ERR_INVALID for
+ *     another value or null attribute arrays.
  *   biasact_tune_gemm / biasact_tune_conv: run the fused call once plus
  *     `reps` timed calls, then the two-kernel call likewise (only with a
  *     workspace of *_workspace_size bytes, and never for int8), SYNCHRONISING
  *     `stream` (the only library calls that do); the output buffer is
  *     overwritten; the chosen path goes to *path.  Returns a status code.
  *     The record is process-wide and guarded by a lock.
- *   gemm_bias_act_auto / conv2d_bias_act_auto: the recorded path when its
- *     workspace is given and large enough, else the fused path. */
+ *   gemm_bias_act_auto / conv2d_bias_act_auto: the recorded path, else the
+ *     static rule; the two-kernel path only when its workspace is given and
+ *     large enough, else the fused path. */
 #define BA_PATH_FUSED 0
 #define BA_PATH_TWO_KERNEL 1
 int biasact_gemm_path(int64_t M, int64_t N, int64_t K, uint32_t dtypes, int act);
 int biasact_conv_path(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Co, int64_t kh,
                       int64_t kw, const int32_t strides[2], const int32_t pads[4],
                       const int32_t dilations[2], uint32_t dtypes, int act);
+int biasact_gemm_static_path(const void* A, const void* B, const void* bias, const void* C,
+                             int64_t M, int64_t N, int64_t K, uint32_t dtypes, int act,
+                             const void* workspace, size_t workspace_bytes);
+int biasact_set_gemm_path(int64_t M, int64_t N, int64_t K, uint32_t dtypes, int act, int path);
+int biasact_set_conv_path(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Co, int64_t kh,
+                          int64_t kw, const int32_t strides[2], const int32_t pads[4],
+                          const int32_t dilations[2], uint32_t dtypes, int act, int path);
 int biasact_tune_gemm(const void* A, const void* B, const void* bias, void* C, int64_t M,
                       int64_t N, int64_t K, uint32_t dtypes, int act, float alpha, void* workspace,
                       size_t workspace_bytes, int reps, hipStream_t stream, int* path);
@@ -223,8 +260,9 @@ int biasact_tile_config_name(int id, char* buf, size_t n);
  * launched anything):
  * its kind and tile, e.g. "gemm 64x64/2x2 all-k", "gemm 256x256/2x4
  * ping-pong", "conv-halo 9 taps, 64 co x 8x56 positions, 2 chunk sets";
- * "none" before the first launch.  For a *_2k call it names the first of the
- * two kernels.  BA_ERR_INVALID for a null buf or n == 0. */
+ * "none" before the first launch.  A two-kernel call (*_2k, or *_auto taking
+ * that path) reports "two-kernel: " followed by its first kernel.
+ * BA_ERR_INVALID for a null buf or n == 0. */
 int biasact_last_tile_config(char* buf, size_t n);
 /* Tile config the library picks for a GEMM / conv problem (no launch). */
 int biasact_gemm_tile_config(int64_t M, int64_t N, int64_t K, uint32_t dtypes);

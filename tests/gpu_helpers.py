@@ -6,7 +6,7 @@ from __future__ import annotations
 import numpy as np
 
 import oracle as orc
-from oracle.compare import compare, decode_out, gamma
+from oracle.compare import compare, decode_out, merge, propagated_bound
 import workloads as wl
 
 _O = None
@@ -92,89 +92,80 @@ def guard_intact(buf, guard: int, dt: str, canary: int) -> bool:
 # reference computation on the oracle
 # ---------------------------------------------------------------------------
 
-def _needs_floor(in_dtype, out_dtype, K):
-    return out_dtype != "f32" or (in_dtype == "f32" and K > 512)
+def acc_bound(out_dtype, n_terms, z, abs_sum, act, alpha):
+    """The accumulation-error allowance of the acceptance rule
+    (oracle/compare.py): for 16-bit outputs, gamma_n * abs_sum carried
+    through the activation's largest slope near the pre-activation z; None
+    for fp32 and int32 outputs, whose rules take no such allowance."""
+    if out_dtype in ("f32", "i32"):
+        return None
+    return propagated_bound(z, abs_sum, n_terms, act, alpha)
 
 
-def _floor(in_dtype, out_dtype, K, abs_sum):
-    """Accumulation-error bound E for the acceptance rule (oracle/compare.py):
-    the worst-case gamma_{K+1} * sum|a b| for 16-bit outputs; for fp32 inputs
-    beyond K = 512 the probabilistic bound lambda * sqrt(K+1) * u * sum|a b|
-    (Higham & Mary, 2019) with lambda = 6."""
-    if out_dtype != "f32":
-        return gamma(K + 1) * abs_sum
-    return 6.0 * np.sqrt(K + 1) * 2.0 ** -24 * abs_sum
-
-
-def gemm_reference(case: wl.GemmCase, inp, idx=None):
-    """Oracle values (and the fp32 accumulation-error floor) for all outputs,
-    or for the flat indices `idx`."""
+def gemm_reference(case: wl.GemmCase, inp, idx=None, rows=None):
+    """Oracle values and the accumulation allowance for all outputs, for the
+    flat indices `idx`, or for the output rows `rows` (a slice)."""
     o = O()
-    A = o.decode(inp["A"], case.in_dtype)
-    B = o.decode(inp["B"], case.in_dtype)
+    A = o.decode(inp["A"], case.in_dtype).reshape(case.M, case.K)
+    B = o.decode(inp["B"], case.in_dtype).reshape(case.K, case.N)
     bias = o.decode(inp["bias"], case.bias_dtype) if inp["bias"] is not None else None
     alpha = orc.f32(case.alpha)
-    floor = None
-    need = _needs_floor(case.in_dtype, case.out_dtype, case.K)
+    need = case.out_dtype not in ("f32", "i32")
     absb = None if bias is None else np.abs(bias)
     R = None if inp.get("R") is None else o.decode(inp["R"].ravel(), case.out_dtype)
-    terms = case.K + (R is not None)
+    n_terms = case.K + 1 + (R is not None)
+    s = None
     if idx is None:
-        if R is None:
-            ref = o.gemm(A, B, bias, case.act, alpha).ravel()
-        else:
-            ref = o.gemm_residual(A, B, bias, R.reshape(case.M, case.N), case.act, alpha).ravel()
+        if rows is not None:
+            A = A[rows]
+            if R is not None:
+                R = R.reshape(case.M, case.N)[rows].ravel()
+        z = o.gemm(A, B, bias, "none").ravel()
         if need:
             s = o.gemm(np.abs(A), np.abs(B), absb, "none").ravel()
-            if R is not None:
-                s = s + np.abs(R)
-            floor = _floor(case.in_dtype, case.out_dtype, terms, s)
     else:
         ii, jj = idx // case.N, idx % case.N
-        if R is None:
-            ref = o.gemm_elems(A, B, bias, ii, jj, case.act, alpha)
-        else:
-            ref = o.gemm_residual_elems(A, B, bias, R[idx], ii, jj, case.act, alpha)
+        z = o.gemm_elems(A, B, bias, ii, jj, "none")
         if need:
             s = o.gemm_elems(np.abs(A), np.abs(B), absb, ii, jj, "none")
-            if R is not None:
-                s = s + np.abs(R[idx])
-            floor = _floor(case.in_dtype, case.out_dtype, terms, s)
-    return ref, floor
+        if R is not None:
+            R = R[idx]
+    if R is not None:
+        z = z + R
+        if s is not None:
+            s = s + np.abs(R)
+    ref = o.act(z, case.act, alpha)
+    return ref, acc_bound(case.out_dtype, n_terms, z, s, case.act, alpha)
 
 
 def conv_reference(case: wl.ConvCase, inp, idx=None):
     o = O()
-    x = o.decode(inp["x"], case.in_dtype)
-    w = o.decode(inp["w"], case.in_dtype)
+    x = o.decode(inp["x"], case.in_dtype).reshape(case.N, case.C, case.H, case.W)
+    w = o.decode(inp["w"], case.in_dtype).reshape(case.Co, case.C, case.kh, case.kw)
     bias = o.decode(inp["bias"], case.bias_dtype) if inp["bias"] is not None else None
     args = (case.strides, case.pads, case.dilations)
-    K = case.C * case.kh * case.kw
-    floor = None
+    alpha = orc.f32(case.alpha)
+    need = case.out_dtype not in ("f32", "i32")
     absb = None if bias is None else np.abs(bias)
-    need = _needs_floor(case.in_dtype, case.out_dtype, K)
     R = None if inp.get("R") is None else o.decode(inp["R"].ravel(), case.out_dtype)
-    terms = K + (R is not None)
+    n_terms = case.C * case.kh * case.kw + 1 + (R is not None)
+    s = None
     if idx is None:
-        if R is None:
-            ref = o.conv2d(x, w, bias, *args, case.act, orc.f32(case.alpha)).ravel()
-        else:
-            z = o.conv2d(x, w, bias, *args, "none").ravel()
-            ref = o.residual_act(z, R, case.act, orc.f32(case.alpha))
+        z = o.conv2d(x, w, bias, *args, "none").ravel()
         if need:
             s = o.conv2d(np.abs(x), np.abs(w), absb, *args, "none").ravel()
-            floor = _floor(case.in_dtype, case.out_dtype, terms, s if R is None else s + np.abs(R))
     else:
-        if R is None:
-            ref = o.conv2d_elems(x, w, bias, *args, idx, case.act, orc.f32(case.alpha))
-        else:
-            ref = o.conv2d_residual_elems(x, w, bias, R[idx], *args, idx, case.act,
-                                          orc.f32(case.alpha))
+        z = o.conv2d_elems(x, w, bias, *args, idx, "none")
         if need:
             s = o.conv2d_elems(np.abs(x), np.abs(w), absb, *args, idx, "none")
-            floor = _floor(case.in_dtype, case.out_dtype, terms,
-                           s if R is None else s + np.abs(R[idx]))
-    return ref, floor
+        if R is not None:
+            R = R[idx]
+    if R is not None:
+        z = z + R
+        if s is not None:
+            s = s + np.abs(R)
+    ref = o.act(z, case.act, alpha)
+    return ref, acc_bound(case.out_dtype, n_terms, z, s, case.act, alpha)
 
 
 # ---------------------------------------------------------------------------

@@ -254,3 +254,66 @@ def test_python_binding_raises_value_error_on_bad_names():
         ba._binding._act("swish")
     assert ba.conv_out_hw(224, 224, 7, 7, (2, 2), (3, 3, 3, 3), (1, 1)) == (112, 112)
     assert ba.conv_out_hw(2, 2, 3, 3, (1, 1), (0, 0, 0, 0), (1, 1)) is None
+
+
+def test_conv_out_dims_query():
+    # the library's one output-size rule (no launch): floor((H + pt + pb -
+    # dh*(kh-1) - 1) / sh) + 1, likewise for W
+    ho, wo = ctypes.c_int64(-1), ctypes.c_int64(-1)
+    q = lambda H, W, kh, kw, st, pd, dl: L.conv2d_bias_act_out_dims(
+        H, W, kh, kw, _i32(*st), _i32(*pd), _i32(*dl), ctypes.byref(ho), ctypes.byref(wo))
+    assert q(224, 224, 7, 7, (2, 2), (3, 3, 3, 3), (1, 1)) == 0 and (ho.value, wo.value) == (112, 112)
+    assert q(28, 28, 3, 3, (1, 1), (2, 2, 2, 2), (2, 2)) == 0 and (ho.value, wo.value) == (28, 28)
+    assert q(9, 7, 3, 2, (2, 1), (1, 0, 2, 1), (1, 2)) == 0 and (ho.value, wo.value) == (4, 8)
+    assert q(56, 56, 1, 1, (2, 2), (0, 0, 0, 0), (1, 1)) == 0 and (ho.value, wo.value) == (28, 28)
+    assert q(2, 2, 3, 3, (1, 1), (0, 0, 0, 0), (1, 1)) == 1          # empty output
+    assert q(8, 8, 3, 3, (0, 1), (1, 1, 1, 1), (1, 1)) == 1          # stride < 1
+    assert q(8, 8, 3, 3, (1, 1), (1, 1, -1, 1), (1, 1)) == 1         # pad < 0
+    assert q(0, 8, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1)) == 1
+    assert q(1 << 31, 8, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1)) == 2
+    assert L.conv2d_bias_act_out_dims(8, 8, 3, 3, _i32(1, 1), _i32(1, 1, 1, 1), _i32(1, 1),
+                                      None, ctypes.byref(wo)) == 1
+    # the binding takes its shapes from the library
+    assert ba.conv_out_hw(9, 7, 3, 2, (2, 1), (1, 0, 2, 1), (1, 2)) == (4, 8)
+
+
+def test_static_path_rule():
+    # fused unless the output's alignment keeps the fused GEMM off the
+    # ping-pong main loop that kernel 1 keeps when writing an aligned workspace
+    dt = _dt(BF16, BF16, F32, BF16)
+    A = ctypes.c_void_p(0x10000)
+    C_al, C_mis = ctypes.c_void_p(0x20000), ctypes.c_void_p(0x20002)
+    ws, ws_mis = ctypes.c_void_p(0x40000), ctypes.c_void_p(0x40004)
+    big = 4096 * 4096 * 4
+    sp = lambda C, M, N, K, w, n, d=dt: L.biasact_gemm_static_path(A, A, A, C, M, N, K, d, 1, w, n)
+    assert sp(C_al, 4096, 4096, 4096, ws, big) == 0            # aligned: fused ping-pong
+    assert sp(C_mis, 4096, 4096, 4096, ws, big) == 1           # misaligned C: two kernels
+    assert sp(C_mis, 4096, 4096, 4096, NUL, 0) == 0            # no workspace
+    assert sp(C_mis, 4096, 4096, 4096, ws, big - 4) == 0       # workspace too small
+    assert sp(C_mis, 4096, 4096, 4096, ws_mis, big) == 0       # workspace not 16-byte aligned
+    assert sp(C_mis, 1024, 640, 256, ws, big) == 0             # small grid: no ping-pong either way
+    assert sp(C_mis, 4096, 4096, 4096, ws, big, _dt(F32, F32, F32, F32)) == 0
+    assert sp(C_mis, 4096, 4096, 4100, ws, big) == 0           # K % 8: no ping-pong either way
+    assert sp(NUL, 4096, 4096, 4096, ws, big) == 0             # invalid: fused (the call will reject it)
+
+
+def test_recorded_path_roundtrip():
+    dt = _dt(F16, F16, F32, F16)
+    assert L.biasact_gemm_path(77, 88, 99, dt, 3) == 0
+    assert L.biasact_set_gemm_path(77, 88, 99, dt, 3, 1) == 0
+    assert L.biasact_gemm_path(77, 88, 99, dt, 3) == 1
+    assert L.biasact_gemm_path(77, 88, 99, dt, 4) == 0              # another activation
+    assert L.biasact_set_gemm_path(77, 88, 99, dt, 3, -1) == 0       # forget
+    assert L.biasact_gemm_path(77, 88, 99, dt, 3) == 0
+    assert L.biasact_set_gemm_path(77, 88, 99, dt, 3, 2) == 1
+    c = (_i32(1, 1), _i32(1, 1, 1, 1), _i32(1, 1))
+    cdt = _dt(F16, F16, F16, F16)
+    assert L.biasact_set_conv_path(3, 8, 9, 9, 5, 3, 3, *c, cdt, 3, 1) == 0
+    assert L.biasact_conv_path(3, 8, 9, 9, 5, 3, 3, *c, cdt, 3) == 1
+    assert L.biasact_set_conv_path(3, 8, 9, 9, 5, 3, 3, *c, cdt, 3, -1) == 0
+    assert L.biasact_conv_path(3, 8, 9, 9, 5, 3, 3, *c, cdt, 3) == 0
+    assert L.biasact_set_conv_path(3, 8, 9, 9, 5, 3, 3, None, c[1], c[2], cdt, 3, 1) == 1
+    assert ba.set_gemm_path(5, 6, 7, dt, "tanh", "2k") is None
+    assert ba.gemm_path(5, 6, 7, dt, "tanh") == "2k"
+    ba.set_gemm_path(5, 6, 7, dt, "tanh", None)
+    assert ba.gemm_path(5, 6, 7, dt, "tanh") == "fused"

@@ -10,7 +10,7 @@ call of the same entry point on the same inputs.
 import pytest
 
 import workloads as wl
-from gpu_helpers import gemm_reference, check, to_dev, torch_dtype, values_of
+from gpu_helpers import check, conv_reference, gemm_reference, to_dev, torch_dtype, values_of
 
 pytestmark = pytest.mark.gpu
 
@@ -153,7 +153,7 @@ def test_last_tile_config_names_the_kernel(ba):
                              "f32", "2k")
     call()
     torch.cuda.synchronize()
-    assert m.last_tile_config().startswith("conv-halo fp32"), m.last_tile_config()
+    assert m.last_tile_config().startswith("two-kernel: conv-halo fp32"), m.last_tile_config()
 
 
 def test_tuned_path_choice_and_auto_calls(ba):
@@ -205,3 +205,97 @@ def _gemm_tensors(case, inp):
     bias, _ = to_dev(inp["bias"], "f32")
     C = torch.empty((case.M, case.N), dtype=torch_dtype(case.out_dtype), device="cuda")
     return A, B, bias, C
+
+
+def test_recorded_two_kernel_choice_matches_oracle(ba):
+    # A recorded two-kernel choice: the auto entry points take the two-kernel
+    # branch (and report it), and the result matches the oracle and the fused
+    # call's bits; without a workspace they fall back to the fused call.
+    import conv_bias_activation_amd as m
+    M, N, K, ti, to, act = 520, 384, 640, "bf16", "bf16", "gelu"
+    case, inp, _, C, call = _gemm_setup(ba, M, N, K, ti, to, act, "fused")
+    call()
+    torch.cuda.synchronize()
+    want = C.clone()
+    A, B, bias, C2 = _gemm_tensors(case, inp)
+    ws = torch.empty(m.gemm_bias_act_workspace_size(M, N) // 4, dtype=torch.float32, device="cuda")
+    dt = m.dtypes_code(ti, ti, "f32", to)
+    m.set_gemm_path(M, N, K, dt, act, "2k")
+    try:
+        assert m.gemm_path(M, N, K, dt, act) == "2k"
+        m.gemm_bias_act_auto(A, B, bias, C2, act, 0.05, workspace=ws)
+        torch.cuda.synchronize()
+        assert m.last_tile_config().startswith("two-kernel: "), m.last_tile_config()
+        ref, acc = gemm_reference(case, inp)
+        rep = check(values_of(C2, to), ref, acc, case)
+        assert rep["ok"], rep
+        assert torch.equal(_bits(C2), _bits(want))
+        m.gemm_bias_act_auto(A, B, bias, C2, act, 0.05)
+        torch.cuda.synchronize()
+        assert not m.last_tile_config().startswith("two-kernel"), m.last_tile_config()
+    finally:
+        m.set_gemm_path(M, N, K, dt, act, None)
+    # conv: fp16 3x3 with a bias, recorded two-kernel, against the oracle
+    geom = (2, 64, 14, 14, 64, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1))
+    Nb, C_, H, W, Co, kh, kw, st, pd, dl = geom
+    ccase = wl.ConvCase("c", Nb, C_, H, W, Co, kh, kw, st, pd, dl, "f16", "f16", "f16", "tanh", 0.0,
+                        ("uniform", -0.5, 0.5), ("uniform", -0.5, 0.5), ("uniform", -0.5, 0.5))
+    cinp = wl.gen_conv(ccase, seed=22)
+    x, y, ccall = _conv_setup(ba, geom, "f16", "f16", "fused")
+    ccall()
+    torch.cuda.synchronize()
+    cwant = y.clone()
+    w, _ = to_dev(cinp["w"].reshape(Co, C_, kh, kw), "f16")
+    cb, _ = to_dev(cinp["bias"], "f16")
+    y2 = torch.empty_like(y)
+    n = m.conv2d_bias_act_workspace_size(*geom)
+    cws = torch.empty(n // 4, dtype=torch.float32, device="cuda")
+    cdt = m.dtypes_code("f16", "f16", "f16", "f16")
+    m.set_conv_path(*geom, cdt, "tanh", "2k")
+    try:
+        m.conv2d_bias_act_auto(x, w, cb, y2, st, pd, dl, "tanh", workspace=cws)
+        torch.cuda.synchronize()
+        assert m.last_tile_config().startswith("two-kernel: conv-halo"), m.last_tile_config()
+        ref, acc = conv_reference(ccase, cinp)
+        rep = check(values_of(y2, "f16"), ref, acc, ccase)
+        assert rep["ok"], rep
+        assert torch.equal(_bits(y2), _bits(cwant))
+    finally:
+        m.set_conv_path(*geom, cdt, "tanh", None)
+
+
+def test_static_rule_takes_two_kernels_for_a_misaligned_output(ba):
+    # Nothing recorded, C two bytes off its allocation: the fused call loses
+    # the ping-pong main loop (its epilogue needs 4-element aligned rows),
+    # kernel 1 of the two-kernel path keeps it on the aligned workspace, so
+    # the static rule takes the two-kernel branch.  Both paths match the
+    # oracle on every output.
+    import conv_bias_activation_amd as m
+    M, N, K = 4096, 4096, 256
+    case = wl.GemmCase("misaligned", M, N, K, "bf16", "f32", "bf16", "relu", 0.0,
+                       ("normal", 1.0 / 16.0), ("normal", 1.0 / 16.0), ("uniform", -0.1, 0.1))
+    inp = wl.gen_gemm(case, seed=31)
+    A, _ = to_dev(inp["A"].reshape(M, K), "bf16")
+    B, _ = to_dev(inp["B"].reshape(K, N), "bf16")
+    bias, _ = to_dev(inp["bias"], "f32")
+    buf = torch.empty(M * N + 1, dtype=torch.bfloat16, device="cuda")
+    C = buf[1:].view(M, N)
+    ws = torch.empty(M * N, dtype=torch.float32, device="cuda")
+    dt = m.dtypes_code("bf16", "bf16", "f32", "bf16")
+    assert m.gemm_path(M, N, K, dt, "relu") == "fused"           # nothing recorded
+    assert m.gemm_static_path(A, B, bias, C, "relu", workspace=ws) == "2k"
+    assert m.gemm_static_path(A, B, bias, C, "relu") == "fused"  # no workspace given
+    ref, acc = gemm_reference(case, inp)
+    m.gemm_bias_act_auto(A, B, bias, C, "relu", workspace=ws)
+    torch.cuda.synchronize()
+    assert m.last_tile_config() == "two-kernel: gemm 256x256/2x4 ping-pong", m.last_tile_config()
+    rep = check(values_of(C, "bf16"), ref, acc, case)
+    assert rep["ok"], rep
+    two = C.clone()
+    m.gemm_bias_act(A, B, bias, C, "relu")
+    torch.cuda.synchronize()
+    assert "ping-pong" not in m.last_tile_config(), m.last_tile_config()
+    rep = check(values_of(C, "bf16"), ref, acc, case)
+    assert rep["ok"], rep
+    # both main loops sum the same 16-wide k-steps in ascending order from the bias
+    assert torch.equal(_bits(C), _bits(two))

@@ -130,3 +130,34 @@ def test_int8_ping_pong_vs_oracle(ba, shape, to, acts):
                 assert rep["ok"], (act, rep)
     finally:
         ba.force_tile_config(-1)
+
+
+def test_int8_ping_pong_misaligned_bias(ba):
+    # an int32 bias one element into its buffer is read element by element,
+    # an aligned one as runs of four columns: the same exact sums
+    from gpu_helpers import to_dev
+    M, N, K = 300, 528, 208
+    case = _case(M, N, K, "i32", "relu")
+    inp = wl.gen_gemm(case, seed=131)
+    ref, _ = gemm_reference(case, inp)
+    A, _ = to_dev(inp["A"].reshape(M, K), "i8")
+    B, _ = to_dev(inp["B"].reshape(K, N), "i8")
+    bias0, _ = to_dev(inp["bias"], "i32")
+    outs = []
+    ba.force_tile_config(6)
+    try:
+        for off in (0, 1):
+            bias = bias0
+            if off:
+                buf = torch.empty(N + off, dtype=torch.int32, device="cuda")
+                bias = buf[off:]
+                bias.copy_(bias0)
+            C = torch.empty((M, N), dtype=torch.int32, device="cuda")
+            ba.gemm_bias_act(A, B, bias, C, "relu", 0.0)
+            torch.cuda.synchronize()
+            assert "ping-pong int8" in ba.last_tile_config(), ba.last_tile_config()
+            outs.append(words_of(C, "i32"))
+    finally:
+        ba.force_tile_config(-1)
+    for w in outs:
+        assert np.array_equal(w.view(np.int32).astype(np.float64), ref)

@@ -3,7 +3,8 @@ the same seeded input bits, element by element.
 
 Acceptance (oracle/compare.py): fp32 output with fp16/bf16 inputs within
 1e-3*(1+|ref|); fp32 inputs within 1e-5*(1+|ref|); fp16/bf16 output within one
-output ulp (taken at max(|ref|, fp32 accumulation-error bound)).  Where the
+output ulp, or half an ulp plus the fp32 accumulation-error bound carried
+through the activation's slope where that bound is the larger.  Where the
 result is exact in fp32 (small-integer operands, identity B) the test demands
 bit equality; fused vs two-kernel and run-to-run must be bitwise equal.
 """
@@ -11,7 +12,7 @@ import numpy as np
 import pytest
 
 import workloads as wl
-from gpu_helpers import (check, conv_reference, empty_out, gemm_reference, guard_intact, run_conv,
+from gpu_helpers import (check, conv_reference, empty_out, gemm_reference, guard_intact, merge, run_conv,
                          run_gemm, to_dev, values_of, words_of)
 
 pytestmark = pytest.mark.gpu
@@ -26,11 +27,22 @@ def ba():
     return m
 
 
-def _gcase(M, N, K, ti, to, tb, act, alpha=0.01, dist=("uniform", -1.0, 1.0)):
+# fp32 operands with a reduction longer than 512 are drawn from U(-0.1, 0.1):
+# their fp32 accumulation error then stays well inside 1e-5 * (1 + |ref|)
+# (the rule takes no allowance for it), where U(-1, 1) operands would put
+# the error of a correct fp32 sum at the tolerance's own scale.
+SMALL_F32 = ("uniform", -0.1, 0.1)
+
+
+def _gcase(M, N, K, ti, to, tb, act, alpha=0.01, dist=None):
+    if dist is None:
+        dist = SMALL_F32 if ti == "f32" and K > 512 else ("uniform", -1.0, 1.0)
     return wl.GemmCase(f"g{M}x{N}x{K}", M, N, K, ti, tb, to, act, alpha, dist, dist, dist)
 
 
-def _ccase(N, C, H, W, Co, kh, kw, st, pd, dl, ti, to, tb, act, dist=("uniform", -0.5, 0.5)):
+def _ccase(N, C, H, W, Co, kh, kw, st, pd, dl, ti, to, tb, act, dist=None):
+    if dist is None:
+        dist = SMALL_F32 if ti == "f32" and C * kh * kw > 512 else ("uniform", -0.5, 0.5)
     return wl.ConvCase(f"c{N}x{C}x{H}x{W}", N, C, H, W, Co, kh, kw, st, pd, dl, ti, tb, to, act, 0.0,
                        dist, dist, dist)
 
@@ -84,17 +96,17 @@ def test_gemm_every_tile_config(ba, tile):
         ba.force_tile_config(-1)
 
 
-@pytest.mark.parametrize("tb", ["f32", "bf16"])
-def test_pp_bias_vector_and_element_loads_agree(ba, tb):
+@pytest.mark.parametrize("ti,tb", [("bf16", "f32"), ("bf16", "bf16"), ("f16", "f16"), ("f16", "f32")])
+def test_pp_bias_vector_and_element_loads_agree(ba, ti, tb):
     # The ping-pong kernel reads each lane's bias as runs of 4 columns (one
     # 16- or 8-byte load each) when the bias is aligned for it, and element by
     # element otherwise: bias one element into its buffer gives the same bits
     M, N, K = 300, 520, 200
-    case = _gcase(M, N, K, "bf16", "bf16", tb, "gelu")
+    case = _gcase(M, N, K, ti, ti, tb, "gelu")
     inp = wl.gen_gemm(case, seed=23)
     ref, floor = gemm_reference(case, inp)
-    A, _ = to_dev(inp["A"].reshape(M, K), "bf16")
-    B, _ = to_dev(inp["B"].reshape(K, N), "bf16")
+    A, _ = to_dev(inp["A"].reshape(M, K), ti)
+    B, _ = to_dev(inp["B"].reshape(K, N), ti)
     bias0, _ = to_dev(inp["bias"], tb)
     outs = []
     ba.force_tile_config(6)
@@ -106,17 +118,18 @@ def test_pp_bias_vector_and_element_loads_agree(ba, tb):
                 bias.copy_(bias0)
             else:
                 bias = bias0
-            C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            C = torch.empty((M, N), dtype=A.dtype, device="cuda")
             ba.gemm_bias_act(A, B, bias, C, "gelu", 0.0)
             torch.cuda.synchronize()
             assert "ping-pong" in ba.last_tile_config()
             outs.append(C)
     finally:
         ba.force_tile_config(-1)
-    rep = check(values_of(outs[0], "bf16"), ref, floor, case)
-    _report(f"pp bias {tb}", rep)
-    assert rep["ok"], rep
-    assert np.array_equal(words_of(outs[0], "bf16"), words_of(outs[1], "bf16"))
+    for C in outs:
+        rep = check(values_of(C, ti), ref, floor, case)
+        _report(f"pp bias {ti} {tb}", rep)
+        assert rep["ok"], rep
+    assert np.array_equal(words_of(outs[0], ti), words_of(outs[1], ti))
 
 
 @pytest.mark.parametrize("ti", ["bf16", "f16", "f32"])
@@ -516,48 +529,65 @@ def test_python_binding_rejects_bad_tensors(ba):
 
 
 # ---------------------------------------------------------------------------
-# the named workloads at full size (sampled outputs; full output for the
-# small MatmulLeakyRelu spec case)
+# the named workloads at full size: every output, seeds 0, 1 and 2
 # ---------------------------------------------------------------------------
 
 NAMED = list(wl.CASES)
+CHUNK = 1 << 24          # outputs per oracle call on the GEMMs (bounds host memory)
 
 
+def _log_report(name, seed, rep):
+    """Print the report; with BIASACT_PARITY_LOG set, also append it there as
+    one JSON line (the per-workload error record)."""
+    import json
+    import os
+    line = {"workload": name, "seed": seed, **{k: v for k, v in rep.items() if k != "worst"}}
+    print(f"[full {name} seed {seed}] {json.dumps(line)}", flush=True)
+    path = os.environ.get("BIASACT_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(line) + "\n")
+
+
+@pytest.mark.parametrize("seed", (0, 1, 2))
 @pytest.mark.parametrize("name", NAMED)
-def test_named_workload_full_size(ba, name):
+def test_named_workload_full_size(ba, name, seed):
     case = wl.CASES[name]
     is_gemm = isinstance(case, wl.GemmCase)
-    for seed in (0, 1):
-        inp = wl.gen_gemm(case, seed) if is_gemm else wl.gen_conv(case, seed)
-        y_t = run_gemm(case, inp) if is_gemm else run_conv(case, inp)
-        total = y_t.numel()
-        small = name == "gemm_leaky_1024x640x256_f16"
-        idx = None if small else wl.sample_indices(total, 6000, seed)
-        ref, floor = (gemm_reference if is_gemm else conv_reference)(case, inp, idx)
-        vals = values_of(y_t, case.out_dtype)
-        got = vals if idx is None else vals[idx]
-        rep = check(got, ref, floor, case)
-        _report(f"{name} seed {seed}", rep)
-        assert rep["ok"], rep
-        assert np.all(np.isfinite(vals))
-        # the two-kernel path gives the same bits at full size (int8 GEMMs
-        # have the fused path only)
-        if seed == 0 and case.in_dtype != "i8":
-            y2 = run_gemm(case, inp, "2k") if is_gemm else run_conv(case, inp, "2k")
-            assert np.array_equal(words_of(y2, case.out_dtype), words_of(y_t, case.out_dtype))
-        del y_t
-        torch.cuda.empty_cache()
+    inp = wl.gen_gemm(case, seed) if is_gemm else wl.gen_conv(case, seed)
+    y_t = run_gemm(case, inp) if is_gemm else run_conv(case, inp)
+    vals = values_of(y_t, case.out_dtype)
+    assert np.all(np.isfinite(vals))
+    if is_gemm:
+        rows = max(1, CHUNK // case.N)
+        reps = []
+        for r0 in range(0, case.M, rows):
+            r1 = min(case.M, r0 + rows)
+            ref, acc = gemm_reference(case, inp, rows=slice(r0, r1))
+            reps.append(check(vals[r0 * case.N:r1 * case.N], ref, acc, case))
+        rep = merge(reps)
+    else:
+        ref, acc = conv_reference(case, inp)
+        rep = check(vals, ref, acc, case)
+    _log_report(name, seed, rep)
+    assert rep["ok"], rep
+    # the two-kernel path gives the same bits at full size (int8 GEMMs have
+    # the fused path only)
+    if seed == 0 and case.in_dtype != "i8":
+        y2 = run_gemm(case, inp, "2k") if is_gemm else run_conv(case, inp, "2k")
+        assert np.array_equal(words_of(y2, case.out_dtype), words_of(y_t, case.out_dtype))
+        del y2
+    del y_t
+    torch.cuda.empty_cache()
 
 
-def test_matmul_leakyrelu_sample_acceptance_rule(ba):
-    """The sample's own check: fp32 matmul of the fp16 operands plus bias,
-    LeakyReLU by torch.where, allclose with rtol = atol = 1e-3."""
+def test_matmul_leakyrelu_sample_acceptance_scale(ba):
+    """The MatmulLeakyRelu sample's acceptance scale ("CANN pyasc
+    MatmulLeakyRelu 融合算子实战", section 编译执行: relative and absolute
+    tolerance 1e-3 over the whole output), stated here as an explicit bound
+    against the oracle: |C - ref| <= 1e-3 * (1 + |ref|) for every element."""
     case = wl.CASES["gemm_leaky_1024x640x256_f16"]
     inp = wl.gen_gemm(case, 0)
-    c = run_gemm(case, inp).float().cpu()
-    a = torch.from_numpy(inp["A"].view(np.float16).astype(np.float32))
-    b = torch.from_numpy(inp["B"].view(np.float16).astype(np.float32))
-    bias = torch.from_numpy(inp["bias"].view(np.float32))
-    alpha = float(np.float32(case.alpha))
-    mm = a @ b + bias
-    assert torch.allclose(c, torch.where(mm >= 0, mm, mm * alpha), rtol=1e-3, atol=1e-3)
+    c = values_of(run_gemm(case, inp), "f32")
+    ref, _ = gemm_reference(case, inp)
+    assert np.all(np.abs(c - ref) <= 1e-3 * (1.0 + np.abs(ref)))

@@ -7,13 +7,13 @@ conv-halo kernels and the generic conv), fused and two-kernel paths (bitwise
 equal), in place (R is the output buffer), and with R misaligned against the
 output so the kernels fall back to element-wise accesses.  The acceptance rule
 is the one of the other parity tests; for 16-bit outputs the accumulation
-floor counts R as one more term of the fp32 sum.
+allowance counts R as one more term of the fp32 sum.
 """
 import numpy as np
 import pytest
 
 import workloads as wl
-from gpu_helpers import O, _floor, _needs_floor, check, to_dev, torch_dtype, values_of, words_of
+from gpu_helpers import O, acc_bound, check, to_dev, torch_dtype, values_of, words_of
 import oracle as orc
 
 pytestmark = pytest.mark.gpu
@@ -61,12 +61,11 @@ def _gemm_ref(case, inp, r_words):
     B = o.decode(inp["B"], case.in_dtype).reshape(case.K, case.N)
     bias = o.decode(inp["bias"], case.bias_dtype)
     R = o.decode(r_words.ravel(), case.out_dtype).reshape(case.M, case.N)
-    ref = o.gemm_residual(A, B, bias, R, case.act, orc.f32(case.alpha)).ravel()
-    floor = None
-    if _needs_floor(case.in_dtype, case.out_dtype, case.K):
-        s = o.gemm(np.abs(A), np.abs(B), np.abs(bias), "none") + np.abs(R)
-        floor = _floor(case.in_dtype, case.out_dtype, case.K + 1, s.ravel())
-    return ref, floor
+    alpha = orc.f32(case.alpha)
+    ref = o.gemm_residual(A, B, bias, R, case.act, alpha).ravel()
+    z = (o.gemm(A, B, bias, "none") + R).ravel()
+    s = (o.gemm(np.abs(A), np.abs(B), np.abs(bias), "none") + np.abs(R)).ravel()
+    return ref, acc_bound(case.out_dtype, case.K + 2, z, s, case.act, alpha)
 
 
 def _run_gemm(ba, case, inp, r_words, path="fused", inplace=False, r_offset=0, c_offset=0):
@@ -212,12 +211,10 @@ def _conv_ref(case, inp, r_words):
     R = o.decode(r_words.ravel(), case.out_dtype).reshape(case.N, case.Co, Ho, Wo)
     args = (case.strides, case.pads, case.dilations)
     ref = o.conv2d_residual(x, w, bias, R, *args, case.act).ravel()
-    floor = None
     K = case.C * case.kh * case.kw
-    if _needs_floor(case.in_dtype, case.out_dtype, K):
-        s = o.conv2d(np.abs(x), np.abs(w), np.abs(bias), *args, "none") + np.abs(R)
-        floor = _floor(case.in_dtype, case.out_dtype, K + 1, s.ravel())
-    return ref, floor
+    z = (o.conv2d(x, w, bias, *args, "none") + R).ravel()
+    s = (o.conv2d(np.abs(x), np.abs(w), np.abs(bias), *args, "none") + np.abs(R)).ravel()
+    return ref, acc_bound(case.out_dtype, K + 2, z, s, case.act, 0.0)
 
 
 def _run_conv(ba, case, inp, r_words, path="fused", inplace=False, r_offset=0):

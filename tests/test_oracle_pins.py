@@ -23,7 +23,7 @@ import pytest
 
 import oracle as orc
 from oracle import Oracle
-from oracle.compare import compare, tolerance, ulp
+from oracle.compare import ETA_ACT, compare, gamma, propagated_bound, slope_bound, tolerance, ulp
 import workloads
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -534,10 +534,42 @@ def test_compare_flags_errors():
     # 16-bit output: one ulp passes, two fail
     assert compare(np.array([1.0 + 2 ** -7]), np.array([1.0]), "bf16", "bf16")["ok"]
     assert not compare(np.array([1.0 + 2 ** -6]), np.array([1.0]), "bf16", "bf16")["ok"]
-    # 16-bit output: one ulp at |ref| plus the accumulation-error bound
-    assert tolerance(np.array([1.0]), "bf16", "bf16", np.array([0.5]))[0] == 2.0 ** -7 + 0.5
-    assert tolerance(np.array([2.0]), "f32", "f32", np.array([1.0]))[0] == 1.0
+    # 16-bit output: one ulp, or half an ulp (at |ref| + d) plus d where the
+    # allowance d = L*E + ETA*|ref| exceeds half an ulp
+    eta = ETA_ACT
+    assert tolerance(np.array([1.0]), "bf16", "bf16")[0] == 2.0 ** -7
+    assert tolerance(np.array([1.0]), "bf16", "bf16", np.array([2.0 ** -9]))[0] == 2.0 ** -7
+    t = tolerance(np.array([1.0]), "bf16", "bf16", np.array([0.5]))[0]
+    assert t == 0.5 * 2.0 ** -7 + 0.5 + eta               # ulp at 1.5 is still 2^-7
+    t = tolerance(np.array([1.0]), "bf16", "bf16", np.array([1.0]))[0]
+    assert t == 0.5 * 2.0 ** -6 + 1.0 + eta               # 2 + eta lies in the next binade
+    # fp32 outputs take no accumulation allowance
+    assert abs(tolerance(np.array([2.0]), "f32", "f32", np.array([1.0]))[0] - 3e-5) < 1e-18
     assert abs(tolerance(np.array([2.0]), "f32", "f32")[0] - 3e-5) < 1e-18
+    assert tolerance(np.array([5.0]), "i8", "i32")[0] == 0.0
+
+
+def test_slope_bound_closed_forms():
+    z0 = np.zeros(1)
+    assert slope_bound(z0, 0.0, "tanh")[0] == 1.0                 # tanh'(0) = 1
+    assert slope_bound(z0, 0.0, "sigmoid")[0] == 0.25             # s'(0) = 1/4
+    assert slope_bound(z0, 0.0, "gelu")[0] == 0.5                 # Phi(0) + 0
+    # tanh'(ln 3) = 1 - (4/5)^2; the interval's point nearest 0 decides
+    assert abs(slope_bound(np.array([math.log(3.0) + 0.5]), 0.5, "tanh")[0] - 9.0 / 25.0) < 1e-15
+    assert abs(slope_bound(np.array([-math.log(3.0)]), 0.0, "sigmoid")[0] - 0.75 * 0.25) < 1e-15
+    # GELU' peaks at sqrt(2): Phi(sqrt 2) + sqrt(2) phi(sqrt 2), an interior point of [1, 2]
+    r2 = math.sqrt(2.0)
+    peak = 0.5 * math.erfc(-1.0) + r2 * math.exp(-1.0) / math.sqrt(2.0 * math.pi)
+    assert abs(slope_bound(np.array([1.5]), 0.5, "gelu")[0] - peak) < 1e-14
+    assert slope_bound(np.array([1.5]), 0.5, "gelu")[0] > max(slope_bound(np.array([1.0]), 0.0, "gelu")[0],
+                                                              slope_bound(np.array([2.0]), 0.0, "gelu")[0])
+    # ReLU passes nothing below zero unless the interval reaches it; LeakyReLU alpha
+    assert slope_bound(np.array([-1.0, -1.0, 0.5]), np.array([0.5, 1.5, 0.1]), "relu").tolist() == [0, 1, 1]
+    assert slope_bound(np.array([-1.0, -0.1]), 0.5, "leaky_relu", 0.01).tolist() == [0.01, 1.0]
+    assert slope_bound(np.array([-7.0]), 0.0, "none")[0] == 1.0
+    # the propagated bound is gamma_n * S times the slope
+    pb = propagated_bound(np.array([-3.0]), np.array([2.0]), 100, "leaky_relu", 0.25)[0]
+    assert pb == 0.25 * gamma(100) * 2.0
 
 
 def test_generator_rounding_and_determinism():
