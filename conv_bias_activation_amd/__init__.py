@@ -37,6 +37,7 @@ from ._binding import (  # noqa: F401
     conv2d_bias_add_act,
     conv2d_bias_add_act_2k,
     gemm_bias_act_2k,
+    gemm_bias_act_2k_noalloc,
     gemm_bias_act_workspace_size,
     gemm_tile_config,
     conv_tile_config,

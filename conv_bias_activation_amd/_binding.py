@@ -40,6 +40,9 @@ def _load():
     l.gemm_bias_act_2k.argtypes = [vp, vp, vp, vp, i64, i64, i64, u32, ctypes.c_int, ctypes.c_float,
                                    vp, ctypes.c_size_t, vp]
     l.gemm_bias_act_2k.restype = ctypes.c_int
+    l.gemm_bias_act_2k_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i64, u32, ctypes.c_int,
+                                           ctypes.c_float, vp]
+    l.gemm_bias_act_2k_noalloc.restype = ctypes.c_int
     l.gemm_bias_act_workspace_size.argtypes = [i64, i64]
     l.gemm_bias_act_workspace_size.restype = ctypes.c_size_t
     conv = [vp, vp, vp, vp] + [i64] * 7 + [i32p, i32p, i32p, u32, ctypes.c_int]
@@ -220,6 +223,16 @@ def gemm_bias_act_2k(A, B, bias, C, act="none", alpha: float = 0.0, workspace=No
                               M, N, K, dt, _act(act), float(alpha), _dev(workspace, "workspace"),
                               nbytes, _stream(stream))
     _check(rc, "gemm_bias_act_2k")
+    return C
+
+
+def gemm_bias_act_2k_noalloc(A, B, bias, C, act="none", alpha: float = 0.0, stream=None):
+    """The two-kernel GEMM with the library's own fixed workspace (no
+    allocation; M * N * 4 <= 64 MiB; calls overlapping on one GPU race)."""
+    M, N, K, dt = _gemm_args(A, B, bias, C)
+    rc = lib.gemm_bias_act_2k_noalloc(_dev(A, "A"), _dev(B, "B"), _dev(bias, "bias"), _dev(C, "C"),
+                                      M, N, K, dt, _act(act), float(alpha), _stream(stream))
+    _check(rc, "gemm_bias_act_2k_noalloc")
     return C
 
 

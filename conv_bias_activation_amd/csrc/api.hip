@@ -228,6 +228,43 @@ int conv_2k_impl(const void* x, const void* w, const void* bias, const void* r, 
   return launch_second_kernel(p.dto, workspace, y, need / 4u, act, 0.0f, r, stream);
 }
 
+// ---- the two-kernel GEMM without allocation -------------------------------
+// Callers that cannot allocate (graph capture, serving loops) get the
+// two-kernel path with its fp32 workspace in this fixed device array: 64 MiB,
+// the workspace of a 4096 x 4096 output.  Each GPU the library runs on holds
+// its own copy until the process ends; calls on one GPU share it.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+// Device address of `scratch` on each device, looked up once per device with
+// that device current.  In host code `scratch` itself is only a host-side
+// stand-in for the symbol: kernels get these addresses.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    t_last_hip = e;
+    return kErrHip;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return kErrUnsupported;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      t_last_hip = e != hipSuccess ? e : hipErrorInvalidSymbol;
+      return kErrHip;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return kOk;
+}
+
 // ---- fused-vs-two-kernel selection --------------------------------------
 // Decisions recorded by the tuning calls, per problem (kind, sizes, types,
 // activation); the auto entry points look them up.
@@ -349,6 +386,24 @@ int gemm_bias_act_2k(const void* A, const void* B, const void* bias, void* C, in
                      size_t workspace_bytes, hipStream_t stream) {
   return gemm_2k_impl(A, B, bias, nullptr, C, M, N, K, dtypes, act, alpha, workspace,
                       workspace_bytes, stream);
+}
+
+int gemm_bias_act_2k_noalloc(const void* A, const void* B, const void* bias, void* C, int64_t M,
+                             int64_t N, int64_t K, uint32_t dtypes, int act, float alpha,
+                             hipStream_t stream) {
+  // every check that needs no HIP call comes first
+  GemmPlan p;
+  int rc = plan_gemm(A, B, bias, C, M, N, K, dtypes, act, &p);
+  if (rc || p.empty) return rc;
+  if (p.dti == DT_I8) return kErrUnsupported;
+  if ((uint64_t)M * (uint64_t)N * 4u > kScratchBytes) return kErrUnsupported;
+  void* ws = nullptr;
+  rc = scratch_of_current_device(&ws);
+  if (rc) return rc;
+  // kernel 1 writes every workspace element kernel 2 reads, in stream order:
+  // nothing needs clearing
+  return gemm_2k_impl(A, B, bias, nullptr, C, M, N, K, dtypes, act, alpha, ws, kScratchBytes,
+                      stream);
 }
 
 int gemm_bias_add_act(const void* A, const void* B, const void* bias, const void* R, void* C,

@@ -142,6 +142,24 @@ int gemm_bias_act_2k(const void* A, const void* B, const void* bias, void* C,
                      int act, float alpha, void* workspace, size_t workspace_bytes,
                      hipStream_t stream);
 
+/* gemm_bias_act_2k without a caller workspace and without any allocation,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  The fp32
+ * workspace is a fixed 64 MiB device array inside the library, one per GPU,
+ * held from the library's first use of that GPU until the process ends; the
+ * calling thread's current device must be the stream's device.  Limit:
+ * M * N * 4 <= 64 MiB (e.g. a 4096 x 4096 output), else BA_ERR_UNSUPPORTED
+ * with nothing launched; int8 operands: BA_ERR_UNSUPPORTED.  Kernel 1 writes
+ * every workspace element that kernel 2 reads, so nothing needs clearing.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (other streams, other threads) race and give undefined results;
+ * serialise them on one stream.  Results are bitwise those of
+ * gemm_bias_act_2k with a 16-byte aligned workspace.  Other arguments, checks
+ * and return codes as gemm_bias_act. */
+int gemm_bias_act_2k_noalloc(const void* A, const void* B, const void* bias, void* C,
+                             int64_t M, int64_t N, int64_t K, uint32_t dtypes,
+                             int act, float alpha, hipStream_t stream);
+
 size_t conv2d_bias_act_workspace_size(int64_t N, int64_t C, int64_t H, int64_t W, int64_t Co,
                                       int64_t kh, int64_t kw, const int32_t strides[2],
                                       const int32_t pads[4], const int32_t dilations[2]);

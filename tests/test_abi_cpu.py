@@ -317,3 +317,14 @@ def test_recorded_path_roundtrip():
     assert ba.gemm_path(5, 6, 7, dt, "tanh") == "2k"
     ba.set_gemm_path(5, 6, 7, dt, "tanh", None)
     assert ba.gemm_path(5, 6, 7, dt, "tanh") == "fused"
+
+
+def test_noalloc_entry_point_checks_before_any_hip_call():
+    dt = _dt(BF16, BF16, F32, BF16)
+    f = L.gemm_bias_act_2k_noalloc
+    assert f(P, P, P, P, 8192, 4096, 64, dt, 1, 0.0, NUL) == 2       # 128 MiB workspace > 64 MiB
+    assert f(P, P, P, P, 4096, 4097, 64, dt, 1, 0.0, NUL) == 2       # just past the limit
+    assert f(NUL, P, P, P, 64, 64, 64, dt, 1, 0.0, NUL) == 1
+    assert f(P, P, P, P, 64, 64, 64, dt, 9, 0.0, NUL) == 1
+    assert f(P, P, P, P, 64, 64, 64, _dt(3, 3, 4, 4), 1, 0.0, NUL) == 2   # int8: fused only
+    assert f(P, P, P, P, 0, 64, 64, dt, 1, 0.0, NUL) == 0              # empty: nothing to launch
