@@ -21,7 +21,10 @@ Besides the headline, the line carries:
                 `cpu_oracle` the fp64 oracle's rate on a bounded sample of
                 it, on all host threads (and on one, for the small workloads);
   path_rule     the static fused-vs-two-kernel rule's case (the 4096^3 GEMM
-                with a misaligned output): fused, two-kernel and auto calls.
+                with a misaligned output): fused, two-kernel and auto calls;
+  launch_floor  the per-call time of a trivial kernel on the same stream
+                (eager and graph replays), next to which the latency-bound
+                small workloads are read.
 """
 from __future__ import annotations
 
@@ -327,6 +330,19 @@ def measure_case(case, path, min_ms=200.0):
     return out
 
 
+def launch_floor():
+    """Per-call time of the smallest kernel torch launches (an in-place add on
+    64 floats) on this stream, eager back-to-back and in graph replays: the
+    launch and scheduling floor that a latency-bound call cannot go below."""
+    import torch
+    t = torch.zeros(64, dtype=torch.float32, device="cuda")
+    step = lambda: t.add_(1.0)
+    ms, _ = time_steps(step, 2000, 50)
+    R, med, mn = graph_trials(step, ms)
+    return {"kernel": "torch add_ on 64 floats", "eager_ms": round(ms, 5),
+            "graph_median_ms": round(med, 5), "graph_min_ms": round(mn, 5), "steps_per_replay": R}
+
+
 def path_rule_case():
     """The static fused-vs-two-kernel rule's case: the 4096^3 bf16 GEMM + ReLU
     with C two bytes off its allocation (not aligned for 4-element accesses).
@@ -347,6 +363,9 @@ def path_rule_case():
     calls = {"fused": lambda: ba.gemm_bias_act(A, B, bias, C, "relu"),
              "2k": lambda: ba.gemm_bias_act_2k(A, B, bias, C, "relu", workspace=ws),
              "auto": lambda: ba.gemm_bias_act_auto(A, B, bias, C, "relu", workspace=ws)}
+    # the tuner may have recorded a path for this problem (with an aligned C);
+    # forget it so the auto call applies the static rule
+    ba.set_gemm_path(case.M, case.N, case.K, ba.dtypes_code("bf16", "bf16", "f32", "bf16"), "relu", None)
     out = {"workload": case.name + ", C misaligned by 2 bytes",
            "static_path": ba.gemm_static_path(A, B, bias, C, "relu", workspace=ws)}
     for name, step in calls.items():
@@ -545,6 +564,10 @@ def main():
             others[name] = entry
             torch.cuda.empty_cache()
         line["others"] = others
+        try:
+            line["launch_floor"] = launch_floor()
+        except Exception as e:  # report, never hide
+            line["launch_floor"] = {"error": repr(e)}
         try:
             line["path_rule"] = path_rule_case()
         except Exception as e:  # report, never hide

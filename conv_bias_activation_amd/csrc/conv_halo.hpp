@@ -171,12 +171,15 @@ __global__ __launch_bounds__(256, (occupancy<BM, KS, SN>())) void conv16_halo_ke
     }
   };
 
-  // ---- input halo: item it = (halo row, column pair, channel group) --------
+  // ---- input halo: item it = (halo row, channel group, column pair) --------
   // x offset of channel 8g of chunk 0 (kOOB outside the image), channel offset
   // 8g (kFar when the item does not exist), LDS addresses of its two columns.
+  // The column pair varies fastest across lanes, so each of an item's eight
+  // 4-byte loads (one channel each) reads consecutive column pairs of one
+  // input row: a wave's load covers a few cache lines, not one line per lane.
   auto halo_item = [&](uint32_t it, uint32_t& src, uint32_t& g8, uint32_t& lo, uint32_t& hi) {
-    const uint32_t g = it % NCH, rp = it / NCH;
-    const uint32_t pr = rp % pairs, hr = rp / pairs;
+    const uint32_t pr = it % pairs, rg = it / pairs;
+    const uint32_t g = rg % NCH, hr = rg / NCH;
     const int32_t ih = ih_lo + (int32_t)hr, iw = iw_lo + 2 * (int32_t)pr;
     const bool exists = it < h_items;
     // W even: iw + 1 < W too
@@ -375,6 +378,109 @@ __global__ __launch_bounds__(256, (occupancy<BM, KS, SN>())) void conv16_halo_ke
   const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.r, a.r ? a.y_bytes : 0u);
   const uint32_t howo = G.Ho * G.Wo;
   const uint32_t npos = a.PH * a.PW;
+
+  // Staged epilogue.  The accumulator layout gives a lane 4 consecutive
+  // positions of one output channel, and the 32 lanes of a store hold 32
+  // channels: direct stores scatter 8-byte pieces over 32 rows of y.  When a
+  // patch spans whole output rows (PW == Wo) its positions are one contiguous
+  // run of y per channel, so the pre-activations (accumulator + bias, fp32)
+  // go through LDS as [channel][position] rows, and each thread then takes 8
+  // consecutive positions of one channel: one 16-byte load of the residual,
+  // the activation, one 16-byte store (two of each for fp32 outputs).  The
+  // same fp32 operations in the same order as the direct path: the same bits.
+  constexpr int ZSTR = 64 * SN + 4;                     // floats per channel row (+16 B: no bank conflicts)
+  static_assert(BM * ZSTR * 4 <= LDS - NDMA * 1024, "the staged tile must fit the halo buffer");
+  constexpr uint32_t E16 = 16 / Elem<DTO>::bytes;       // outputs per 16 bytes
+  const bool staged = a.PW == G.Wo && (a.PH * G.Wo) % E16 == 0 && howo % E16 == 0 &&
+                      ((reinterpret_cast<uintptr_t>(a.y) | reinterpret_cast<uintptr_t>(a.r)) & 15u) == 0;
+  if (staged) {
+    __syncthreads();                                   // every wave is done with the halo
+    float* zt = reinterpret_cast<float*>(s_halo);
+#pragma unroll
+    for (int si = 0; si < SN; ++si)
+#pragma unroll
+      for (int sj = 0; sj < SM; ++sj)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t col = wave_m * WTM + sj * 32 + lrow;
+          const uint32_t q = wave_n * WTN + si * 32 + 8 * g + 4 * half;
+          f32x4 v;
+          v.x = acc[si][sj][4 * g + 0] + bv[sj];
+          v.y = acc[si][sj][4 * g + 1] + bv[sj];
+          v.z = acc[si][sj][4 * g + 2] + bv[sj];
+          v.w = acc[si][sj][4 * g + 3] + bv[sj];
+          *reinterpret_cast<f32x4*>(zt + col * ZSTR + q) = v;
+        }
+    __syncthreads();
+    const uint32_t rows_here = G.Ho - oh0 < a.PH ? G.Ho - oh0 : a.PH;
+    const uint32_t nvalid = rows_here * G.Wo;          // this patch's positions, contiguous from (oh0, 0)
+    constexpr uint32_t CPR = 64 * SN / 8;              // groups of 8 positions per channel row
+    with_act(a.act, [&](auto act_c) __attribute__((always_inline)) {
+      constexpr int ACT = decltype(act_c)::value;
+      with_residual(a.r != nullptr, [&](auto res_c) __attribute__((always_inline)) {
+        constexpr bool HAS_R = decltype(res_c)::value;
+        for (uint32_t i = threadIdx.x; i < (uint32_t)BM * CPR; i += NTH) {
+          const uint32_t col = i / CPR, q0 = 8 * (i - col * CPR);
+          const uint32_t co = co0 + col;
+          if (co >= G.Co || q0 >= nvalid) continue;
+          const float* zp = zt + col * ZSTR + q0;
+          const f32x4 z0 = *reinterpret_cast<const f32x4*>(zp);
+          const f32x4 z1 = *reinterpret_cast<const f32x4*>(zp + 4);
+          float z[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+          const uint32_t base = (img * G.Co + co) * howo + oh0 * G.Wo + q0;
+          if (q0 + 8 <= nvalid) {
+            if constexpr (Elem<DTO>::bytes == 4) {
+              if constexpr (HAS_R) {
+                const u32x4 r0 = ld_b128(rr, base * 4u), r1 = ld_b128(rr, base * 4u + 16u);
+                z[0] += __uint_as_float(r0.x); z[1] += __uint_as_float(r0.y);
+                z[2] += __uint_as_float(r0.z); z[3] += __uint_as_float(r0.w);
+                z[4] += __uint_as_float(r1.x); z[5] += __uint_as_float(r1.y);
+                z[6] += __uint_as_float(r1.z); z[7] += __uint_as_float(r1.w);
+              }
+              u32x4 o0, o1;
+              o0.x = __float_as_uint(act_fn<ACT, DTO>(z[0], a.alpha));
+              o0.y = __float_as_uint(act_fn<ACT, DTO>(z[1], a.alpha));
+              o0.z = __float_as_uint(act_fn<ACT, DTO>(z[2], a.alpha));
+              o0.w = __float_as_uint(act_fn<ACT, DTO>(z[3], a.alpha));
+              o1.x = __float_as_uint(act_fn<ACT, DTO>(z[4], a.alpha));
+              o1.y = __float_as_uint(act_fn<ACT, DTO>(z[5], a.alpha));
+              o1.z = __float_as_uint(act_fn<ACT, DTO>(z[6], a.alpha));
+              o1.w = __float_as_uint(act_fn<ACT, DTO>(z[7], a.alpha));
+              st_b128(ry, base * 4u, o0);
+              st_b128(ry, base * 4u + 16u, o1);
+            } else {
+              if constexpr (HAS_R) {
+                const u32x4 rv = ld_b128(rr, base * 2u);
+                const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  z[2 * e] += widen<DTO>(rw[e] & 0xffffu);
+                  z[2 * e + 1] += widen<DTO>(rw[e] >> 16);
+                }
+              }
+              uint32_t o[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                o[e] = narrow<DTO>(act_fn<ACT, DTO>(z[2 * e], a.alpha)) |
+                       (narrow<DTO>(act_fn<ACT, DTO>(z[2 * e + 1], a.alpha)) << 16);
+              st_b128(ry, base * 2u, u32x4{o[0], o[1], o[2], o[3]});
+            }
+          } else {
+            // the last rows of the image end inside this group
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const bool ok = q0 + e < nvalid;
+              float ze = z[e];
+              if constexpr (HAS_R) ze += load1<DTO>(rr, base + e, ok);
+              store1<DTO>(ry, base + e, ok, act_fn<ACT, DTO>(ze, a.alpha));
+            }
+          }
+        }
+      });
+    });
+    return;
+  }
+
   auto epilogue = [&](auto act_c, auto res_c) __attribute__((always_inline)) {
     constexpr int ACT = decltype(act_c)::value;
     constexpr bool HAS_R = decltype(res_c)::value;
@@ -402,9 +508,9 @@ __global__ __launch_bounds__(256, (occupancy<BM, KS, SN>())) void conv16_halo_ke
 #pragma unroll
               for (int e = 0; e < 4; ++e) z[e] += rv[e];
             }
-            store4<DTO>(ry, ybase + oh * G.Wo + ow, ok, act_fn<ACT>(z[0], a.alpha),
-                        act_fn<ACT>(z[1], a.alpha), act_fn<ACT>(z[2], a.alpha),
-                        act_fn<ACT>(z[3], a.alpha));
+            store4<DTO>(ry, ybase + oh * G.Wo + ow, ok, act_fn<ACT, DTO>(z[0], a.alpha),
+                        act_fn<ACT, DTO>(z[1], a.alpha), act_fn<ACT, DTO>(z[2], a.alpha),
+                        act_fn<ACT, DTO>(z[3], a.alpha));
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -414,7 +520,7 @@ __global__ __launch_bounds__(256, (occupancy<BM, KS, SN>())) void conv16_halo_ke
               const bool ok = cok && qe < npos && oh < G.Ho && ow < G.Wo;
               float ze = z[e];
               if constexpr (HAS_R) ze += load1<DTO>(rr, ybase + oh * G.Wo + ow, ok);
-              store1<DTO>(ry, ybase + oh * G.Wo + ow, ok, act_fn<ACT>(ze, a.alpha));
+              store1<DTO>(ry, ybase + oh * G.Wo + ow, ok, act_fn<ACT, DTO>(ze, a.alpha));
             }
           }
         }

@@ -272,9 +272,9 @@ __global__ __launch_bounds__(256, 2) void conv32_halo_kernel(HaloArgs a) {
 #pragma unroll
               for (int e = 0; e < 4; ++e) z[e] += rv[e];
             }
-            store4<DTO>(ry, ybase + oh * G.Wo + ow, ok, act_fn<ACT>(z[0], a.alpha),
-                        act_fn<ACT>(z[1], a.alpha), act_fn<ACT>(z[2], a.alpha),
-                        act_fn<ACT>(z[3], a.alpha));
+            store4<DTO>(ry, ybase + oh * G.Wo + ow, ok, act_fn<ACT, DTO>(z[0], a.alpha),
+                        act_fn<ACT, DTO>(z[1], a.alpha), act_fn<ACT, DTO>(z[2], a.alpha),
+                        act_fn<ACT, DTO>(z[3], a.alpha));
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -284,7 +284,7 @@ __global__ __launch_bounds__(256, 2) void conv32_halo_kernel(HaloArgs a) {
               const bool ok = cok && qe < npos && oh < G.Ho && ow < G.Wo;
               float ze = z[e];
               if constexpr (HAS_R) ze += load1<DTO>(rr, ybase + oh * G.Wo + ow, ok);
-              store1<DTO>(ry, ybase + oh * G.Wo + ow, ok, act_fn<ACT>(ze, a.alpha));
+              store1<DTO>(ry, ybase + oh * G.Wo + ow, ok, act_fn<ACT, DTO>(ze, a.alpha));
             }
           }
         }

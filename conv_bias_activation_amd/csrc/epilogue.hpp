@@ -68,9 +68,9 @@ __device__ __forceinline__ float out_value(float z, float alpha) {
   if constexpr (DTI == DT_I8) {
     const int zi = __float_as_int(z);
     if constexpr (DTO == DT_I32) return __int_as_float(ACT == ACT_RELU ? (zi > 0 ? zi : 0) : zi);
-    else return act_fn<ACT>((float)zi, alpha);
+    else return act_fn<ACT, DTO>((float)zi, alpha);
   } else {
-    return act_fn<ACT>(z, alpha);
+    return act_fn<ACT, DTO>(z, alpha);
   }
 }
 

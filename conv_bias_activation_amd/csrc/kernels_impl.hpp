@@ -181,8 +181,8 @@ __global__ __launch_bounds__(TL::threads, 1) void conv_bias_act_kernel(ConvArgs 
 #pragma unroll
             for (int e = 0; e < 4; ++e) z[e] += rv[e];
           }
-          store4<DTO>(ry, off, ok, act_fn<ACT>(z[0], a.alpha), act_fn<ACT>(z[1], a.alpha),
-                      act_fn<ACT>(z[2], a.alpha), act_fn<ACT>(z[3], a.alpha));
+          store4<DTO>(ry, off, ok, act_fn<ACT, DTO>(z[0], a.alpha), act_fn<ACT, DTO>(z[1], a.alpha),
+                      act_fn<ACT, DTO>(z[2], a.alpha), act_fn<ACT, DTO>(z[3], a.alpha));
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(TL::threads, 1) void conv_bias_act_kernel(ConvArgs 
             const bool ok = cok && pe < G.P;
             float ze = z[e];
             if constexpr (HAS_R) ze += load1<DTO>(rr, off, ok);
-            store1<DTO>(ry, off, ok, act_fn<ACT>(ze, a.alpha));
+            store1<DTO>(ry, off, ok, act_fn<ACT, DTO>(ze, a.alpha));
           }
         }
       }
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(256) void act_cast_kernel(const float* ws, void* ou
       }
       float y[EPT];
 #pragma unroll
-      for (uint32_t e = 0; e < EPT; ++e) y[e] = act_fn<ACT>(z[e], alpha);
+      for (uint32_t e = 0; e < EPT; ++e) y[e] = act_fn<ACT, DTO>(z[e], alpha);
       if (full) {
 #pragma unroll
         for (uint32_t q = 0; q < EPT / 4; ++q)

@@ -246,6 +246,31 @@ def test_tanh_sweep_through_k1_gemm(ba):
     assert np.array_equal(neg, -pos)
 
 
+@pytest.mark.parametrize("to", ["f16", "bf16"])
+def test_tanh_sweep_16bit_outputs(ba, to):
+    # 16-bit outputs take the shorter tanh (series below 2^-6, the e^{2|x|}
+    # identity above): z through an fp32 K = 1 GEMM, against the oracle at one
+    # output ulp, across the switch point, the small-|z| range and saturation
+    t = np.float32(2.0 ** -6)
+    z = np.concatenate([np.array([0.0, 1e-30, 1e-8, 6e-8, 1e-5, 1e-3, 0.01, 0.5, 1.0, 4.0, 9.0, 10.0,
+                                  20.0, 89.0, 1e4, 3.4e38], np.float32),
+                        np.nextafter(t, np.float32(0)) * np.ones(1, np.float32), t * np.ones(1, np.float32),
+                        np.nextafter(t, np.float32(1)) * np.ones(1, np.float32),
+                        np.geomspace(1e-7, 12.0, 6000).astype(np.float32)])
+    z = np.concatenate([z, -z])
+    M = z.size
+    inp = {"A": wl.encode(z.reshape(M, 1), "f32"), "B": wl.encode(np.ones((1, 1), np.float32), "f32"),
+           "bias": None}
+    case = wl.GemmCase("tanh16", M, 1, 1, "f32", None, to, "tanh")
+    y = values_of(run_gemm(case, inp), to)
+    ref, acc = gemm_reference(case, inp)
+    rep = check(y, ref, acc, case)
+    _report(f"tanh sweep {to}", rep)
+    assert rep["ok"], rep
+    half = M // 2
+    assert np.array_equal(y[half:], -y[:half])               # odd
+
+
 @pytest.mark.parametrize("act", ["gelu", "sigmoid"])
 def test_gelu_sigmoid_sweep_through_k1_gemm(ba, act):
     # z through an fp32 K = 1 GEMM (A = z, B = 1, no bias): y = act(z) against
