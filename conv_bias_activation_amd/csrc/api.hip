@@ -135,6 +135,11 @@ int launch_conv_plan(const ConvPlan& p, const void* x, const void* w, const void
     h.kpad = p.h_kpad;
     h.div_kstr = make_fastdiv(p.h_kstr ? p.h_kstr : 1u);
     h.groups = p.h_groups;
+    h.div_cob = make_fastdiv(p.h_co_blocks ? p.h_co_blocks : 1u);
+    h.div_wb = make_fastdiv(p.h_w_blocks ? p.h_w_blocks : 1u);
+    h.div_hb = make_fastdiv(p.h_h_blocks ? p.h_h_blocks : 1u);
+    h.div_pw = make_fastdiv(p.h_PW ? p.h_PW : 1u);
+    h.div_pairs = make_fastdiv(p.h_HC >= 2 ? p.h_HC / 2 : 1u);
     rc = launch_conv_halo(p.dti, dto, (int)(p.kh * p.kw), (int)p.h_bm, (int)p.h_ks, (int)p.h_sn, h, s);
     if (rc) return kErrUnsupported;
     return launch_status();

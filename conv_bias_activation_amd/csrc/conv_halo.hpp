@@ -101,6 +101,7 @@ constexpr int occupancy() { return KS * (BM / 64) <= 2 && SN * (BM / 64) <= 2 ? 
 template <int DTI, int DTO, int T, int BM, int KS, int SN>
 __global__ __launch_bounds__(256, (occupancy<BM, KS, SN>())) void conv16_halo_kernel(HaloArgs a) {
   static_assert(DTI == DT_F16 || DTI == DT_BF16, "16-bit operands only");
+  static_assert(T == 1 || T == 9, "1x1 or 3x3 filters (the planner admits no other shape)");
   constexpr int WTM = BM / 2, SM = WTM / 32, WTN = 32 * SN;
   constexpr int LDS = occupancy<BM, KS, SN>() == 2 ? halo::LDS_TWO : halo::LDS_ONE;
   static_assert(KS * SM <= 4, "weight fragments of a chunk must fit in registers");
@@ -119,9 +120,14 @@ __global__ __launch_bounds__(256, (occupancy<BM, KS, SN>())) void conv16_halo_ke
 
   // workgroup -> (co block, output-column block, output-row block, image)
   uint32_t bid = blockIdx.x;
-  const uint32_t cb = bid % a.co_blocks;  bid /= a.co_blocks;
-  const uint32_t wb = bid % a.w_blocks;   bid /= a.w_blocks;
-  const uint32_t hb = bid % a.h_blocks;   bid /= a.h_blocks;
+  // (divisions by the grid's invariant block counts through FastDiv: a
+  // runtime integer division costs tens of VALU instructions)
+  uint32_t qd = fdiv(bid, a.div_cob);
+  const uint32_t cb = bid - qd * a.co_blocks;  bid = qd;
+  qd = fdiv(bid, a.div_wb);
+  const uint32_t wb = bid - qd * a.w_blocks;   bid = qd;
+  qd = fdiv(bid, a.div_hb);
+  const uint32_t hb = bid - qd * a.h_blocks;   bid = qd;
   const uint32_t img = bid;
   const uint32_t co0 = cb * BM, oh0 = hb * a.PH, ow0 = wb * a.PW;
 
@@ -148,27 +154,41 @@ __global__ __launch_bounds__(256, (occupancy<BM, KS, SN>())) void conv16_halo_ke
   // Piece P of the chunk = (row P / (RP+1), piece P % (RP+1)); the last piece
   // of a row is padding so rows start in different banks.  Padding, rows past
   // Co and channel groups past C are filled with zeros (out-of-range loads).
-  // Wave w issues the direct loads w, w + 4, ...: piece P advances by 256.
-  auto weights_to_lds = [&](uint32_t c0) {
-    constexpr uint32_t DROW = 256 / (RP + 1), DPC = 256 % (RP + 1);
-    uint32_t row = (uint32_t)(wave * 64 + lane) / (RP + 1);
-    uint32_t pc = (uint32_t)(wave * 64 + lane) - row * (RP + 1);
-    const uint32_t cbase = c0 * T * 2u;
+  // Wave w issues the direct loads w, w + 4, ...
+  constexpr int KWL = (NDMA + 3) / 4;                   // direct weight loads per wave
+  // Direct load k of this wave (load i = wave + 4k covers pieces 64i .. 64i+63).
+  // These loads are issue-bound by the VALU work of their addresses: a probe
+  // of this copy pattern moved 20 B/clk per CU with the addresses computed
+  // per load, and 52 B/clk (the rate of plain contiguous kilobytes) with them
+  // computed beforehand.  The chunk-independent part of each lane's offset is
+  // therefore computed once (kOOB for pad pieces and rows past the block), and
+  // a chunk whose channels and output-channel rows all exist (every chunk of
+  // the named convs) adds its channel offset and skips the remaining tests.
+  const bool full_co = co0 + BM <= G.Co;
+  uint32_t wofs[KWL];
 #pragma unroll
-    for (int k = 0; k < (NDMA + 3) / 4; ++k) {
-      const int i = wave + 4 * k;
-      if (i < NDMA) {
-        const bool ok = pc < RP && row < BM && co0 + row < G.Co && c0 + 8 * (pc / T) < G.C;
-        const uint32_t src = ok ? (co0 + row) * G.C * T * 2u + cbase + pc * 16u : kOOB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(s_raw + i * 1024), 16, src, 0, 0, 0);
+  for (int k = 0; k < KWL; ++k) {
+    const uint32_t P = (uint32_t)(wave + 4 * k) * 64 + lane;
+    const uint32_t row = P / (RP + 1), pc = P - row * (RP + 1);
+    wofs[k] = pc < RP && row < BM ? (co0 + row) * G.C * T * 2u + pc * 16u : kOOB;
+  }
+  auto weight_load = [&](auto k_c, uint32_t c0, bool full) {
+    constexpr int k = decltype(k_c)::value;
+    const int i = wave + 4 * k;
+    if (i < NDMA) {
+      bool ok = wofs[k] != kOOB;
+      if (!full) {
+        const uint32_t P = (uint32_t)i * 64 + lane;
+        const uint32_t row = P / (RP + 1), pc = P - row * (RP + 1);
+        ok = ok && co0 + row < G.Co && c0 + 8 * (pc / T) < G.C;
       }
-      pc += DPC;
-      row += DROW;
-      if (pc >= RP + 1) {
-        pc -= RP + 1;
-        ++row;
-      }
+      const uint32_t src = ok ? wofs[k] + c0 * T * 2u : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(s_raw + i * 1024), 16, src, 0, 0, 0);
     }
+  };
+  auto weights_to_lds = [&](uint32_t c0) {
+    const bool full = full_co && c0 + BKC <= G.C;
+    halo::unroll<KWL>([&](auto k_c) { weight_load(k_c, c0, full); });
   };
 
   // ---- input halo: item it = (halo row, channel group, column pair) --------
@@ -178,7 +198,7 @@ __global__ __launch_bounds__(256, (occupancy<BM, KS, SN>())) void conv16_halo_ke
   // 4-byte loads (one channel each) reads consecutive column pairs of one
   // input row: a wave's load covers a few cache lines, not one line per lane.
   auto halo_item = [&](uint32_t it, uint32_t& src, uint32_t& g8, uint32_t& lo, uint32_t& hi) {
-    const uint32_t pr = it % pairs, rg = it / pairs;
+    const uint32_t rg = fdiv(it, a.div_pairs), pr = it - rg * pairs;
     const uint32_t g = rg % NCH, hr = rg / NCH;
     const int32_t ih = ih_lo + (int32_t)hr, iw = iw_lo + 2 * (int32_t)pr;
     const bool exists = it < h_items;
@@ -232,13 +252,14 @@ __global__ __launch_bounds__(256, (occupancy<BM, KS, SN>())) void conv16_halo_ke
 #pragma unroll
     for (int si = 0; si < SN; ++si) {
       const uint32_t q = wave_n * WTN + si * 32 + lrow;
-      const uint32_t qh = q / a.PW, qw = q - qh * a.PW;
+      const uint32_t qh = fdiv(q, a.div_pw), qw = q - qh * a.PW;
       // lanes past the patch read halo position 0 (in range); their results are never stored
       pos[si] = q < a.PH * a.PW ? (qh * G.sh) * HC + qw * G.sw + col_shift : 0u;
     }
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      const uint32_t r = (uint32_t)t / G.kw, s = (uint32_t)t - r * G.kw;
+      constexpr uint32_t KW = T == 9 ? 3 : 1;             // 3x3 or 1x1 filters only
+      const uint32_t r = (uint32_t)t / KW, s = (uint32_t)t - r * KW;
       const uint32_t tap = (r * G.dh) * HC + s * G.dw;
 #pragma unroll
       for (int si = 0; si < SN; ++si) {
@@ -304,16 +325,25 @@ __global__ __launch_bounds__(256, (occupancy<BM, KS, SN>())) void conv16_halo_ke
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[si][sj][r] = 0.0f;
 
-  // All KS * T steps of one chunk (k-step major); with PREFETCH the input
-  // batch of the chunk at channel c1 rides along, PER loads per step.
+  // All KS * T steps of one chunk (k-step major); with PREFETCH the weight
+  // copy and the input batch of the chunk at channel c1 ride along (WPS
+  // direct loads and PER input loads per step), so their issue, which waits
+  // whenever the memory pipeline is full, stays behind the MFMAs.
+  constexpr int WPS = (KWL + NSTEP - 1) / NSTEP;
   auto multiply = [&](auto prefetch_c, uint32_t c1) {
     constexpr bool PREFETCH = decltype(prefetch_c)::value;
+    const bool full = full_co && c1 + BKC <= G.C;
     u32x4 fi[2][SN];
     load_b(std::integral_constant<int, 0>{}, fi[0]);
     halo::unroll<NSTEP>([&](auto st_c) {
       constexpr int st = decltype(st_c)::value;
       constexpr int cur = st & 1, ks = st / T, t = st % T;
       if constexpr (st + 1 < NSTEP) load_b(std::integral_constant<int, st + 1>{}, fi[cur ^ 1]);
+      constexpr int w0 = PREFETCH ? (st * WPS < KWL ? st * WPS : KWL) : 0;
+      constexpr int w1 = PREFETCH ? ((st + 1) * WPS < KWL ? (st + 1) * WPS : KWL) : 0;
+      halo::unroll<w1 - w0>([&](auto k_c) {
+        weight_load(std::integral_constant<int, w0 + decltype(k_c)::value>{}, c1, full);
+      });
       constexpr int v0 = PREFETCH ? (st * PER < NPF ? st * PER : NPF) : 0;
       constexpr int v1 = PREFETCH ? ((st + 1) * PER < NPF ? (st + 1) * PER : NPF) : 0;
       halo::unroll<v1 - v0>([&](auto k_c) {
@@ -323,7 +353,7 @@ __global__ __launch_bounds__(256, (occupancy<BM, KS, SN>())) void conv16_halo_ke
       for (int si = 0; si < SN; ++si)
 #pragma unroll
         for (int sj = 0; sj < SM; ++sj) mfma_chunk<DTI>(acc[si][sj], fi[cur][si], afr[ks][t][sj]);
-      halo::interleave<SN * SM, st + 1 < NSTEP ? SN : 0, v1 - v0>();
+      halo::interleave<SN * SM, st + 1 < NSTEP ? SN : 0, (v1 - v0) + (w1 - w0)>();
       __builtin_amdgcn_sched_barrier(0);
     });
   };
@@ -361,8 +391,7 @@ __global__ __launch_bounds__(256, (occupancy<BM, KS, SN>())) void conv16_halo_ke
     build_weights();
     if (more) {
       __syncthreads();                                 // every wave has its fragments: reuse the raw rows
-      weights_to_lds(c0 + BKC);
-      multiply(std::true_type{}, c0 + BKC);
+      multiply(std::true_type{}, c0 + BKC);            // copies the next chunk's weights as it goes
     } else {
       multiply(std::false_type{}, 0u);
     }
@@ -499,7 +528,7 @@ __global__ __launch_bounds__(256, (occupancy<BM, KS, SN>())) void conv16_halo_ke
           for (int e = 0; e < 4; ++e) z[e] = acc[si][sj][4 * g + e] + bv[sj];
           if (a.vec_y) {
             // PW % 4 == 0 and Wo % 4 == 0: positions q..q+3 share an output row
-            const uint32_t qh = q / a.PW, qw = q - qh * a.PW;
+            const uint32_t qh = fdiv(q, a.div_pw), qw = q - qh * a.PW;
             const uint32_t oh = oh0 + qh, ow = ow0 + qw;
             const bool ok = cok && q < npos && oh < G.Ho && ow < G.Wo;
             if constexpr (HAS_R) {
@@ -515,7 +544,7 @@ __global__ __launch_bounds__(256, (occupancy<BM, KS, SN>())) void conv16_halo_ke
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const uint32_t qe = q + e;
-              const uint32_t qh = qe / a.PW, qw = qe - qh * a.PW;
+              const uint32_t qh = fdiv(qe, a.div_pw), qw = qe - qh * a.PW;
               const uint32_t oh = oh0 + qh, ow = ow0 + qw;
               const bool ok = cok && qe < npos && oh < G.Ho && ow < G.Wo;
               float ze = z[e];

@@ -43,6 +43,8 @@ struct HaloArgs {
   uint32_t co_blocks, w_blocks, h_blocks, blocks;
   uint32_t groups;          // fp32 kernel: workgroups of a resident-filter grid (0: one patch each)
   bool vec_y;               // Wo % 4 == 0 and y aligned for 4-element stores
+  // 16-bit kernel: divisions by workgroup-invariant values (FastDiv)
+  FastDiv div_cob, div_wb, div_hb, div_pw, div_pairs;
   // fp32 kernel only
   uint32_t hrcp;            // halo floats per channel (HR * HC rounded up to 64)
   FastDiv div_hc;

@@ -146,7 +146,7 @@ bool plan_halo(ConvPlan* p, const void* x, const void* w) {
   if (p->dti == kF32) return plan_halo32(p, x, w);
   if (p->C % 8 != 0 || p->W % 2 != 0) return false;
   const uint32_t T = p->kh * p->kw;
-  if (T != 1 && T != 9) return false;
+  if (!((p->kh == 1 && p->kw == 1) || (p->kh == 3 && p->kw == 3))) return false;   // 1x1 or 3x3
   if (!aligned(x, 4) || !aligned(w, 16)) return false;
   // One configuration = (bm output channels, 2 x 32 sn positions, LDS budget).
   // LDS: the halo (HR x HC positions x bkc channels) and one raw weight chunk

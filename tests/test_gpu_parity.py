@@ -324,6 +324,8 @@ CONV_SHAPES = [
     (1, 3, 31, 29, 64, 7, 7, (2, 2), (3, 3, 3, 3), (1, 1)),
     (2, 64, 14, 14, 64, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1)),
     (1, 40, 9, 9, 136, 3, 3, (1, 1), (2, 2, 2, 2), (2, 2)),
+    (1, 16, 6, 20, 24, 1, 9, (1, 1), (0, 0, 4, 4), (1, 1)),     # 9 taps, not 3x3: the generic kernel
+    (1, 16, 20, 6, 24, 9, 1, (1, 1), (4, 4, 0, 0), (1, 1)),
 ]
 CONV_TYPES = [("f16", "f16", "f16"), ("bf16", "bf16", "bf16"), ("f32", "f32", "f32"),
               ("f16", "f32", "f32"), ("bf16", "bf16", "f32")]
