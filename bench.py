@@ -129,6 +129,8 @@ def _parse():
     ap.add_argument("--tile", type=int, default=-1, help="force a tile config (tuning)")
     ap.add_argument("--fingerprint", default=None, metavar="KERNEL",
                     help="print the source hash of a kernel (e.g. gemm16_pp_kernel) and exit")
+    ap.add_argument("--launch-floor", action="store_true",
+                    help="only measure the trivial-kernel launch floor (eager and graph replays) and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a device copy of 256 MiB (read 256 MiB + write 256 MiB) --steps "
                          "times; its FETCH_SIZE / WRITE_SIZE counters scale the kernel's counters "
@@ -492,6 +494,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes_read": n, "calibrate_copy_bytes_written": n,
                           "launches": args.steps}), flush=True)
+        return
+    if args.launch_floor:
+        print(json.dumps({"launch_floor": launch_floor()}), flush=True)
         return
     import conv_bias_activation_amd as ba
     import workloads as wl
