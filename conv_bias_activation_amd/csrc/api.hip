@@ -140,7 +140,7 @@ int launch_conv_plan(const ConvPlan& p, const void* x, const void* w, const void
     h.div_hb = make_fastdiv(p.h_h_blocks ? p.h_h_blocks : 1u);
     h.div_pw = make_fastdiv(p.h_PW ? p.h_PW : 1u);
     h.div_pairs = make_fastdiv(p.h_HC >= 2 ? p.h_HC / 2 : 1u);
-    rc = launch_conv_halo(p.dti, dto, (int)(p.kh * p.kw), (int)p.h_bm, (int)p.h_ks, (int)p.h_sn, h, s);
+    rc = launch_conv_halo(p.dti, dto, (int)(p.kh * p.kw), (int)p.h_bm, (int)p.h_ks, (int)p.h_sn, (int)p.h_nw, h, s);
     if (rc) return kErrUnsupported;
     return launch_status();
   }
@@ -629,7 +629,7 @@ int biasact_force_tile_config(int id) {
 }
 
 int biasact_force_halo_variant(int v) {
-  if (v < -1 || v > 2) return kErrInvalid;
+  if (v < -1 || v > 3) return kErrInvalid;
   set_forced_halo_variant(v);
   return kOk;
 }

@@ -5,7 +5,7 @@ namespace biasact {
 int launch_conv_f16_f32(int tile, const ConvArgs& a, hipStream_t s) {
   return launch_conv_tile<DT_F16, DT_F32>(tile, a, s);
 }
-int launch_conv_halo_f16_f32(int taps, int bm, int ks, int sn, const HaloArgs& a, hipStream_t s) {
-  return launch_conv_halo_tile<DT_F16, DT_F32>(taps, bm, ks, sn, a, s);
+int launch_conv_halo_f16_f32(int taps, int bm, int ks, int sn, int nw, const HaloArgs& a, hipStream_t s) {
+  return launch_conv_halo_tile<DT_F16, DT_F32>(taps, bm, ks, sn, nw, a, s);
 }
 }  // namespace biasact

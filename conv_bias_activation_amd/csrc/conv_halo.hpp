@@ -15,11 +15,13 @@
 // chunk instead of once per tap.  Channels are staged in chunks of
 // BKC = 16 * KS (KS = 1, 2, 4 MFMA k-steps per tap; zero-filled past C).
 //
-// Workgroup: 256 threads (2 x 2 waves), BM output channels x a patch of PH
-// output rows x PW output columns (positions q = row * PW + col, at most
-// 64 * SN).  Variants small enough for two workgroups per CU (80 KB of LDS,
+// Workgroup: NW = 4 or 8 waves as 2 (output-channel halves) x NW / 2
+// (position groups), BM output channels x a patch of PH output rows x PW
+// output columns (positions q = row * PW + col, at most 32 * SN * NW / 2).
+// Four-wave variants small enough for two workgroups per CU (80 KB of LDS,
 // two fragment sets per wave) let one workgroup's staging and epilogue
-// overlap another's MFMAs.
+// overlap another's MFMAs; the eight-wave variant has its CU alone with two
+// waves per SIMD, which fetches each weight chunk once per CU.
 // Staging items: input (halo row, column pair, 8 channels) — eight 4-byte
 // loads transposed in registers into two 16-byte LDS writes; weights (output
 // channel, 8 channels) — T 16-byte loads (8 channels x T taps are contiguous
@@ -48,7 +50,6 @@
 namespace biasact {
 
 namespace halo {
-constexpr int THREADS = 256;
 constexpr int LDS_ONE = 144 * 1024;     // LDS of a workgroup that has its CU alone
 constexpr int LDS_TWO = 80 * 1024;      // LDS of a workgroup that shares its CU with another
 constexpr int HB = 4;     // input items per thread in the precomputed batch (2 at occupancy 2)
@@ -90,24 +91,29 @@ __device__ __forceinline__ void interleave() {
 }
 }  // namespace halo
 
-// Two workgroups share a CU when a wave holds at most two weight-fragment
-// sets and two accumulator tiles (then 256 registers per lane suffice).
-template <int BM, int KS, int SN>
-constexpr int occupancy() { return KS * (BM / 64) <= 2 && SN * (BM / 64) <= 2 ? 2 : 1; }
+// Two four-wave workgroups share a CU when a wave holds at most two
+// weight-fragment sets and two accumulator tiles (then 256 registers per lane
+// suffice); an eight-wave workgroup has its CU alone (two waves per SIMD).
+template <int BM, int KS, int SN, int NW = 4>
+constexpr int occupancy() { return NW == 4 && KS * (BM / 64) <= 2 && SN * (BM / 64) <= 2 ? 2 : 1; }
 
 // T = taps (kh*kw: 1 or 9), BM = output channels per workgroup (64 or 128),
 // KS = 16-channel k-steps per tap and chunk (1, 2 or 4; KS * BM / 64 <= 4),
-// SN = 32-position MFMA tiles per wave (2 x SN x 32 positions per workgroup).
-template <int DTI, int DTO, int T, int BM, int KS, int SN>
-__global__ __launch_bounds__(256, (occupancy<BM, KS, SN>())) void conv16_halo_kernel(HaloArgs a) {
+// SN = 32-position MFMA tiles per wave, NW = waves (4 or 8) as a grid of 2
+// (output-channel halves) x NW / 2 (position groups): NW / 2 x SN x 32
+// positions per workgroup.
+template <int DTI, int DTO, int T, int BM, int KS, int SN, int NW>
+__global__ __launch_bounds__(NW * 64, (occupancy<BM, KS, SN, NW>())) void conv16_halo_kernel(HaloArgs a) {
   static_assert(DTI == DT_F16 || DTI == DT_BF16, "16-bit operands only");
   static_assert(T == 1 || T == 9, "1x1 or 3x3 filters (the planner admits no other shape)");
   constexpr int WTM = BM / 2, SM = WTM / 32, WTN = 32 * SN;
-  constexpr int LDS = occupancy<BM, KS, SN>() == 2 ? halo::LDS_TWO : halo::LDS_ONE;
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
+  constexpr int LDS = occupancy<BM, KS, SN, NW>() == 2 ? halo::LDS_TWO : halo::LDS_ONE;
+  constexpr int WGN = NW / 2;                           // position groups
   static_assert(KS * SM <= 4, "weight fragments of a chunk must fit in registers");
   constexpr int BKC = 16 * KS, NCH = 2 * KS, ROWB = NCH * 16;
   constexpr int NSTEP = T * KS;
-  constexpr int HB = occupancy<BM, KS, SN>() == 2 ? 2 : halo::HB, NTH = halo::THREADS;
+  constexpr int HB = occupancy<BM, KS, SN, NW>() == 2 || NW == 8 ? 2 : halo::HB, NTH = NW * 64;
   constexpr int RP = BKC * T / 8;                       // 16-byte pieces of one weight row
   constexpr int RSTR = (RP + 1) * 16;                   // row stride: the pieces and a pad
   constexpr int NPIECE = BM * (RP + 1);
@@ -133,7 +139,7 @@ __global__ __launch_bounds__(256, (occupancy<BM, KS, SN>())) void conv16_halo_ke
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wave_m = wave >> 1, wave_n = wave & 1;
+  const int wave_m = wave / WGN, wave_n = wave % WGN;
   const int half = lane >> 5, lrow = lane & 31;
 
   // halo geometry of this patch
@@ -155,40 +161,35 @@ __global__ __launch_bounds__(256, (occupancy<BM, KS, SN>())) void conv16_halo_ke
   // of a row is padding so rows start in different banks.  Padding, rows past
   // Co and channel groups past C are filled with zeros (out-of-range loads).
   // Wave w issues the direct loads w, w + 4, ...
-  constexpr int KWL = (NDMA + 3) / 4;                   // direct weight loads per wave
-  // Direct load k of this wave (load i = wave + 4k covers pieces 64i .. 64i+63).
-  // These loads are issue-bound by the VALU work of their addresses: a probe
-  // of this copy pattern moved 20 B/clk per CU with the addresses computed
-  // per load, and 52 B/clk (the rate of plain contiguous kilobytes) with them
-  // computed beforehand.  The chunk-independent part of each lane's offset is
-  // therefore computed once (kOOB for pad pieces and rows past the block), and
-  // a chunk whose channels and output-channel rows all exist (every chunk of
-  // the named convs) adds its channel offset and skips the remaining tests.
-  const bool full_co = co0 + BM <= G.Co;
-  uint32_t wofs[KWL];
+  constexpr int KWL = (NDMA + NW - 1) / NW;             // direct weight loads per wave
+  // Direct load k of this wave (load i = wave + NW k covers pieces 64i .. 64i+63).
+  // Each lane's offset within the chunk is computed once (kOOB for pad
+  // pieces and rows past Co) with the first channel of its piece; a chunk at
+  // channel c0 then passes c0 * T * 2 as the scalar offset of the load, and a
+  // lane whose channels lie past C (a partial last chunk) passes kOOB.  The
+  // issue of these loads is bound by the vector instructions of their
+  // addresses (a probe of this copy moved 20 B/clk per CU with the addresses
+  // computed per load and 52 B/clk with them computed beforehand).
+  uint32_t wofs[KWL], wch[KWL];
 #pragma unroll
   for (int k = 0; k < KWL; ++k) {
-    const uint32_t P = (uint32_t)(wave + 4 * k) * 64 + lane;
+    const uint32_t P = (uint32_t)(wave + NW * k) * 64 + lane;
     const uint32_t row = P / (RP + 1), pc = P - row * (RP + 1);
-    wofs[k] = pc < RP && row < BM ? (co0 + row) * G.C * T * 2u + pc * 16u : kOOB;
+    const bool ok = pc < RP && row < BM && co0 + row < G.Co;
+    wofs[k] = ok ? (co0 + row) * G.C * T * 2u + pc * 16u : kOOB;
+    wch[k] = ok ? 8 * (pc / T) : halo::kFar;
   }
-  auto weight_load = [&](auto k_c, uint32_t c0, bool full) {
+  // lim = channels left from c0 (0: issue the loads but fetch nothing)
+  auto weight_load = [&](auto k_c, uint32_t c0, uint32_t lim) {
     constexpr int k = decltype(k_c)::value;
-    const int i = wave + 4 * k;
-    if (i < NDMA) {
-      bool ok = wofs[k] != kOOB;
-      if (!full) {
-        const uint32_t P = (uint32_t)i * 64 + lane;
-        const uint32_t row = P / (RP + 1), pc = P - row * (RP + 1);
-        ok = ok && co0 + row < G.Co && c0 + 8 * (pc / T) < G.C;
-      }
-      const uint32_t src = ok ? wofs[k] + c0 * T * 2u : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(s_raw + i * 1024), 16, src, 0, 0, 0);
+    const int li = wave + NW * k;
+    if (k + 1 < KWL || li < NDMA) {                    // only the last load can be past the chunk
+      const uint32_t src = wch[k] < lim ? wofs[k] : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(s_raw + li * 1024), 16, src, c0 * T * 2u, 0, 0);
     }
   };
-  auto weights_to_lds = [&](uint32_t c0) {
-    const bool full = full_co && c0 + BKC <= G.C;
-    halo::unroll<KWL>([&](auto k_c) { weight_load(k_c, c0, full); });
+  auto weights_to_lds = [&](uint32_t c0, uint32_t lim) {
+    halo::unroll<KWL>([&](auto k_c) { weight_load(k_c, c0, lim); });
   };
 
   // ---- input halo: item it = (halo row, channel group, column pair) --------
@@ -237,11 +238,19 @@ __global__ __launch_bounds__(256, (occupancy<BM, KS, SN>())) void conv16_halo_ke
   uint32_t hd_src[HB], hd_g8[HB], hd_lo[HB], hd_hi[HB];
 #pragma unroll
   for (int b = 0; b < HB; ++b) halo_item(b * NTH + threadIdx.x, hd_src[b], hd_g8[b], hd_lo[b], hd_hi[b]);
-  // load number i of the batch of the chunk starting at channel c0
+  // Batch of the chunk at channel c0 with lim channels left from c0 (0: fetch
+  // nothing): per item the x offset of its channel group at chunk 0, or kOOB
+  // (set once per chunk); load e of the item adds (c0 + e) * HW2 as the scalar
+  // offset of the load.  (kOOB plus a scalar offset below 2^31 stays past
+  // every buffer: all tensors are smaller than 2^31 bytes.)
+  uint32_t hbase[HB];
+  auto batch_bases = [&](uint32_t lim) {
+#pragma unroll
+    for (int b = 0; b < HB; ++b) hbase[b] = hd_g8[b] < lim ? hd_src[b] : kOOB;
+  };
   auto batch_load = [&](auto i_c, uint32_t c0) {
     constexpr int b = decltype(i_c)::value / 8, e = decltype(i_c)::value % 8;
-    const bool ok = hd_src[b] != kOOB && c0 + hd_g8[b] < G.C;
-    hreg[b][e] = ld_b32(rx, ok ? hd_src[b] + (c0 + e) * HW2 : kOOB);
+    hreg[b][e] = __builtin_amdgcn_raw_buffer_load_b32(rx, hbase[b], (c0 + e) * HW2, 0);
   };
 
   // ---- fragment addresses --------------------------------------------------
@@ -317,49 +326,61 @@ __global__ __launch_bounds__(256, (occupancy<BM, KS, SN>())) void conv16_halo_ke
       fi[si] = *reinterpret_cast<const u32x4*>(s_halo + (h_addr[t][si] ^ flip));
   };
 
-  f32x16 acc[SN][SM];
+  // Accumulators.  A wave with a single 32x32 tile alternates two of them
+  // between consecutive steps: an MFMA that waits for the previous one's
+  // result issues about a third slower than one that does not.
+  constexpr int NACC = SN * SM == 1 ? 2 : 1;
+  f32x16 acc[NACC][SN][SM];
 #pragma unroll
-  for (int si = 0; si < SN; ++si)
+  for (int c = 0; c < NACC; ++c)
 #pragma unroll
-    for (int sj = 0; sj < SM; ++sj)
+    for (int si = 0; si < SN; ++si)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[si][sj][r] = 0.0f;
+      for (int sj = 0; sj < SM; ++sj)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[c][si][sj][r] = 0.0f;
 
-  // All KS * T steps of one chunk (k-step major); with PREFETCH the weight
-  // copy and the input batch of the chunk at channel c1 ride along (WPS
-  // direct loads and PER input loads per step), so their issue, which waits
-  // whenever the memory pipeline is full, stays behind the MFMAs.
+  // All KS * T steps of one chunk (k-step major).  The weight copy and the
+  // input batch of the chunk at channel c1 (lim1 channels left from c1; 0 past
+  // the last chunk: then the loads fetch nothing) ride along, WPS direct loads
+  // and PER input loads per step, so their issue, which waits whenever the
+  // memory pipeline is full, stays behind the MFMAs.  One instance of the
+  // step sequence for every chunk keeps the accumulators in the same
+  // registers throughout.
   constexpr int WPS = (KWL + NSTEP - 1) / NSTEP;
-  auto multiply = [&](auto prefetch_c, uint32_t c1) {
-    constexpr bool PREFETCH = decltype(prefetch_c)::value;
-    const bool full = full_co && c1 + BKC <= G.C;
-    u32x4 fi[2][SN];
-    load_b(std::integral_constant<int, 0>{}, fi[0]);
+  constexpr int PD = NSTEP >= 3 ? 2 : 1, NB = PD + 1;
+  auto multiply = [&](uint32_t c1, uint32_t lim1) {
+    batch_bases(lim1);
+    // fragments are read PD steps ahead: one step's MFMAs are too short to
+    // cover the latency of an LDS read
+    u32x4 fi[NB][SN];
+    halo::unroll<PD>([&](auto j_c) { load_b(j_c, fi[decltype(j_c)::value]); });
     halo::unroll<NSTEP>([&](auto st_c) {
       constexpr int st = decltype(st_c)::value;
-      constexpr int cur = st & 1, ks = st / T, t = st % T;
-      if constexpr (st + 1 < NSTEP) load_b(std::integral_constant<int, st + 1>{}, fi[cur ^ 1]);
-      constexpr int w0 = PREFETCH ? (st * WPS < KWL ? st * WPS : KWL) : 0;
-      constexpr int w1 = PREFETCH ? ((st + 1) * WPS < KWL ? (st + 1) * WPS : KWL) : 0;
+      constexpr int cur = st % NB, ks = st / T, t = st % T;
+      if constexpr (st + PD < NSTEP) load_b(std::integral_constant<int, st + PD>{}, fi[(st + PD) % NB]);
+      constexpr int w0 = st * WPS < KWL ? st * WPS : KWL;
+      constexpr int w1 = (st + 1) * WPS < KWL ? (st + 1) * WPS : KWL;
       halo::unroll<w1 - w0>([&](auto k_c) {
-        weight_load(std::integral_constant<int, w0 + decltype(k_c)::value>{}, c1, full);
+        weight_load(std::integral_constant<int, w0 + decltype(k_c)::value>{}, c1, lim1);
       });
-      constexpr int v0 = PREFETCH ? (st * PER < NPF ? st * PER : NPF) : 0;
-      constexpr int v1 = PREFETCH ? ((st + 1) * PER < NPF ? (st + 1) * PER : NPF) : 0;
+      constexpr int v0 = st * PER < NPF ? st * PER : NPF;
+      constexpr int v1 = (st + 1) * PER < NPF ? (st + 1) * PER : NPF;
       halo::unroll<v1 - v0>([&](auto k_c) {
         batch_load(std::integral_constant<int, v0 + decltype(k_c)::value>{}, c1);
       });
 #pragma unroll
       for (int si = 0; si < SN; ++si)
 #pragma unroll
-        for (int sj = 0; sj < SM; ++sj) mfma_chunk<DTI>(acc[si][sj], fi[cur][si], afr[ks][t][sj]);
-      halo::interleave<SN * SM, st + 1 < NSTEP ? SN : 0, (v1 - v0) + (w1 - w0)>();
+        for (int sj = 0; sj < SM; ++sj) mfma_chunk<DTI>(acc[st % NACC][si][sj], fi[cur][si], afr[ks][t][sj]);
+      halo::interleave<SN * SM, st + PD < NSTEP ? SN : 0, (v1 - v0) + (w1 - w0)>();
       __builtin_amdgcn_sched_barrier(0);
     });
   };
 
   // ---- chunk loop ------------------------------------------------------------
-  weights_to_lds(0);
+  weights_to_lds(0u, G.C);
+  batch_bases(G.C);
   halo::unroll<NPF>([&](auto i_c) { batch_load(i_c, 0u); });
   // raw bias words of this lane's output channels, converted in the epilogue
   uint32_t braw[SM];
@@ -374,8 +395,7 @@ __global__ __launch_bounds__(256, (occupancy<BM, KS, SN>())) void conv16_halo_ke
     }
   }
   for (uint32_t ck = 0; ck < nchunks; ++ck) {
-    const uint32_t c0 = ck * BKC;
-    const bool more = ck + 1 < nchunks;
+    const uint32_t c0 = ck * BKC, c1 = c0 + BKC;
     if (ck > 0) __syncthreads();                       // the previous multiply is done with the halo
 #pragma unroll
     for (int b = 0; b < HB; ++b) halo_store1(hreg[b], hd_lo[b], hd_hi[b]);
@@ -389,12 +409,16 @@ __global__ __launch_bounds__(256, (occupancy<BM, KS, SN>())) void conv16_halo_ke
     __builtin_amdgcn_s_waitcnt(0x0F70);                // this thread's direct weight loads have landed
     __syncthreads();
     build_weights();
-    if (more) {
-      __syncthreads();                                 // every wave has its fragments: reuse the raw rows
-      multiply(std::true_type{}, c0 + BKC);            // copies the next chunk's weights as it goes
-    } else {
-      multiply(std::false_type{}, 0u);
-    }
+    __syncthreads();                                   // every wave has its fragments: reuse the raw rows
+    multiply(c1, c1 < G.C ? G.C - c1 : 0u);            // copies the next chunk's weights as it goes
+  }
+
+  // the last multiply issued loads that fetch nothing (past the last chunk):
+  // let them land before the workgroup can end
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  if constexpr (NACC == 2) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[0][0][0][r] += acc[1][0][0][r];
   }
 
   // ---- epilogue: bias, activation, cast, store -------------------------------
@@ -417,7 +441,7 @@ __global__ __launch_bounds__(256, (occupancy<BM, KS, SN>())) void conv16_halo_ke
   // consecutive positions of one channel: one 16-byte load of the residual,
   // the activation, one 16-byte store (two of each for fp32 outputs).  The
   // same fp32 operations in the same order as the direct path: the same bits.
-  constexpr int ZSTR = 64 * SN + 4;                     // floats per channel row (+16 B: no bank conflicts)
+  constexpr int ZSTR = WGN * 32 * SN + 4;               // floats per channel row (+16 B: no bank conflicts)
   static_assert(BM * ZSTR * 4 <= LDS - NDMA * 1024, "the staged tile must fit the halo buffer");
   constexpr uint32_t E16 = 16 / Elem<DTO>::bytes;       // outputs per 16 bytes
   const bool staged = a.PW == G.Wo && (a.PH * G.Wo) % E16 == 0 && howo % E16 == 0 &&
@@ -434,16 +458,16 @@ __global__ __launch_bounds__(256, (occupancy<BM, KS, SN>())) void conv16_halo_ke
           const uint32_t col = wave_m * WTM + sj * 32 + lrow;
           const uint32_t q = wave_n * WTN + si * 32 + 8 * g + 4 * half;
           f32x4 v;
-          v.x = acc[si][sj][4 * g + 0] + bv[sj];
-          v.y = acc[si][sj][4 * g + 1] + bv[sj];
-          v.z = acc[si][sj][4 * g + 2] + bv[sj];
-          v.w = acc[si][sj][4 * g + 3] + bv[sj];
+          v.x = acc[0][si][sj][4 * g + 0] + bv[sj];
+          v.y = acc[0][si][sj][4 * g + 1] + bv[sj];
+          v.z = acc[0][si][sj][4 * g + 2] + bv[sj];
+          v.w = acc[0][si][sj][4 * g + 3] + bv[sj];
           *reinterpret_cast<f32x4*>(zt + col * ZSTR + q) = v;
         }
     __syncthreads();
     const uint32_t rows_here = G.Ho - oh0 < a.PH ? G.Ho - oh0 : a.PH;
     const uint32_t nvalid = rows_here * G.Wo;          // this patch's positions, contiguous from (oh0, 0)
-    constexpr uint32_t CPR = 64 * SN / 8;              // groups of 8 positions per channel row
+    constexpr uint32_t CPR = WGN * 32 * SN / 8;        // groups of 8 positions per channel row
     with_act(a.act, [&](auto act_c) __attribute__((always_inline)) {
       constexpr int ACT = decltype(act_c)::value;
       with_residual(a.r != nullptr, [&](auto res_c) __attribute__((always_inline)) {
@@ -525,7 +549,7 @@ __global__ __launch_bounds__(256, (occupancy<BM, KS, SN>())) void conv16_halo_ke
           const uint32_t q = wave_n * WTN + si * 32 + 8 * g + 4 * half;
           float z[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) z[e] = acc[si][sj][4 * g + e] + bv[sj];
+          for (int e = 0; e < 4; ++e) z[e] = acc[0][si][sj][4 * g + e] + bv[sj];
           if (a.vec_y) {
             // PW % 4 == 0 and Wo % 4 == 0: positions q..q+3 share an output row
             const uint32_t qh = fdiv(q, a.div_pw), qw = q - qh * a.PW;
@@ -562,11 +586,11 @@ __global__ __launch_bounds__(256, (occupancy<BM, KS, SN>())) void conv16_halo_ke
   });
 }
 
-template <int DTI, int DTO, int T, int BM, int KS, int SN>
+template <int DTI, int DTO, int T, int BM, int KS, int SN, int NW = 4>
 inline void launch_conv_halo_t(const HaloArgs& a, hipStream_t s) {
-  note_launch("conv-halo %d taps, %d co x %ux%u positions, %d chunk set%s", T, BM, a.PH, a.PW, KS,
-              KS > 1 ? "s" : "");
-  launch_kernel(conv16_halo_kernel<DTI, DTO, T, BM, KS, SN>, dim3(a.blocks), dim3(halo::THREADS), s, a);
+  note_launch("conv-halo %d taps, %d co x %ux%u positions, %d chunk set%s, %d waves", T, BM, a.PH, a.PW, KS,
+              KS > 1 ? "s" : "", NW);
+  launch_kernel(conv16_halo_kernel<DTI, DTO, T, BM, KS, SN, NW>, dim3(a.blocks), dim3(NW * 64), s, a);
 }
 
 }  // namespace biasact

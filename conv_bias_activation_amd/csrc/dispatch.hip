@@ -90,26 +90,26 @@ int launch_conv_bf16(int dto, int tile, const ConvArgs& a, hipStream_t s) {
   }
 }
 
-int launch_conv_halo_f32_f32(int taps, int bm, int ks, int sn, const HaloArgs& a, hipStream_t s);
-int launch_conv_halo_f32_f16(int taps, int bm, int ks, int sn, const HaloArgs& a, hipStream_t s);
-int launch_conv_halo_f32_bf16(int taps, int bm, int ks, int sn, const HaloArgs& a, hipStream_t s);
-int launch_conv_halo_f16_f32(int taps, int bm, int ks, int sn, const HaloArgs& a, hipStream_t s);
-int launch_conv_halo_f16_f16(int taps, int bm, int ks, int sn, const HaloArgs& a, hipStream_t s);
-int launch_conv_halo_f16_bf16(int taps, int bm, int ks, int sn, const HaloArgs& a, hipStream_t s);
-int launch_conv_halo_bf16_f32(int taps, int bm, int ks, int sn, const HaloArgs& a, hipStream_t s);
-int launch_conv_halo_bf16_f16(int taps, int bm, int ks, int sn, const HaloArgs& a, hipStream_t s);
-int launch_conv_halo_bf16_bf16(int taps, int bm, int ks, int sn, const HaloArgs& a, hipStream_t s);
+int launch_conv_halo_f32_f32(int taps, int bm, int ks, int sn, int nw, const HaloArgs& a, hipStream_t s);
+int launch_conv_halo_f32_f16(int taps, int bm, int ks, int sn, int nw, const HaloArgs& a, hipStream_t s);
+int launch_conv_halo_f32_bf16(int taps, int bm, int ks, int sn, int nw, const HaloArgs& a, hipStream_t s);
+int launch_conv_halo_f16_f32(int taps, int bm, int ks, int sn, int nw, const HaloArgs& a, hipStream_t s);
+int launch_conv_halo_f16_f16(int taps, int bm, int ks, int sn, int nw, const HaloArgs& a, hipStream_t s);
+int launch_conv_halo_f16_bf16(int taps, int bm, int ks, int sn, int nw, const HaloArgs& a, hipStream_t s);
+int launch_conv_halo_bf16_f32(int taps, int bm, int ks, int sn, int nw, const HaloArgs& a, hipStream_t s);
+int launch_conv_halo_bf16_f16(int taps, int bm, int ks, int sn, int nw, const HaloArgs& a, hipStream_t s);
+int launch_conv_halo_bf16_bf16(int taps, int bm, int ks, int sn, int nw, const HaloArgs& a, hipStream_t s);
 
-int launch_conv_halo(int dti, int dto, int taps, int bm, int ks, int sn, const HaloArgs& a, hipStream_t s) {
-  if (dti == DT_F32 && dto == DT_F32) return launch_conv_halo_f32_f32(taps, bm, ks, sn, a, s);
-  if (dti == DT_F32 && dto == DT_F16) return launch_conv_halo_f32_f16(taps, bm, ks, sn, a, s);
-  if (dti == DT_F32 && dto == DT_BF16) return launch_conv_halo_f32_bf16(taps, bm, ks, sn, a, s);
-  if (dti == DT_F16 && dto == DT_F32) return launch_conv_halo_f16_f32(taps, bm, ks, sn, a, s);
-  if (dti == DT_F16 && dto == DT_F16) return launch_conv_halo_f16_f16(taps, bm, ks, sn, a, s);
-  if (dti == DT_F16 && dto == DT_BF16) return launch_conv_halo_f16_bf16(taps, bm, ks, sn, a, s);
-  if (dti == DT_BF16 && dto == DT_F32) return launch_conv_halo_bf16_f32(taps, bm, ks, sn, a, s);
-  if (dti == DT_BF16 && dto == DT_F16) return launch_conv_halo_bf16_f16(taps, bm, ks, sn, a, s);
-  if (dti == DT_BF16 && dto == DT_BF16) return launch_conv_halo_bf16_bf16(taps, bm, ks, sn, a, s);
+int launch_conv_halo(int dti, int dto, int taps, int bm, int ks, int sn, int nw, const HaloArgs& a, hipStream_t s) {
+  if (dti == DT_F32 && dto == DT_F32) return launch_conv_halo_f32_f32(taps, bm, ks, sn, nw, a, s);
+  if (dti == DT_F32 && dto == DT_F16) return launch_conv_halo_f32_f16(taps, bm, ks, sn, nw, a, s);
+  if (dti == DT_F32 && dto == DT_BF16) return launch_conv_halo_f32_bf16(taps, bm, ks, sn, nw, a, s);
+  if (dti == DT_F16 && dto == DT_F32) return launch_conv_halo_f16_f32(taps, bm, ks, sn, nw, a, s);
+  if (dti == DT_F16 && dto == DT_F16) return launch_conv_halo_f16_f16(taps, bm, ks, sn, nw, a, s);
+  if (dti == DT_F16 && dto == DT_BF16) return launch_conv_halo_f16_bf16(taps, bm, ks, sn, nw, a, s);
+  if (dti == DT_BF16 && dto == DT_F32) return launch_conv_halo_bf16_f32(taps, bm, ks, sn, nw, a, s);
+  if (dti == DT_BF16 && dto == DT_F16) return launch_conv_halo_bf16_f16(taps, bm, ks, sn, nw, a, s);
+  if (dti == DT_BF16 && dto == DT_BF16) return launch_conv_halo_bf16_bf16(taps, bm, ks, sn, nw, a, s);
   return -1;
 }
 

@@ -342,10 +342,17 @@ inline int launch_conv_tile(int tile, const ConvArgs& a, hipStream_t s) {
 }
 
 template <int DTI, int DTO, int T, int BM>
-inline int launch_conv_halo_ks(int ks, int sn, const HaloArgs& a, hipStream_t s) {
+inline int launch_conv_halo_ks(int ks, int sn, int nw, const HaloArgs& a, hipStream_t s) {
   // a wave keeps KS * BM / 64 weight-fragment sets of a chunk in registers (at
   // most 4); the one-tile-per-wave variants exist only where two workgroups
-  // share a CU
+  // share a CU, or as the eight-wave 64-channel variant (two fragment sets)
+  if (nw == 8) {
+    if constexpr (BM == 64) {
+      if (ks == 2 && sn == 1) { launch_conv_halo_t<DTI, DTO, T, BM, 2, 1, 8>(a, s); return 0; }
+    }
+    return -1;
+  }
+  if (nw != 4) return -1;
   if (sn == 2) {
     switch (ks) {
       case 1: launch_conv_halo_t<DTI, DTO, T, BM, 1, 2>(a, s); return 0;
@@ -370,19 +377,20 @@ inline int launch_conv_halo_ks(int ks, int sn, const HaloArgs& a, hipStream_t s)
 }
 
 template <int DTI, int DTO>
-inline int launch_conv_halo_tile(int taps, int bm, int ks, int sn, const HaloArgs& a, hipStream_t s) {
+inline int launch_conv_halo_tile(int taps, int bm, int ks, int sn, int nw, const HaloArgs& a, hipStream_t s) {
   if constexpr (DTI == DT_F32) {
     (void)taps;
     (void)ks;
     (void)sn;
+    (void)nw;
     if (bm == 64) { launch_conv32_halo_t<DTO, 64>(a, s); return 0; }
     if (bm == 128) { launch_conv32_halo_t<DTO, 128>(a, s); return 0; }
     return -1;
   } else {
-    if (taps == 9 && bm == 64) return launch_conv_halo_ks<DTI, DTO, 9, 64>(ks, sn, a, s);
-    if (taps == 9 && bm == 128) return launch_conv_halo_ks<DTI, DTO, 9, 128>(ks, sn, a, s);
-    if (taps == 1 && bm == 64) return launch_conv_halo_ks<DTI, DTO, 1, 64>(ks, sn, a, s);
-    if (taps == 1 && bm == 128) return launch_conv_halo_ks<DTI, DTO, 1, 128>(ks, sn, a, s);
+    if (taps == 9 && bm == 64) return launch_conv_halo_ks<DTI, DTO, 9, 64>(ks, sn, nw, a, s);
+    if (taps == 9 && bm == 128) return launch_conv_halo_ks<DTI, DTO, 9, 128>(ks, sn, nw, a, s);
+    if (taps == 1 && bm == 64) return launch_conv_halo_ks<DTI, DTO, 1, 64>(ks, sn, nw, a, s);
+    if (taps == 1 && bm == 128) return launch_conv_halo_ks<DTI, DTO, 1, 128>(ks, sn, nw, a, s);
     return -1;
   }
 }

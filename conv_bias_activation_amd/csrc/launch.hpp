@@ -62,7 +62,7 @@ int launch_gemm_i8(int dto, int tile, const GemmArgs& a, hipStream_t s);
 int launch_conv_f32(int dto, int tile, const ConvArgs& a, hipStream_t s);
 int launch_conv_f16(int dto, int tile, const ConvArgs& a, hipStream_t s);
 int launch_conv_bf16(int dto, int tile, const ConvArgs& a, hipStream_t s);
-int launch_conv_halo(int dti, int dto, int taps, int bm, int ks, int sn, const HaloArgs& a, hipStream_t s);
+int launch_conv_halo(int dti, int dto, int taps, int bm, int ks, int sn, int nw, const HaloArgs& a, hipStream_t s);
 int launch_act_cast(int dto, const float* ws, void* out, uint32_t n, int act, float alpha,
                     const void* res, hipStream_t s);
 

@@ -107,6 +107,7 @@ bool plan_halo32(ConvPlan* p, const void* x, const void* w) {
   p->h_bm = bm;
   p->h_ks = 0;
   p->h_sn = 2;
+  p->h_nw = 4;
   p->h_PH = PH;
   p->h_PW = PW;
   p->h_HR = (uint32_t)HR;
@@ -155,15 +156,18 @@ bool plan_halo(ConvPlan* p, const void* x, const void* w) {
   // 16 (zero-filled past C), with at most four (k-step, 32-row) weight-fragment
   // sets per wave held in registers -- two where two workgroups share a CU.
   struct Cfg {
-    uint32_t bm, sn, ks, PH, PW, HR, HC, bkc, co_blocks, w_blocks, h_blocks;
+    uint32_t bm, sn, nw, ks, PH, PW, HR, HC, bkc, co_blocks, w_blocks, h_blocks;
     uint64_t blocks;
     bool ok;
   };
-  auto make = [&](uint32_t bm, uint32_t sn, bool shared) {
+  // shared: two four-wave workgroups per CU; nw = 8: one eight-wave workgroup
+  // per CU (two waves per SIMD, at most 256 registers per lane each)
+  auto make = [&](uint32_t bm, uint32_t sn, bool shared, uint32_t nw = 4) {
     Cfg c{};
     c.bm = bm;
     c.sn = sn;
-    const uint32_t bn = 64 * sn;
+    c.nw = nw;
+    const uint32_t bn = 32 * sn * (nw / 2);
     c.PW = p->Wo < bn ? p->Wo : bn;
     c.PH = bn / c.PW < p->Ho ? bn / c.PW : p->Ho;            // rows of one image only
     c.HR = (c.PH - 1) * p->sh + (p->kh - 1) * p->dh + 1;
@@ -177,14 +181,14 @@ bool plan_halo(ConvPlan* p, const void* x, const void* w) {
     // the kernel's occupancy rule: two workgroups per CU (80 KB of LDS each)
     // when a wave holds at most two fragment sets and two accumulator tiles
     auto limit = [&](uint64_t b) {
-      const bool two = (b / 16) * (bm / 64) <= 2 && sn * (bm / 64) <= 2;
+      const bool two = nw == 4 && (b / 16) * (bm / 64) <= 2 && sn * (bm / 64) <= 2;
       return (uint64_t)(two ? 80 : 144) * 1024;
     };
     auto lds_bytes = [&](uint64_t b) {
       const uint64_t raw = ((uint64_t)bm * (b * T / 8 + 1) + 63) / 64 * 1024;
       return (uint64_t)c.HR * c.HC * b * 2 + raw;
     };
-    const uint32_t max_sets = shared ? 2 : 4;                  // k-steps x 32-row tiles per wave
+    const uint32_t max_sets = shared || nw == 8 ? 2 : 4;       // k-steps x 32-row tiles per wave
     uint32_t bkc = 16 * (max_sets / (bm / 64));
     if (bkc > 64) bkc = 64;
     while (bkc > 16 && bkc / 2 >= p->C) bkc /= 2;            // no wider than the channel count needs
@@ -199,18 +203,24 @@ bool plan_halo(ConvPlan* p, const void* x, const void* w) {
     c.ok = c.ok && c.blocks < (1u << 31);
     return c;
   };
-  // A workgroup per CU with the widest tile, unless that leaves fewer than two
-  // workgroups per CU: then tiles half as wide in channels (or positions) that
-  // two workgroups can share a CU with, when they give 1.5x the workgroups.
+  // Up to 64 output channels: the eight-wave variant (one workgroup of 64
+  // channels x 128 positions per CU, two waves per SIMD, two fragment sets per
+  // wave), when its chunks are two k-steps wide.  Otherwise a workgroup per CU
+  // with the widest tile, unless that leaves fewer than two workgroups per CU:
+  // then tiles half as wide in channels (or positions) that two workgroups can
+  // share a CU with, when they give 1.5x the workgroups.
   Cfg c = make(p->Co <= 64 ? 64 : 128, 2, false);
-  const Cfg alt[2] = {make(64, 2, true), make(64, 1, true)};
+  const Cfg alt[3] = {make(64, 2, true), make(64, 1, true), make(64, 1, false, 8)};
+  auto eight_ok = [&]() { return alt[2].ok && alt[2].ks == 2; };
   const int forced = forced_halo_variant();
-  if (forced == 1 || forced == 2) {
-    if (alt[forced - 1].ok) c = alt[forced - 1];
+  if (forced >= 1 && forced <= 3) {
+    if (alt[forced - 1].ok && (forced != 3 || eight_ok())) c = alt[forced - 1];
+  } else if (forced < 0 && p->Co <= 64 && eight_ok()) {
+    c = alt[2];
   } else if (forced < 0 && c.ok && c.blocks < 512) {
-    for (const Cfg& a2 : alt)
-      if (a2.ok && a2.blocks * 2 >= c.blocks * 3) {
-        c = a2;
+    for (int i = 0; i < 2; ++i)
+      if (alt[i].ok && alt[i].blocks * 2 >= c.blocks * 3) {
+        c = alt[i];
         break;
       }
   }
@@ -218,6 +228,7 @@ bool plan_halo(ConvPlan* p, const void* x, const void* w) {
   p->h_bm = c.bm;
   p->h_ks = c.ks;                                              // k-steps of 16 channels per tap
   p->h_sn = c.sn;
+  p->h_nw = c.nw;
   p->h_PH = c.PH;
   p->h_PW = c.PW;
   p->h_HR = c.HR;

@@ -46,7 +46,7 @@ struct ConvPlan {
   int tile;
   uint32_t tiles_m, tiles_n;
   // halo kernel (tile 7) parameters
-  uint32_t h_bm, h_ks, h_sn, h_PH, h_PW, h_HR, h_HC, h_bkc, h_co_blocks, h_w_blocks, h_h_blocks, h_blocks;
+  uint32_t h_bm, h_ks, h_sn, h_nw, h_PH, h_PW, h_HR, h_HC, h_bkc, h_co_blocks, h_w_blocks, h_h_blocks, h_blocks;
   uint32_t h_hrcp, h_kpad, h_kstr;   // fp32 halo kernel (see plan_halo32)
   uint32_t h_groups;                 // fp32 halo kernel: resident-filter workgroups, or 0
 };

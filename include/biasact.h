@@ -291,11 +291,13 @@ int biasact_conv_tile_config(int64_t N, int64_t Co, int64_t Ho, int64_t Wo, int6
  * threads.  Returns BA_ERR_INVALID for an unknown id. */
 int biasact_force_tile_config(int id);
 /* Process-wide override of the fp16/bf16 conv-halo variant, for tests and
- * tuning: -1 automatic; 0 the widest tile, one workgroup per CU; 1 64 output
- * channels x 128 positions and 2 64 output channels x 64 positions, both
- * small enough for two workgroups per CU.  A variant that does not apply to a
- * problem falls back to the widest tile.  Not synchronised, like the tile
- * override.  Returns BA_ERR_INVALID outside -1..2. */
+ * tuning: -1 automatic; 0 the widest tile, one four-wave workgroup per CU;
+ * 1 64 output channels x 128 positions and 2 64 output channels x 64
+ * positions, both small enough for two four-wave workgroups per CU; 3 64
+ * output channels x 128 positions in one eight-wave workgroup per CU (chunks
+ * of 32 channels only).  A variant that does not apply to a problem falls
+ * back to the widest tile.  Not synchronised, like the tile override.
+ * Returns BA_ERR_INVALID outside -1..3. */
 int biasact_force_halo_variant(int v);
 
 #ifdef __cplusplus
