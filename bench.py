@@ -121,7 +121,7 @@ def _parse():
     ap.add_argument("--workload", default="gemm_relu_4096_bf16")
     ap.add_argument("--no-others", action="store_true", help="skip the other workloads")
     ap.add_argument("--halo-variant", type=int, default=-1,
-                    help="force the fp16/bf16 conv-halo variant (0 widest, 1 and 2 two per CU, 3 eight waves; -1 auto)")
+                    help="force the fp16/bf16 conv-halo variant (0 widest, 1 and 2 two per CU, 3 and 4 eight waves; -1 auto)")
     ap.add_argument("--path", choices=("fused", "2k"), default="fused",
                     help="time the fused kernel (default) or the two-kernel ablation for --workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")

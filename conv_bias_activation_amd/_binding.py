@@ -484,5 +484,5 @@ def last_tile_config() -> str:
 
 
 def force_halo_variant(v: int):
-    """-1 automatic; 0 widest conv-halo tile; 1, 2 the two-per-CU variants; 3 eight waves."""
+    """-1 automatic; 0 widest conv-halo tile; 1, 2 the two-per-CU variants; 3, 4 eight waves."""
     _check(lib.biasact_force_halo_variant(int(v)), "force_halo_variant")

@@ -629,7 +629,7 @@ int biasact_force_tile_config(int id) {
 }
 
 int biasact_force_halo_variant(int v) {
-  if (v < -1 || v > 3) return kErrInvalid;
+  if (v < -1 || v > 4) return kErrInvalid;
   set_forced_halo_variant(v);
   return kOk;
 }

@@ -345,10 +345,11 @@ template <int DTI, int DTO, int T, int BM>
 inline int launch_conv_halo_ks(int ks, int sn, int nw, const HaloArgs& a, hipStream_t s) {
   // a wave keeps KS * BM / 64 weight-fragment sets of a chunk in registers (at
   // most 4); the one-tile-per-wave variants exist only where two workgroups
-  // share a CU, or as the eight-wave 64-channel variant (two fragment sets)
+  // share a CU, or in the eight-wave 64-channel variants (two fragment sets)
   if (nw == 8) {
     if constexpr (BM == 64) {
       if (ks == 2 && sn == 1) { launch_conv_halo_t<DTI, DTO, T, BM, 2, 1, 8>(a, s); return 0; }
+      if (ks == 2 && sn == 2) { launch_conv_halo_t<DTI, DTO, T, BM, 2, 2, 8>(a, s); return 0; }
     }
     return -1;
   }

@@ -170,6 +170,7 @@ bool plan_halo(ConvPlan* p, const void* x, const void* w) {
     const uint32_t bn = 32 * sn * (nw / 2);
     c.PW = p->Wo < bn ? p->Wo : bn;
     c.PH = bn / c.PW < p->Ho ? bn / c.PW : p->Ho;            // rows of one image only
+    c.PH = (p->Ho + (p->Ho + c.PH - 1) / c.PH - 1) / ((p->Ho + c.PH - 1) / c.PH);   // as even as the block count allows
     c.HR = (c.PH - 1) * p->sh + (p->kh - 1) * p->dh + 1;
     // a patch whose first input column ow0*sw - pl is odd starts one column
     // into its (even-aligned) halo: one more column; when every patch starts
@@ -203,20 +204,24 @@ bool plan_halo(ConvPlan* p, const void* x, const void* w) {
     c.ok = c.ok && c.blocks < (1u << 31);
     return c;
   };
-  // Up to 64 output channels: the eight-wave variant (one workgroup of 64
-  // channels x 128 positions per CU, two waves per SIMD, two fragment sets per
-  // wave), when its chunks are two k-steps wide.  Otherwise a workgroup per CU
-  // with the widest tile, unless that leaves fewer than two workgroups per CU:
-  // then tiles half as wide in channels (or positions) that two workgroups can
-  // share a CU with, when they give 1.5x the workgroups.
+  // Eight-wave variants (one workgroup of 64 channels per CU, two waves per
+  // SIMD, chunks of 32 channels): 64 channels x 128 positions up to 64 output
+  // channels; 64 x 256 positions beyond, when that still gives 200 or more
+  // workgroups.  Otherwise a four-wave workgroup per CU with the widest tile,
+  // unless that leaves fewer than two workgroups per CU: then tiles half as
+  // wide in channels (or positions) that two workgroups can share a CU with,
+  // when they give 1.5x the workgroups.
   Cfg c = make(p->Co <= 64 ? 64 : 128, 2, false);
-  const Cfg alt[3] = {make(64, 2, true), make(64, 1, true), make(64, 1, false, 8)};
-  auto eight_ok = [&]() { return alt[2].ok && alt[2].ks == 2; };
+  const Cfg alt[4] = {make(64, 2, true), make(64, 1, true), make(64, 1, false, 8), make(64, 2, false, 8)};
+  auto eight_ok = [&](const Cfg& e) { return e.ok && e.ks == 2; };
   const int forced = forced_halo_variant();
-  if (forced >= 1 && forced <= 3) {
-    if (alt[forced - 1].ok && (forced != 3 || eight_ok())) c = alt[forced - 1];
-  } else if (forced < 0 && p->Co <= 64 && eight_ok()) {
+  if (forced >= 1 && forced <= 4) {
+    const Cfg& f = alt[forced - 1];
+    if (forced <= 2 ? f.ok : eight_ok(f)) c = f;
+  } else if (forced < 0 && p->Co <= 64 && eight_ok(alt[2])) {
     c = alt[2];
+  } else if (forced < 0 && p->Co > 64 && eight_ok(alt[3]) && alt[3].blocks >= 200) {
+    c = alt[3];
   } else if (forced < 0 && c.ok && c.blocks < 512) {
     for (int i = 0; i < 2; ++i)
       if (alt[i].ok && alt[i].blocks * 2 >= c.blocks * 3) {

@@ -293,11 +293,11 @@ int biasact_force_tile_config(int id);
 /* Process-wide override of the fp16/bf16 conv-halo variant, for tests and
  * tuning: -1 automatic; 0 the widest tile, one four-wave workgroup per CU;
  * 1 64 output channels x 128 positions and 2 64 output channels x 64
- * positions, both small enough for two four-wave workgroups per CU; 3 64
- * output channels x 128 positions in one eight-wave workgroup per CU (chunks
- * of 32 channels only).  A variant that does not apply to a problem falls
- * back to the widest tile.  Not synchronised, like the tile override.
- * Returns BA_ERR_INVALID outside -1..3. */
+ * positions, both small enough for two four-wave workgroups per CU; 3 and 4
+ * 64 output channels x 128 and x 256 positions in one eight-wave workgroup
+ * per CU (chunks of 32 channels only).  A variant that does not apply to a
+ * problem falls back to the widest tile.  Not synchronised, like the tile
+ * override.  Returns BA_ERR_INVALID outside -1..4. */
 int biasact_force_halo_variant(int v);
 
 #ifdef __cplusplus

@@ -98,10 +98,10 @@ def test_tile_table_introspection():
 
 
 def test_halo_variant_override_range():
-    for v in (-1, 0, 1, 2, 3):
+    for v in (-1, 0, 1, 2, 3, 4):
         ba.force_halo_variant(v)
     ba.force_halo_variant(-1)
-    for v in (-2, 4):
+    for v in (-2, 5):
         with pytest.raises(ValueError):
             ba.force_halo_variant(v)
 

@@ -388,7 +388,7 @@ def test_conv_halo_path_vs_oracle(ba, shape, types):
     N, C, H, W, Co, kh, kw, st, pd, dl = shape
     ti, to, tb = types
     # automatic choice, then every conv-halo variant forced
-    for tile, variant in ((-1, -1), (7, 0), (7, 1), (7, 2), (7, 3)):
+    for tile, variant in ((-1, -1), (7, 0), (7, 1), (7, 2), (7, 3), (7, 4)):
         ba.force_tile_config(tile)
         ba.force_halo_variant(variant)
         try:
