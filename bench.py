@@ -45,15 +45,17 @@ PEAK_HBM_GBS = 8000.0
 
 # Sources that define each kernel; a committed HBM-traffic record carries
 # their hash and is reported only while they are unchanged.
-KERNEL_SOURCES = {
+KERNEL_SOURCES = {   # each kernel's source and every header it includes
     "gemm16_pp_kernel": ["gemm_pp.hpp", "epilogue.hpp", "device_common.hpp", "gemm_args.hpp",
-                         "tile_map.hpp"],
-    "conv16_halo_kernel": ["conv_halo.hpp", "device_common.hpp", "mfma_core.hpp"],
-    "conv32_halo_kernel": ["conv_halo32.hpp", "device_common.hpp", "mfma_core.hpp"],
-    "gemm_bias_act_kernel": ["kernels_impl.hpp", "mfma_core.hpp", "epilogue.hpp",
-                             "device_common.hpp", "tile_map.hpp"],
-    "conv_bias_act_kernel": ["kernels_impl.hpp", "mfma_core.hpp", "epilogue.hpp",
-                             "device_common.hpp", "tile_map.hpp"],
+                         "tile_map.hpp", "launch_kernel.hpp"],
+    "conv16_halo_kernel": ["conv_halo.hpp", "epilogue.hpp", "launch.hpp", "launch_kernel.hpp",
+                           "mfma_core.hpp", "device_common.hpp", "gemm_args.hpp", "tile_map.hpp"],
+    "conv32_halo_kernel": ["conv_halo32.hpp", "epilogue.hpp", "launch.hpp", "launch_kernel.hpp",
+                           "mfma_core.hpp", "device_common.hpp", "gemm_args.hpp", "tile_map.hpp"],
+    "gemm_bias_act_kernel": ["kernels_impl.hpp", "mfma_core.hpp", "epilogue.hpp", "launch.hpp",
+                             "launch_kernel.hpp", "device_common.hpp", "gemm_args.hpp", "tile_map.hpp"],
+    "conv_bias_act_kernel": ["kernels_impl.hpp", "mfma_core.hpp", "epilogue.hpp", "launch.hpp",
+                             "launch_kernel.hpp", "device_common.hpp", "gemm_args.hpp", "tile_map.hpp"],
 }
 TRAFFIC_RECORDS = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 TWO_KERNEL = "two-kernel: "

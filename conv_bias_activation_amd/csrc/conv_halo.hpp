@@ -46,6 +46,7 @@
 #include "launch.hpp"
 #include "launch_kernel.hpp"
 #include "mfma_core.hpp"
+#include "tile_map.hpp"
 
 namespace biasact {
 
@@ -124,8 +125,10 @@ __global__ __launch_bounds__(NW * 64, (occupancy<BM, KS, SN, NW>())) void conv16
   __shared__ __attribute__((aligned(16))) uint8_t s_halo[LDS - NDMA * 1024];
   const ConvGeom& G = a.geom;
 
-  // workgroup -> (co block, output-column block, output-row block, image)
-  uint32_t bid = blockIdx.x;
+  // workgroup -> (co block, output-column block, output-row block, image),
+  // numbered so that each XCD takes a contiguous range: neighbouring row
+  // blocks, whose halos share input rows, then share an L2
+  uint32_t bid = xcd_contiguous(blockIdx.x, gridDim.x);
   // (divisions by the grid's invariant block counts through FastDiv: a
   // runtime integer division costs tens of VALU instructions)
   uint32_t qd = fdiv(bid, a.div_cob);

@@ -39,6 +39,7 @@
 #include "launch.hpp"
 #include "launch_kernel.hpp"
 #include "mfma_core.hpp"
+#include "tile_map.hpp"
 
 namespace biasact {
 
@@ -71,14 +72,17 @@ __global__ __launch_bounds__(256, 2) void conv32_halo_kernel(HaloArgs a) {
   // column block fastest.  Workgroup -> (co block, one patch); with a resident
   // filter (a.groups > 0, one co block, one chunk) workgroup b takes patches
   // [b P / groups, (b + 1) P / groups) of the P = N * h_blocks * w_blocks.
+  // Workgroups are renumbered so that each XCD takes a contiguous range of
+  // patches: neighbouring patches, whose halos share input rows, share an L2.
+  const uint32_t wg = xcd_contiguous(blockIdx.x, gridDim.x);
   uint32_t cb = 0, p_first, p_end;
   if (a.groups) {
     const uint32_t P = G.N * a.h_blocks * a.w_blocks;
-    p_first = (uint32_t)((uint64_t)blockIdx.x * P / a.groups);
-    p_end = (uint32_t)((uint64_t)(blockIdx.x + 1) * P / a.groups);
+    p_first = (uint32_t)((uint64_t)wg * P / a.groups);
+    p_end = (uint32_t)((uint64_t)(wg + 1) * P / a.groups);
   } else {
-    cb = blockIdx.x % a.co_blocks;
-    p_first = blockIdx.x / a.co_blocks;
+    cb = wg % a.co_blocks;
+    p_first = wg / a.co_blocks;
     p_end = p_first + 1;
   }
   const uint32_t co0 = cb * BM;
