@@ -503,7 +503,7 @@ def main():
     import conv_bias_activation_amd as ba
     import workloads as wl
 
-    case = wl.CASES[args.workload]
+    case = wl.CASES[args.workload] if args.workload in wl.CASES else wl.FILTER_CASES[args.workload]
     if args.tile >= 0:
         ba.force_tile_config(args.tile)
     if args.halo_variant >= 0:
@@ -571,6 +571,14 @@ def main():
             others[name] = entry
             torch.cuda.empty_cache()
         line["others"] = others
+        # 16-bit convs with 5x5 and 7x7 filters (not named workloads)
+        larger = {}
+        for name, c in wl.FILTER_CASES.items():
+            try:
+                larger[name] = measure_case(c, "fused")
+            except Exception as e:  # report, never hide
+                larger[name] = {"error": repr(e)}
+        line["larger_filters"] = larger
         try:
             line["launch_floor"] = launch_floor()
         except Exception as e:  # report, never hide

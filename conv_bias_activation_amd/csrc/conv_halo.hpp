@@ -20,18 +20,22 @@
 // output columns (positions q = row * PW + col, at most 32 * SN * NW / 2).
 // Four-wave variants small enough for two workgroups per CU (80 KB of LDS,
 // two fragment sets per wave) let one workgroup's staging and epilogue
-// overlap another's MFMAs; the eight-wave variant has its CU alone with two
-// waves per SIMD, which fetches each weight chunk once per CU.
+// overlap another's MFMAs; the eight-wave variants have their CU alone with
+// two waves per SIMD, which fetches each weight chunk once per CU.  Square
+// filters up to 7x7: beyond 3x3 (T = 25, 49 taps) one four-wave configuration
+// (64 channels, one 16-channel k-step per chunk) whose wave holds the 4 T
+// fragment registers of a chunk in the accumulation registers.
 // Staging items: input (halo row, column pair, 8 channels) — eight 4-byte
-// loads transposed in registers into two 16-byte LDS writes; weights (output
-// channel, 8 channels) — T 16-byte loads (8 channels x T taps are contiguous
-// in OIHW) regrouped into T 16-byte LDS writes.  The first HB input items
-// and WB weight items of each thread form a batch whose offsets are computed
-// once; the batch of chunk 0 is issued before anything waits, and the batch of
-// chunk ck + 1 is spread over the MFMA steps of chunk ck.  Items beyond the
-// batch (large halos) are staged with their own loads before the multiply.
-// The multiply is unrolled over its T * KS (tap, k-step) steps; the fragments
-// of step s + 1 are read while the MFMAs of step s run.
+// loads transposed in registers into two 16-byte LDS writes; weights — the
+// chunk's raw OIHW rows (8 channels x T taps are contiguous) copied into LDS
+// by 16-byte direct loads, then regrouped in each wave's registers into MFMA
+// fragments.  The first HB input items of each thread form a batch whose
+// offsets are computed once; the batch and weights of chunk 0 are issued
+// before anything waits, and those of chunk ck + 1 are spread over the MFMA
+// steps of chunk ck.  Items beyond the batch (large halos) are staged with
+// their own loads before the multiply.  The multiply is unrolled over its
+// T * KS (tap, k-step) steps; a step's input fragments are read two steps
+// ahead.
 //
 // LDS rows (one halo position, or one (tap, co) weight row) hold NCH = 2 * KS
 // chunks of 16 bytes; chunk c of row p sits at slot c ^ ((p >> S) % NCH) with
@@ -93,28 +97,36 @@ __device__ __forceinline__ void interleave() {
 }  // namespace halo
 
 // Two four-wave workgroups share a CU when a wave holds at most two
-// weight-fragment sets and two accumulator tiles (then 256 registers per lane
-// suffice); an eight-wave workgroup has its CU alone (two waves per SIMD).
-template <int BM, int KS, int SN, int NW = 4>
-constexpr int occupancy() { return NW == 4 && KS * (BM / 64) <= 2 && SN * (BM / 64) <= 2 ? 2 : 1; }
+// weight-fragment sets of at most 9 taps and two accumulator tiles (then 256
+// registers per lane suffice); an eight-wave workgroup has its CU alone (two
+// waves per SIMD), and so has a four-wave one with a larger filter (its wave
+// holds 4 T fragment registers: up to 512 registers per lane with the
+// accumulation registers).
+template <int BM, int KS, int SN, int NW = 4, int T = 9>
+constexpr int occupancy() {
+  return NW == 4 && T <= 9 && KS * (BM / 64) <= 2 && SN * (BM / 64) <= 2 ? 2 : 1;
+}
 
-// T = taps (kh*kw: 1 or 9), BM = output channels per workgroup (64 or 128),
+// T = taps (kh*kw: a square 1x1, 3x3, 5x5 or 7x7 filter), BM = output
+// channels per workgroup (64 or 128),
 // KS = 16-channel k-steps per tap and chunk (1, 2 or 4; KS * BM / 64 <= 4),
 // SN = 32-position MFMA tiles per wave, NW = waves (4 or 8) as a grid of 2
 // (output-channel halves) x NW / 2 (position groups): NW / 2 x SN x 32
 // positions per workgroup.
 template <int DTI, int DTO, int T, int BM, int KS, int SN, int NW>
-__global__ __launch_bounds__(NW * 64, (occupancy<BM, KS, SN, NW>())) void conv16_halo_kernel(HaloArgs a) {
+__global__ __launch_bounds__(NW * 64, (occupancy<BM, KS, SN, NW, T>())) void conv16_halo_kernel(HaloArgs a) {
   static_assert(DTI == DT_F16 || DTI == DT_BF16, "16-bit operands only");
-  static_assert(T == 1 || T == 9, "1x1 or 3x3 filters (the planner admits no other shape)");
+  static_assert(T == 1 || T == 9 || T == 25 || T == 49, "square 1x1, 3x3, 5x5 or 7x7 filters");
+  static_assert(T <= 9 || (KS == 1 && BM == 64 && NW == 4), "larger filters: one k-step, 64 channels, four waves");
+  constexpr uint32_t KW = T == 49 ? 7 : T == 25 ? 5 : T == 9 ? 3 : 1;   // filter width
   constexpr int WTM = BM / 2, SM = WTM / 32, WTN = 32 * SN;
   static_assert(NW == 4 || NW == 8, "four or eight waves");
-  constexpr int LDS = occupancy<BM, KS, SN, NW>() == 2 ? halo::LDS_TWO : halo::LDS_ONE;
+  constexpr int LDS = occupancy<BM, KS, SN, NW, T>() == 2 ? halo::LDS_TWO : halo::LDS_ONE;
   constexpr int WGN = NW / 2;                           // position groups
   static_assert(KS * SM <= 4, "weight fragments of a chunk must fit in registers");
   constexpr int BKC = 16 * KS, NCH = 2 * KS, ROWB = NCH * 16;
   constexpr int NSTEP = T * KS;
-  constexpr int HB = occupancy<BM, KS, SN, NW>() == 2 || NW == 8 ? 2 : halo::HB, NTH = NW * 64;
+  constexpr int HB = occupancy<BM, KS, SN, NW, T>() == 2 || NW == 8 || T > 9 ? 2 : halo::HB, NTH = NW * 64;
   constexpr int RP = BKC * T / 8;                       // 16-byte pieces of one weight row
   constexpr int RSTR = (RP + 1) * 16;                   // row stride: the pieces and a pad
   constexpr int NPIECE = BM * (RP + 1);
@@ -167,27 +179,28 @@ __global__ __launch_bounds__(NW * 64, (occupancy<BM, KS, SN, NW>())) void conv16
   constexpr int KWL = (NDMA + NW - 1) / NW;             // direct weight loads per wave
   // Direct load k of this wave (load i = wave + NW k covers pieces 64i .. 64i+63).
   // Each lane's offset within the chunk is computed once (kOOB for pad
-  // pieces and rows past Co) with the first channel of its piece; a chunk at
-  // channel c0 then passes c0 * T * 2 as the scalar offset of the load, and a
-  // lane whose channels lie past C (a partial last chunk) passes kOOB.  The
+  // pieces and rows past Co), its low bits (zero in a 16-byte offset) holding
+  // the piece's 8-channel group; a chunk at channel c0 then passes c0 * T * 2
+  // as the scalar offset of the load, and a lane whose channels lie past C (a
+  // partial last chunk) passes kOOB.  The
   // issue of these loads is bound by the vector instructions of their
   // addresses (a probe of this copy moved 20 B/clk per CU with the addresses
   // computed per load and 52 B/clk with them computed beforehand).
-  uint32_t wofs[KWL], wch[KWL];
+  static_assert(BKC / 8 <= 8, "the channel group must fit the offset's low bits");
+  uint32_t wofs[KWL];
 #pragma unroll
   for (int k = 0; k < KWL; ++k) {
     const uint32_t P = (uint32_t)(wave + NW * k) * 64 + lane;
     const uint32_t row = P / (RP + 1), pc = P - row * (RP + 1);
     const bool ok = pc < RP && row < BM && co0 + row < G.Co;
-    wofs[k] = ok ? (co0 + row) * G.C * T * 2u + pc * 16u : kOOB;
-    wch[k] = ok ? 8 * (pc / T) : halo::kFar;
+    wofs[k] = ok ? ((co0 + row) * G.C * T * 2u + pc * 16u) | (pc / T) : kOOB;
   }
   // lim = channels left from c0 (0: issue the loads but fetch nothing)
   auto weight_load = [&](auto k_c, uint32_t c0, uint32_t lim) {
     constexpr int k = decltype(k_c)::value;
     const int li = wave + NW * k;
     if (k + 1 < KWL || li < NDMA) {                    // only the last load can be past the chunk
-      const uint32_t src = wch[k] < lim ? wofs[k] : kOOB;
+      const uint32_t src = 8u * (wofs[k] & 7u) < lim ? wofs[k] & ~15u : kOOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(s_raw + li * 1024), 16, src, c0 * T * 2u, 0, 0);
     }
   };
@@ -257,28 +270,35 @@ __global__ __launch_bounds__(NW * 64, (occupancy<BM, KS, SN, NW>())) void conv16
   };
 
   // ---- fragment addresses --------------------------------------------------
-  // input (k-step 0; k-step ks flips slot bits by 2*ks): tap t, MFMA tile si
-  uint32_t h_addr[T][SN];
-  {
-    uint32_t pos[SN];
+  // input (k-step 0; k-step ks flips slot bits by 2*ks): tap t, MFMA tile si.
+  // Up to 9 taps the addresses are kept (T * SN registers); larger filters
+  // form them per step from the tap's offset, a scalar.
+  constexpr bool KEEP = T <= 9;
+  uint32_t pos[SN];
 #pragma unroll
-    for (int si = 0; si < SN; ++si) {
-      const uint32_t q = wave_n * WTN + si * 32 + lrow;
-      const uint32_t qh = fdiv(q, a.div_pw), qw = q - qh * a.PW;
-      // lanes past the patch read halo position 0 (in range); their results are never stored
-      pos[si] = q < a.PH * a.PW ? (qh * G.sh) * HC + qw * G.sw + col_shift : 0u;
-    }
+  for (int si = 0; si < SN; ++si) {
+    const uint32_t q = wave_n * WTN + si * 32 + lrow;
+    const uint32_t qh = fdiv(q, a.div_pw), qw = q - qh * a.PW;
+    // lanes past the patch read halo position 0 (in range); their results are never stored
+    pos[si] = q < a.PH * a.PW ? (qh * G.sh) * HC + qw * G.sw + col_shift : 0u;
+  }
+  // halo position of tap (r, s) for tile si: prow[r][si] + s * dw
+  uint32_t prow[KW][SN];
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      constexpr uint32_t KW = T == 9 ? 3 : 1;             // 3x3 or 1x1 filters only
-      const uint32_t r = (uint32_t)t / KW, s = (uint32_t)t - r * KW;
-      const uint32_t tap = (r * G.dh) * HC + s * G.dw;
+  for (uint32_t r = 0; r < KW; ++r)
 #pragma unroll
-      for (int si = 0; si < SN; ++si) {
-        const uint32_t p = pos[si] + tap;
-        h_addr[t][si] = p * ROWB + halo::slot<NCH>(p, (uint32_t)half) * 16;
-      }
-    }
+    for (int si = 0; si < SN; ++si) prow[r][si] = pos[si] + r * G.dh * HC;
+  auto frag_addr = [&](uint32_t t, int si) {
+    const uint32_t r = t / KW, s = t - r * KW;
+    const uint32_t p = prow[r][si] + s * G.dw;
+    return p * ROWB + halo::slot<NCH>(p, (uint32_t)half) * 16;
+  };
+  uint32_t h_addr[KEEP ? T : 1][SN];
+  if constexpr (KEEP) {
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int si = 0; si < SN; ++si) h_addr[t][si] = frag_addr((uint32_t)t, si);
   }
   // weights: this lane's rows (output channels) in the raw chunk
   uint32_t w_row[SM];
@@ -288,8 +308,40 @@ __global__ __launch_bounds__(NW * 64, (occupancy<BM, KS, SN, NW>())) void conv16
   // Weight fragments of a chunk: for k-step ks and row tile sj, this lane's
   // 8 channels (8 * (2 ks + half) ...) of every tap, regrouped from the raw run
   // (channel e, tap t at element e * T + t); channels past C arrive as zeros.
+  // Up to 9 taps the whole run (T 16-byte reads) is read into registers at
+  // once; larger filters read the 8 words of each fragment one by one, so
+  // that only the fragments stay live.
+  auto sel_of = [](int p0, int p1) {
+    return (uint32_t)((p0 & 1) * 2) | ((uint32_t)((p0 & 1) * 2 + 1) << 8) |
+           ((uint32_t)(4 + (p1 & 1) * 2) << 16) | ((uint32_t)(5 + (p1 & 1) * 2) << 24);
+  };
   u32x4 afr[KS][T][SM];
   auto build_weights = [&]() {
+    if constexpr (!KEEP) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int sj = 0; sj < SM; ++sj) {
+          const uint32_t g = 2 * ks + half;
+          const uint8_t* base = s_raw + w_row[sj] + g * 16 * T;
+#pragma unroll
+          for (int t = 0; t < T; ++t) {
+            uint32_t o[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const int p0 = (2 * k) * T + t, p1 = (2 * k + 1) * T + t;
+              const uint32_t d0 = *reinterpret_cast<const uint32_t*>(base + (p0 >> 1) * 4);
+              const uint32_t d1 = *reinterpret_cast<const uint32_t*>(base + (p1 >> 1) * 4);
+              o[k] = __builtin_amdgcn_perm(d1, d0, sel_of(p0, p1));
+            }
+            afr[ks][t][sj] = u32x4{o[0], o[1], o[2], o[3]};
+            // a few fragments at a time: the scheduler would otherwise issue
+            // every read first and hold all their words in registers
+            if (t % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      return;
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -311,9 +363,7 @@ __global__ __launch_bounds__(NW * 64, (occupancy<BM, KS, SN, NW>())) void conv16
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
             const int p0 = (2 * k) * T + t, p1 = (2 * k + 1) * T + t;
-            const uint32_t sel = (uint32_t)((p0 & 1) * 2) | ((uint32_t)((p0 & 1) * 2 + 1) << 8) |
-                                 ((uint32_t)(4 + (p1 & 1) * 2) << 16) | ((uint32_t)(5 + (p1 & 1) * 2) << 24);
-            o[k] = __builtin_amdgcn_perm(v[p1 >> 1], v[p0 >> 1], sel);
+            o[k] = __builtin_amdgcn_perm(v[p1 >> 1], v[p0 >> 1], sel_of(p0, p1));
           }
           afr[ks][t][sj] = u32x4{o[0], o[1], o[2], o[3]};
         }
@@ -325,8 +375,12 @@ __global__ __launch_bounds__(NW * 64, (occupancy<BM, KS, SN, NW>())) void conv16
     constexpr int ks = st / T, t = st % T;
     constexpr uint32_t flip = (uint32_t)(2 * ks) << 4;
 #pragma unroll
-    for (int si = 0; si < SN; ++si)
-      fi[si] = *reinterpret_cast<const u32x4*>(s_halo + (h_addr[t][si] ^ flip));
+    for (int si = 0; si < SN; ++si) {
+      uint32_t ad;
+      if constexpr (KEEP) ad = h_addr[t][si];
+      else ad = frag_addr((uint32_t)t, si);
+      fi[si] = *reinterpret_cast<const u32x4*>(s_halo + (ad ^ flip));
+    }
   };
 
   // Accumulators.  A wave with a single 32x32 tile alternates two of them

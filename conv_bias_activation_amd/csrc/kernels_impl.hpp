@@ -342,7 +342,7 @@ inline int launch_conv_tile(int tile, const ConvArgs& a, hipStream_t s) {
 }
 
 template <int DTI, int DTO, int T, int BM>
-inline int launch_conv_halo_ks(int ks, int sn, int nw, const HaloArgs& a, hipStream_t s) {
+inline int launch_conv_halo_ks_small(int ks, int sn, int nw, const HaloArgs& a, hipStream_t s) {
   // a wave keeps KS * BM / 64 weight-fragment sets of a chunk in registers (at
   // most 4); the one-tile-per-wave variants exist only where two workgroups
   // share a CU, or in the eight-wave 64-channel variants (two fragment sets)
@@ -377,6 +377,20 @@ inline int launch_conv_halo_ks(int ks, int sn, int nw, const HaloArgs& a, hipStr
   return -1;
 }
 
+template <int DTI, int DTO, int T, int BM>
+inline int launch_conv_halo_ks(int ks, int sn, int nw, const HaloArgs& a, hipStream_t s) {
+  if constexpr (T > 9) {
+    // larger filters: one k-step per chunk, two position tiles per wave, four waves
+    if (BM == 64 && ks == 1 && sn == 2 && nw == 4) {
+      launch_conv_halo_t<DTI, DTO, T, 64, 1, 2, 4>(a, s);
+      return 0;
+    }
+    return -1;
+  } else {
+    return launch_conv_halo_ks_small<DTI, DTO, T, BM>(ks, sn, nw, a, s);
+  }
+}
+
 template <int DTI, int DTO>
 inline int launch_conv_halo_tile(int taps, int bm, int ks, int sn, int nw, const HaloArgs& a, hipStream_t s) {
   if constexpr (DTI == DT_F32) {
@@ -392,6 +406,8 @@ inline int launch_conv_halo_tile(int taps, int bm, int ks, int sn, int nw, const
     if (taps == 9 && bm == 128) return launch_conv_halo_ks<DTI, DTO, 9, 128>(ks, sn, nw, a, s);
     if (taps == 1 && bm == 64) return launch_conv_halo_ks<DTI, DTO, 1, 64>(ks, sn, nw, a, s);
     if (taps == 1 && bm == 128) return launch_conv_halo_ks<DTI, DTO, 1, 128>(ks, sn, nw, a, s);
+    if (taps == 25 && bm == 64) return launch_conv_halo_ks<DTI, DTO, 25, 64>(ks, sn, nw, a, s);
+    if (taps == 49 && bm == 64) return launch_conv_halo_ks<DTI, DTO, 49, 64>(ks, sn, nw, a, s);
     return -1;
   }
 }

@@ -137,7 +137,8 @@ bool plan_halo32(ConvPlan* p, const void* x, const void* w) {
 }
 
 // Halo-kernel parameters for a conv (16-bit operands, C % 8 == 0, even W,
-// 1x1 or 3x3 filters, aligned x / w; fp32 operands go to plan_halo32).
+// square 1x1, 3x3, 5x5 or 7x7 filters, aligned x / w; fp32 operands go to
+// plan_halo32).
 // Returns false when it does not apply.
 bool plan_halo(ConvPlan* p, const void* x, const void* w) {
   p->h_hrcp = 0;
@@ -147,7 +148,8 @@ bool plan_halo(ConvPlan* p, const void* x, const void* w) {
   if (p->dti == kF32) return plan_halo32(p, x, w);
   if (p->C % 8 != 0 || p->W % 2 != 0) return false;
   const uint32_t T = p->kh * p->kw;
-  if (!((p->kh == 1 && p->kw == 1) || (p->kh == 3 && p->kw == 3))) return false;   // 1x1 or 3x3
+  if (p->kh != p->kw || (p->kh != 1 && p->kh != 3 && p->kh != 5 && p->kh != 7)) return false;   // square 1, 3, 5, 7
+  const bool large = T > 9;         // 5x5, 7x7: one configuration (64 channels, 4 waves, chunks of 16)
   if (!aligned(x, 4) || !aligned(w, 16)) return false;
   // One configuration = (bm output channels, 2 x 32 sn positions, LDS budget).
   // LDS: the halo (HR x HC positions x bkc channels) and one raw weight chunk
@@ -182,14 +184,14 @@ bool plan_halo(ConvPlan* p, const void* x, const void* w) {
     // the kernel's occupancy rule: two workgroups per CU (80 KB of LDS each)
     // when a wave holds at most two fragment sets and two accumulator tiles
     auto limit = [&](uint64_t b) {
-      const bool two = nw == 4 && (b / 16) * (bm / 64) <= 2 && sn * (bm / 64) <= 2;
+      const bool two = nw == 4 && !large && (b / 16) * (bm / 64) <= 2 && sn * (bm / 64) <= 2;
       return (uint64_t)(two ? 80 : 144) * 1024;
     };
     auto lds_bytes = [&](uint64_t b) {
       const uint64_t raw = ((uint64_t)bm * (b * T / 8 + 1) + 63) / 64 * 1024;
       return (uint64_t)c.HR * c.HC * b * 2 + raw;
     };
-    const uint32_t max_sets = shared || nw == 8 ? 2 : 4;       // k-steps x 32-row tiles per wave
+    const uint32_t max_sets = large ? 1 : shared || nw == 8 ? 2 : 4;   // k-steps x 32-row tiles per wave
     uint32_t bkc = 16 * (max_sets / (bm / 64));
     if (bkc > 64) bkc = 64;
     while (bkc > 16 && bkc / 2 >= p->C) bkc /= 2;            // no wider than the channel count needs
@@ -211,11 +213,13 @@ bool plan_halo(ConvPlan* p, const void* x, const void* w) {
   // unless that leaves fewer than two workgroups per CU: then tiles half as
   // wide in channels (or positions) that two workgroups can share a CU with,
   // when they give 1.5x the workgroups.
-  Cfg c = make(p->Co <= 64 ? 64 : 128, 2, false);
+  Cfg c = make(p->Co <= 64 || large ? 64 : 128, 2, false);
   const Cfg alt[4] = {make(64, 2, true), make(64, 1, true), make(64, 1, false, 8), make(64, 2, false, 8)};
   auto eight_ok = [&](const Cfg& e) { return e.ok && e.ks == 2; };
   const int forced = forced_halo_variant();
-  if (forced >= 1 && forced <= 4) {
+  if (large) {
+    // larger filters have the one configuration
+  } else if (forced >= 1 && forced <= 4) {
     const Cfg& f = alt[forced - 1];
     if (forced <= 2 ? f.ok : eight_ok(f)) c = f;
   } else if (forced < 0 && p->Co <= 64 && eight_ok(alt[2])) {

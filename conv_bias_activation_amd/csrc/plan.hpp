@@ -21,7 +21,7 @@ constexpr TileShapeDesc kTiles[] = {
     {4, 64, 256, 1, 4},
     {5, 64, 64, 2, 2},
     {6, 256, 256, 2, 4},   // 8-wave ping-pong kernel: aligned 16-bit GEMMs only (else as 0)
-    {7, 128, 128, 2, 2},   // conv with a channel-last LDS halo: 16-bit, 1x1 or 3x3 (else as 3)
+    {7, 128, 128, 2, 2},   // conv with a channel-last LDS halo: 16-bit square 1x1 to 7x7, fp32 (else as 3)
 };
 constexpr int kNumTileConfigs = (int)(sizeof(kTiles) / sizeof(kTiles[0]));
 

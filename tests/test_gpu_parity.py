@@ -378,6 +378,10 @@ HALO_SHAPES = [
     (2, 16, 11, 14, 80, 3, 3, (2, 2), (1, 1, 1, 1), (1, 1)),      # 128-row blocks, one k-step
     (1, 72, 6, 16, 200, 1, 1, (1, 1), (0, 0, 0, 0), (1, 1)),      # three chunks, two co blocks
     (1, 64, 9, 130, 32, 3, 3, (2, 2), (1, 1, 1, 1), (1, 1)),      # halo past one load batch
+    (2, 16, 13, 18, 40, 5, 5, (1, 1), (2, 2, 2, 2), (1, 1)),      # 5x5: one 16-channel chunk
+    (1, 32, 9, 12, 64, 5, 5, (1, 1), (4, 4, 4, 4), (2, 2)),       # 5x5 dilated, two chunks
+    (1, 24, 11, 20, 72, 7, 7, (1, 1), (3, 3, 3, 3), (1, 1)),      # 7x7: partial second chunk, two co blocks
+    (1, 8, 17, 30, 33, 7, 7, (2, 2), (3, 2, 1, 3), (1, 1)),       # 7x7 stride 2, asymmetric pads, C = 8
 ]
 
 
@@ -577,9 +581,9 @@ def _log_report(name, seed, rep):
 
 
 @pytest.mark.parametrize("seed", (0, 1, 2))
-@pytest.mark.parametrize("name", NAMED)
+@pytest.mark.parametrize("name", NAMED + list(wl.FILTER_CASES))
 def test_named_workload_full_size(ba, name, seed):
-    case = wl.CASES[name]
+    case = wl.CASES[name] if name in wl.CASES else wl.FILTER_CASES[name]
     is_gemm = isinstance(case, wl.GemmCase)
     inp = wl.gen_gemm(case, seed) if is_gemm else wl.gen_conv(case, seed)
     y_t = run_gemm(case, inp) if is_gemm else run_conv(case, inp)

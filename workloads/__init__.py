@@ -236,6 +236,19 @@ CASES: Dict[str, object] = {
         (1, 1), "f16", "f16", "f16", "tanh", 0.0, U01, U01, U01, U01),
 }
 
+# 16-bit convs with filters larger than 3x3 (the pages' conv suites include
+# 7x7 filters in fp16 and bf16): the fp16 3x3 conv's shape with a 5x5 and a
+# 7x7 filter.  Not named workloads: parity-tested at full size and timed
+# beside them.
+FILTER_CASES: Dict[str, object] = {
+    "conv5x5_tanh_8x64x56_f16": ConvCase(
+        "conv5x5_tanh_8x64x56_f16", 8, 64, 56, 56, 64, 5, 5, (1, 1), (2, 2, 2, 2), (1, 1),
+        "f16", "f16", "f16", "tanh", 0.0, U01, U01, U01),
+    "conv7x7_tanh_8x64x56_bf16": ConvCase(
+        "conv7x7_tanh_8x64x56_bf16", 8, 64, 56, 56, 64, 7, 7, (1, 1), (3, 3, 3, 3), (1, 1),
+        "bf16", "bf16", "bf16", "tanh", 0.0, U01, U01, U01),
+}
+
 # Which case each named workload group covers (group 1 is the small spec case,
 # group 2 the 4096^3 headline, groups 4 and 5 hold two cases each).
 GROUPS = {
