@@ -148,21 +148,29 @@ struct DenseColLoader {
   static constexpr int RB = (NBLK + TL::threads - 1) / TL::threads;
 
   __amdgpu_buffer_rsrc_t rsrc;
-  uint32_t K, N, col[RB];          // first n of the block (global), or N (out of range)
+  uint32_t K, N, n0, col[RB];      // first n of the block (global), or N (out of range)
   int kb[RB], nb[RB];
   bool active[RB];
   bool vec;
   u32x4 reg[RB][EPC];
 
-  __device__ __forceinline__ void init(const void* p, uint32_t nbytes, uint32_t K_, uint32_t N_, uint32_t n0,
+  __device__ __forceinline__ void init(const void* p, uint32_t nbytes, uint32_t K_, uint32_t N_, uint32_t n0_,
                        bool vec_) {
     rsrc = make_rsrc(p, nbytes);
     K = K_;
     N = N_;
+    n0 = n0_;
     vec = vec_;
+    rebase(0);
+  }
+  // Blocks to threads, starting at thread `first` (mod the workgroup): with
+  // fewer blocks than threads, the all-k loop starts each k-tile's blocks
+  // where the previous one's ended, so every wave takes a share of the loads
+  // and register transposes instead of the first wave taking them all.
+  __device__ __forceinline__ void rebase(int first) {
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
-      const int q = threadIdx.x + i * TL::threads;
+      const int q = ((int)threadIdx.x + TL::threads - first) % TL::threads + i * TL::threads;
       active[i] = q < NBLK;
       kb[i] = q / NB_N;
       nb[i] = q % NB_N;
@@ -414,6 +422,7 @@ __device__ __forceinline__ void main_loop_allk(f32x16 (&acc)[TL::SN][TL::SM], co
   for (int k = 0; k < NK; ++k) {
     la[k] = la0;
     lb[k] = lb0;
+    if constexpr (LB::NBLK < TL::threads) lb[k].rebase((k * LB::NBLK) % TL::threads);
     if (k < ktiles) {
       la[k].load(k);
       lb[k].load(k);
