@@ -92,6 +92,8 @@ int launch_conv_plan(const ConvPlan& p, const void* x, const void* w, const void
   g.P = p.P;
   g.div_wo = make_fastdiv(p.Wo);
   g.div_howo = make_fastdiv(p.Ho * p.Wo);
+  g.div_khkw = make_fastdiv(p.kh * p.kw);
+  g.div_kw = make_fastdiv(p.kw);
   a.x_bytes = p.x_bytes;
   a.w_bytes = p.w_bytes;
   a.bias_bytes = p.bias_bytes;

@@ -260,6 +260,7 @@ struct ConvGeom {
   int32_t sh, sw, pt, pl, dh, dw;
   uint32_t K, P;                 // K = C*kh*kw, P = N*Ho*Wo
   FastDiv div_wo, div_howo;
+  FastDiv div_khkw, div_kw;      // the k -> (c_in, r, s) decode
 };
 
 template <int DT, class TL>
@@ -309,10 +310,12 @@ struct ConvGatherLoader {
 #pragma unroll
     for (int v = 0; v < CPP; ++v) {
       // k range of this chunk: wave-uniform
+      // (scalar divisions through FastDiv: a runtime division is tens of
+      // scalar instructions, and this runs for every chunk of every k-tile)
       const uint32_t kc = (uint32_t)kt * BK + (c0 + v * cstep) * EPC;
-      uint32_t cin = kc / (G.kh * G.kw);
+      uint32_t cin = fdiv(kc, G.div_khkw);
       uint32_t rs = kc - cin * G.kh * G.kw;
-      uint32_t r = rs / G.kw;
+      uint32_t r = fdiv(rs, G.div_kw);
       uint32_t s = rs - r * G.kw;
       uint32_t w[PPT][EPC];
 #pragma unroll
