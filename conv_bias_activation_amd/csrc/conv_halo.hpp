@@ -57,8 +57,8 @@ namespace biasact {
 namespace halo {
 constexpr int LDS_ONE = 144 * 1024;     // LDS of a workgroup that has its CU alone
 constexpr int LDS_TWO = 80 * 1024;      // LDS of a workgroup that shares its CU with another
-constexpr int HB = 4;     // input items per thread in the precomputed batch (2 at occupancy 2)
-constexpr int WB = 2;     // weight items per thread in the precomputed batch
+constexpr int HB = 4;     // input items per thread in the precomputed batch (2 with two workgroups
+                          // per CU, eight waves, or filters beyond 3x3)
 constexpr uint32_t kNone = 0xffffffffu;   // "no LDS write" marker of an item
 constexpr uint32_t kFar = 1u << 30;       // channel offset that fails every c < C test
 
