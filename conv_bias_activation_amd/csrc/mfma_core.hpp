@@ -74,6 +74,14 @@ __device__ __forceinline__ uint32_t ld_elem(__amdgpu_buffer_rsrc_t r, uint32_t o
   else return (uint32_t)ld_b16(r, off);
 }
 
+// One element at vector offset voff plus the wave-uniform scalar offset soff.
+template <int DT>
+__device__ __forceinline__ uint32_t ld_elem_so(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  if constexpr (Elem<DT>::bytes == 4) return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+  else if constexpr (Elem<DT>::bytes == 1) return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
+  else return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+
 // ---------------------------------------------------------------------------
 // j-side loader: a dense row-major [rows, K] matrix, k contiguous (GEMM A,
 // conv weights viewed as [Co, C*kh*kw]).  Each thread moves RA chunks per
@@ -275,6 +283,7 @@ struct ConvGatherLoader {
   __amdgpu_buffer_rsrc_t rsrc;
   ConvGeom g;
   int32_t pbase[PPT], ih0[PPT], iw0[PPT];
+  uint32_t pofs[PPT];           // 1x1 filters: the position's byte offset, or kOOB
   int prow[PPT];
   uint32_t c0;                  // first chunk index of this wave (wave-uniform)
   u32x4 reg[PPT][CPP];
@@ -300,11 +309,46 @@ struct ConvGatherLoader {
         iw0[u] = 0;
         pbase[u] = 0;
       }
+      const bool inside = (uint32_t)ih0[u] < geom.H && (uint32_t)iw0[u] < geom.W;
+      pofs[u] = inside ? (uint32_t)pbase[u] * ES : kOOB;
     }
     c0 = __builtin_amdgcn_readfirstlane((uint32_t)(threadIdx.x / TL::BN));
   }
 
+  // 1x1 filter, any stride and padding: k is the input channel and a
+  // position reads the same spatial offset for every k.  A position in the
+  // padding or past P got kOOB once in init(); each element load then takes
+  // its channel's offset as the scalar offset and costs no vector
+  // instruction (pofs + that offset stays below 2^32: both are < 2^31).
+  __device__ __forceinline__ void load_1x1(int kt) {
+    const uint32_t cstep = TL::threads >= TL::BN ? TL::threads / TL::BN : 1;
+    const uint32_t plane = g.H * g.W * ES;
+#pragma unroll
+    for (int v = 0; v < CPP; ++v) {
+      const uint32_t kc = (uint32_t)kt * BK + (c0 + v * cstep) * EPC;   // wave-uniform
+      uint32_t w[PPT][EPC];
+      if (kc + EPC <= g.K) {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e)
+#pragma unroll
+          for (int u = 0; u < PPT; ++u) w[u][e] = ld_elem_so<DT>(rsrc, pofs[u], (kc + e) * plane);
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e)
+#pragma unroll
+          for (int u = 0; u < PPT; ++u)
+            w[u][e] = kc + e < g.K ? ld_elem_so<DT>(rsrc, pofs[u], (kc + e) * plane) : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < PPT; ++u) reg[u][v] = pack_chunk<DT>(w[u]);
+    }
+  }
+
   __device__ __forceinline__ void load(int kt) {
+    if (g.kh == 1 && g.kw == 1) {
+      load_1x1(kt);
+      return;
+    }
     const ConvGeom& G = g;
     const uint32_t cstep = TL::threads >= TL::BN ? TL::threads / TL::BN : 1;
 #pragma unroll

@@ -326,6 +326,8 @@ CONV_SHAPES = [
     (1, 40, 9, 9, 136, 3, 3, (1, 1), (2, 2, 2, 2), (2, 2)),
     (1, 16, 6, 20, 24, 1, 9, (1, 1), (0, 0, 4, 4), (1, 1)),     # 9 taps, not 3x3: the generic kernel
     (1, 16, 20, 6, 24, 9, 1, (1, 1), (4, 4, 0, 0), (1, 1)),
+    (2, 37, 7, 9, 40, 1, 1, (1, 1), (1, 0, 2, 1), (1, 1)),      # 1x1 in padding, ragged last chunk
+    (1, 70, 5, 11, 33, 1, 1, (2, 3), (0, 0, 0, 0), (1, 1)),     # 1x1, unequal strides, odd W
 ]
 CONV_TYPES = [("f16", "f16", "f16"), ("bf16", "bf16", "bf16"), ("f32", "f32", "f32"),
               ("f16", "f32", "f32"), ("bf16", "bf16", "f32")]
@@ -351,13 +353,14 @@ def test_conv_every_tile_config(ba, tile):
     ba.force_tile_config(tile)
     try:
         for ti, to in (("f16", "f16"), ("f32", "f32")):
-            case = _ccase(2, 20, 15, 17, 75, 3, 3, (1, 2), (1, 0, 1, 2), (2, 1), ti, to, ti, "tanh")
-            inp = wl.gen_conv(case, seed=4)
-            y = values_of(run_conv(case, inp), to)
-            ref, floor = conv_reference(case, inp)
-            rep = check(y, ref, floor, case)
-            _report(f"conv tile {tile} {ti}", rep)
-            assert rep["ok"], rep
+            for k, geo in ((3, ((1, 2), (1, 0, 1, 2), (2, 1))), (1, ((2, 1), (1, 0, 0, 1), (1, 1)))):
+                case = _ccase(2, 36 if k == 1 else 20, 15, 17, 75, k, k, *geo, ti, to, ti, "tanh")
+                inp = wl.gen_conv(case, seed=4)
+                y = values_of(run_conv(case, inp), to)
+                ref, floor = conv_reference(case, inp)
+                rep = check(y, ref, floor, case)
+                _report(f"conv tile {tile} {ti} {k}x{k}", rep)
+                assert rep["ok"], rep
     finally:
         ba.force_tile_config(-1)
 
