@@ -158,6 +158,56 @@ __global__ __launch_bounds__(TL::threads, 1) void conv_bias_act_kernel(ConvArgs 
   constexpr int ACT = decltype(act_c)::value;
   with_residual(a.r != nullptr, [&](auto res_c) __attribute__((always_inline)) {
   constexpr bool HAS_R = decltype(res_c)::value;
+  if (a.vec_y) {
+    // Ho*Wo % 4 == 0: every group of four positions lies in one image.  The
+    // pre-activations leave through LDS, one 32-position column block (si) of
+    // every wave per pass, so that a store instruction covers 128-byte runs
+    // of 8 output rows instead of 16- (or 8-) byte pieces of 32 rows: row j
+    // (co - m0) holds WAVES_N runs of 32 positions, 16-byte chunk c of a run
+    // at slot c ^ (j & 7) (8 consecutive rows then spread over all banks).
+    constexpr int RUNS = TL::WAVES_N, ROWB = RUNS * 128;
+    static_assert(TL::BM * ROWB <= 2 * TL::stage_bytes, "staged column block exceeds the LDS tile");
+    constexpr int RSTEP = TL::threads / (8 * RUNS);          // rows between a thread's chunks
+    constexpr int CPT = TL::BM / RSTEP;                      // chunks per thread per pass
+    const uint32_t c = threadIdx.x & 7, rn = (threadIdx.x >> 3) % RUNS, r0 = (threadIdx.x >> 3) / RUNS;
+#pragma unroll
+    for (int si = 0; si < TL::SN; ++si) {
+      __syncthreads();      // the main loop's (or the previous pass's) LDS reads are done
+#pragma unroll
+      for (int sj = 0; sj < TL::SM; ++sj) {
+        const uint32_t j = wave_m * TL::WTM + sj * 32 + lrow;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t slot = (uint32_t)(2 * g + half) ^ (j & 7u);
+          f32x4 v = {acc[si][sj][4 * g + 0], acc[si][sj][4 * g + 1], acc[si][sj][4 * g + 2],
+                     acc[si][sj][4 * g + 3]};
+          *reinterpret_cast<f32x4*>(smem + j * ROWB + wave_n * 128 + slot * 16) = v;
+        }
+      }
+      __syncthreads();
+      const uint32_t p = p0 + rn * TL::WTN + si * 32 + 4 * c;
+      const uint32_t img = fdiv(p, G.div_howo);
+      const uint32_t base = img * G.Co * howo + (p - img * howo);
+      const bool pok = p < G.P;
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) {
+        const uint32_t j = r0 + (uint32_t)(k * RSTEP), co = m0 + j;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(smem + j * ROWB + rn * 128 + ((c ^ (j & 7u)) * 16));
+        float z[4] = {v[0], v[1], v[2], v[3]};
+        const uint32_t off = base + co * howo;
+        const bool ok = pok && co < G.Co;
+        if constexpr (HAS_R) {
+          float rv[4];
+          load4<DTO>(rr, off, ok, rv);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) z[e] += rv[e];
+        }
+        store4<DTO>(ry, off, ok, act_fn<ACT, DTO>(z[0], a.alpha), act_fn<ACT, DTO>(z[1], a.alpha),
+                    act_fn<ACT, DTO>(z[2], a.alpha), act_fn<ACT, DTO>(z[3], a.alpha));
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int si = 0; si < TL::SN; ++si)
 #pragma unroll
@@ -167,34 +217,16 @@ __global__ __launch_bounds__(TL::threads, 1) void conv_bias_act_kernel(ConvArgs 
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const uint32_t p = p0 + wave_n * TL::WTN + si * 32 + 8 * g + 4 * half;
-        float z[4] = {acc[si][sj][4 * g + 0], acc[si][sj][4 * g + 1], acc[si][sj][4 * g + 2],
-                      acc[si][sj][4 * g + 3]};
-        if (a.vec_y) {
-          // Ho*Wo % 4 == 0: the four positions lie in one image
-          const uint32_t img = fdiv(p, G.div_howo);
-          const uint32_t q = p - img * howo;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t pe = p + e;
+          const uint32_t img = fdiv(pe, G.div_howo);
+          const uint32_t q = pe - img * howo;
           const uint32_t off = (img * G.Co + co) * howo + q;
-          const bool ok = cok && p < G.P;
-          if constexpr (HAS_R) {
-            float rv[4];
-            load4<DTO>(rr, off, ok, rv);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) z[e] += rv[e];
-          }
-          store4<DTO>(ry, off, ok, act_fn<ACT, DTO>(z[0], a.alpha), act_fn<ACT, DTO>(z[1], a.alpha),
-                      act_fn<ACT, DTO>(z[2], a.alpha), act_fn<ACT, DTO>(z[3], a.alpha));
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t pe = p + e;
-            const uint32_t img = fdiv(pe, G.div_howo);
-            const uint32_t q = pe - img * howo;
-            const uint32_t off = (img * G.Co + co) * howo + q;
-            const bool ok = cok && pe < G.P;
-            float ze = z[e];
-            if constexpr (HAS_R) ze += load1<DTO>(rr, off, ok);
-            store1<DTO>(ry, off, ok, act_fn<ACT, DTO>(ze, a.alpha));
-          }
+          const bool ok = cok && pe < G.P;
+          float ze = acc[si][sj][4 * g + e];
+          if constexpr (HAS_R) ze += load1<DTO>(rr, off, ok);
+          store1<DTO>(ry, off, ok, act_fn<ACT, DTO>(ze, a.alpha));
         }
       }
     }
