@@ -71,6 +71,37 @@ __global__ __launch_bounds__(TL::threads, 1) void gemm_bias_act_kernel(GemmArgs 
   constexpr int ACT = decltype(act_c)::value;
   with_residual(a.R != nullptr, [&](auto res_c) __attribute__((always_inline)) {
   constexpr bool HAS_R = decltype(res_c)::value;
+  if (a.vec_c) {
+    // N % 4 == 0 and C (and R) 16-byte aligned: the sums leave through LDS
+    // (StagedOut), whole 128-byte row runs per store
+    using SO = StagedOut<TL>;
+    static_assert(SO::bytes <= (NK > 2 ? NK : 2) * TL::stage_bytes, "staged column block exceeds the LDS tile");
+    const SO so;
+#pragma unroll
+    for (int si = 0; si < TL::SN; ++si) {
+      __syncthreads();      // the main loop's (or the previous pass's) LDS reads are done
+      SO::put(acc, smem, si);
+      __syncthreads();
+      const uint32_t n = n0 + so.col(si);
+#pragma unroll
+      for (int k = 0; k < SO::CPT; ++k) {
+        const uint32_t m = m0 + so.row(k);
+        const f32x4 v = so.get(smem, k);
+        float z[4] = {v[0], v[1], v[2], v[3]};
+        const bool ok = m < a.M && n < a.N;
+        if constexpr (HAS_R && DTI != DT_I8) {
+          float rv[4];
+          load4<DTO>(rr, m * a.N + n, ok, rv);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) z[e] += rv[e];
+        }
+        store4<DTO>(rc, m * a.N + n, ok, out_value<DTI, DTO, ACT>(z[0], a.alpha),
+                    out_value<DTI, DTO, ACT>(z[1], a.alpha), out_value<DTI, DTO, ACT>(z[2], a.alpha),
+                    out_value<DTI, DTO, ACT>(z[3], a.alpha));
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int si = 0; si < TL::SN; ++si)
 #pragma unroll
@@ -159,40 +190,24 @@ __global__ __launch_bounds__(TL::threads, 1) void conv_bias_act_kernel(ConvArgs 
   with_residual(a.r != nullptr, [&](auto res_c) __attribute__((always_inline)) {
   constexpr bool HAS_R = decltype(res_c)::value;
   if (a.vec_y) {
-    // Ho*Wo % 4 == 0: every group of four positions lies in one image.  The
-    // pre-activations leave through LDS, one 32-position column block (si) of
-    // every wave per pass, so that a store instruction covers 128-byte runs
-    // of 8 output rows instead of 16- (or 8-) byte pieces of 32 rows: row j
-    // (co - m0) holds WAVES_N runs of 32 positions, 16-byte chunk c of a run
-    // at slot c ^ (j & 7) (8 consecutive rows then spread over all banks).
-    constexpr int RUNS = TL::WAVES_N, ROWB = RUNS * 128;
-    static_assert(TL::BM * ROWB <= 2 * TL::stage_bytes, "staged column block exceeds the LDS tile");
-    constexpr int RSTEP = TL::threads / (8 * RUNS);          // rows between a thread's chunks
-    constexpr int CPT = TL::BM / RSTEP;                      // chunks per thread per pass
-    const uint32_t c = threadIdx.x & 7, rn = (threadIdx.x >> 3) % RUNS, r0 = (threadIdx.x >> 3) / RUNS;
+    // Ho*Wo % 4 == 0: every group of four positions lies in one image; the
+    // pre-activations leave through LDS (StagedOut)
+    using SO = StagedOut<TL>;
+    static_assert(SO::bytes <= 2 * TL::stage_bytes, "staged column block exceeds the LDS tile");
+    const SO so;
 #pragma unroll
     for (int si = 0; si < TL::SN; ++si) {
       __syncthreads();      // the main loop's (or the previous pass's) LDS reads are done
-#pragma unroll
-      for (int sj = 0; sj < TL::SM; ++sj) {
-        const uint32_t j = wave_m * TL::WTM + sj * 32 + lrow;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const uint32_t slot = (uint32_t)(2 * g + half) ^ (j & 7u);
-          f32x4 v = {acc[si][sj][4 * g + 0], acc[si][sj][4 * g + 1], acc[si][sj][4 * g + 2],
-                     acc[si][sj][4 * g + 3]};
-          *reinterpret_cast<f32x4*>(smem + j * ROWB + wave_n * 128 + slot * 16) = v;
-        }
-      }
+      SO::put(acc, smem, si);
       __syncthreads();
-      const uint32_t p = p0 + rn * TL::WTN + si * 32 + 4 * c;
+      const uint32_t p = p0 + so.col(si);
       const uint32_t img = fdiv(p, G.div_howo);
       const uint32_t base = img * G.Co * howo + (p - img * howo);
       const bool pok = p < G.P;
 #pragma unroll
-      for (int k = 0; k < CPT; ++k) {
-        const uint32_t j = r0 + (uint32_t)(k * RSTEP), co = m0 + j;
-        const f32x4 v = *reinterpret_cast<const f32x4*>(smem + j * ROWB + rn * 128 + ((c ^ (j & 7u)) * 16));
+      for (int k = 0; k < SO::CPT; ++k) {
+        const uint32_t co = m0 + so.row(k);
+        const f32x4 v = so.get(smem, k);
         float z[4] = {v[0], v[1], v[2], v[3]};
         const uint32_t off = base + co * howo;
         const bool ok = pok && co < G.Co;

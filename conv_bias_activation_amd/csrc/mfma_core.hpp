@@ -488,4 +488,57 @@ __device__ __forceinline__ void main_loop_allk(f32x16 (&acc)[TL::SN][TL::SM], co
     if (k < ktiles) tile_mma<DT, TL>(acc, smem + k * TL::stage_bytes, smem + k * TL::stage_bytes + TL::a_bytes);
 }
 
+// ---------------------------------------------------------------------------
+// Output staging.  The accumulator layout gives a lane 4 consecutive
+// outputs of one row (GEMM row m, conv output channel co) per register group,
+// so a store straight from it covers 16- (or 8-) byte pieces of 32 rows.
+// Instead, one 32-wide column block (si) of every wave goes through the LDS
+// tile per pass: row j (0 .. BM-1) holds WAVES_N runs of 32 outputs, the
+// 16-byte chunk c of a run at slot c ^ (j & 7), so 8 consecutive rows spread
+// over all banks both when written in the accumulator layout and when read
+// by rows.  Thread t then owns chunk c = t % 8 of run rn = (t / 8) % WAVES_N
+// in rows r0, r0 + RSTEP, ... : a store instruction covers 128-byte runs of
+// 8 rows.
+// ---------------------------------------------------------------------------
+template <class TL>
+struct StagedOut {
+  static constexpr int RUNS = TL::WAVES_N, ROWB = RUNS * 128;
+  static constexpr int RSTEP = TL::threads / (8 * RUNS);   // rows between a thread's chunks
+  static constexpr int CPT = TL::BM / RSTEP;                // chunks per thread per pass
+  static constexpr int bytes = TL::BM * ROWB;
+  uint32_t c, rn, r0;
+
+  __device__ __forceinline__ StagedOut()
+      : c(threadIdx.x & 7), rn((threadIdx.x >> 3) % RUNS), r0((threadIdx.x >> 3) / RUNS) {}
+
+  // column (within the tile) of this thread's first output in pass si
+  __device__ __forceinline__ uint32_t col(int si) const { return rn * TL::WTN + si * 32 + 4 * c; }
+  // row (within the tile) of this thread's chunk k
+  __device__ __forceinline__ uint32_t row(int k) const { return r0 + (uint32_t)(k * RSTEP); }
+
+  // column block si of this wave's accumulators into the staging area (the
+  // caller has a barrier before, so the area is free, and one after)
+  __device__ __forceinline__ static void put(const f32x16 (&acc)[TL::SN][TL::SM], uint8_t* smem, int si) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wave_m = wave / TL::WAVES_N, wave_n = wave % TL::WAVES_N;
+    const int half = lane >> 5, lrow = lane & 31;
+#pragma unroll
+    for (int sj = 0; sj < TL::SM; ++sj) {
+      const uint32_t j = wave_m * TL::WTM + sj * 32 + lrow;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t slot = (uint32_t)(2 * g + half) ^ (j & 7u);
+        const f32x4 v = {acc[si][sj][4 * g + 0], acc[si][sj][4 * g + 1], acc[si][sj][4 * g + 2],
+                         acc[si][sj][4 * g + 3]};
+        *reinterpret_cast<f32x4*>(smem + j * ROWB + wave_n * 128 + slot * 16) = v;
+      }
+    }
+  }
+  // this thread's chunk k of the staged block
+  __device__ __forceinline__ f32x4 get(const uint8_t* smem, int k) const {
+    const uint32_t j = row(k);
+    return *reinterpret_cast<const f32x4*>(smem + j * ROWB + rn * 128 + ((c ^ (j & 7u)) * 16));
+  }
+};
+
 }  // namespace biasact
