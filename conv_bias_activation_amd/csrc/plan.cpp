@@ -266,14 +266,36 @@ int select_gemm_tile(int64_t M, int64_t N, int64_t /*K*/, int dti) {
   return pick_tile(order, 5, M, N, 256);
 }
 
+// Among the tiles (in preference order) that give at least 256 workgroups,
+// the one whose busiest CU computes the fewest outputs: a grid of `tiles`
+// workgroups puts ceil(tiles / 256) of them on some CU.  A later (smaller)
+// tile must cut that load by at least an eighth to be taken, since its
+// per-workgroup costs (operand round trip, epilogue) weigh more.  With no
+// tile reaching 256 workgroups, pick_tile's choice.
+int pick_tile_balanced(const int* order, int n_order, int64_t rows_j, int64_t rows_i) {
+  int best = -1;
+  int64_t best_load = 0;
+  for (int k = 0; k < n_order; ++k) {
+    const TileShapeDesc& t = kTiles[order[k]];
+    const int64_t tiles = ceil_div(rows_j, t.bm) * ceil_div(rows_i, t.bn);
+    if (tiles < 256) continue;
+    const int64_t load = ceil_div(tiles, 256) * t.bm * t.bn;
+    if (best < 0 || load * 8 <= best_load * 7) {
+      best = order[k];
+      best_load = load;
+    }
+  }
+  return best >= 0 ? best : pick_tile(order, n_order, rows_j, rows_i, 256);
+}
+
 int select_conv_tile(int64_t N, int64_t Co, int64_t Ho, int64_t Wo, int64_t /*K*/, int /*dti*/) {
   const int64_t P = N * Ho * Wo;
   if (Co <= 64) {
     static const int order[] = {4, 3, 5};
-    return pick_tile(order, 3, Co, P, 256);
+    return pick_tile_balanced(order, 3, Co, P);
   }
   static const int order[] = {0, 1, 2, 3, 5};
-  return pick_tile(order, 5, Co, P, 256);
+  return pick_tile_balanced(order, 5, Co, P);
 }
 
 int plan_gemm(const void* A, const void* B, const void* bias, const void* C, int64_t M, int64_t N,

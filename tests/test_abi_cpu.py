@@ -97,6 +97,19 @@ def test_tile_table_introspection():
         ba.force_tile_config(n)
 
 
+def test_conv_tile_balances_the_busiest_cu():
+    f32 = _dt(F32, F32, F32, F32)
+    # 16 x 512 x 28 x 28 output (the 1x1 stride-2 conv of 16 x 256 x 56 x 56):
+    # 128x128 tiles make 392 workgroups, two on some CUs (32768 outputs);
+    # 64x64 tiles make 1568, seven on some CUs (28672): an eighth less
+    assert ba.tile_config_name(ba.conv_tile_config(16, 512, 28, 28, 256, f32)) == "64x64/2x2"
+    # 16 x 512 x 32 x 32: 128x256 gives 256 workgroups, one per CU; every
+    # smaller tile gives the busiest CU the same 32768 outputs
+    assert ba.tile_config_name(ba.conv_tile_config(16, 512, 32, 32, 256, f32)) == "128x256/2x2"
+    # Co <= 64: 8 x 64 x 56 x 56 positions, 64x64 tiles (392 workgroups) as before
+    assert ba.tile_config_name(ba.conv_tile_config(8, 64, 56, 56, 576, f32)) == "64x64/2x2"
+
+
 def test_halo_variant_override_range():
     for v in (-1, 0, 1, 2, 3, 4):
         ba.force_halo_variant(v)
