@@ -247,6 +247,11 @@ CONV_CASES = [
     ((1, 5, 13, 9, 70, 5, 5, (1, 1), (2, 1, 0, 2), (1, 1)), "f32", "bf16", "relu", -1, "conv-halo fp32"),
     ((2, 24, 13, 11, 40, 3, 3, (2, 1), (1, 1, 0, 2), (1, 2)), "f16", "f16", "tanh", 3, "conv 64x128"),
     ((2, 32, 14, 14, 48, 1, 1, (2, 2), (0, 0, 0, 0), (1, 1)), "f32", "f32", "none", -1, "conv "),
+    # Ho*Wo % 4 == 0 on the generic kernel: outputs staged through LDS (and,
+    # with R one element off, element-wise: the same bits)
+    ((2, 32, 16, 16, 48, 1, 1, (2, 2), (0, 0, 0, 0), (1, 1)), "f32", "f32", "tanh", -1, "conv "),
+    ((2, 20, 12, 12, 72, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1)), "f16", "f16", "gelu", -1, "conv "),
+    ((1, 36, 10, 10, 130, 1, 1, (1, 1), (1, 1, 1, 1), (1, 1)), "bf16", "bf16", "relu", 1, "conv 128x256"),
 ]
 
 
