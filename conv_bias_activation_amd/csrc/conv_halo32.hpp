@@ -39,7 +39,6 @@
 #include "launch.hpp"
 #include "launch_kernel.hpp"
 #include "mfma_core.hpp"
-#include "tile_map.hpp"
 
 namespace biasact {
 
@@ -72,9 +71,11 @@ __global__ __launch_bounds__(256, 2) void conv32_halo_kernel(HaloArgs a) {
   // column block fastest.  Workgroup -> (co block, one patch); with a resident
   // filter (a.groups > 0, one co block, one chunk) workgroup b takes patches
   // [b P / groups, (b + 1) P / groups) of the P = N * h_blocks * w_blocks.
-  // Workgroups are renumbered so that each XCD takes a contiguous range of
-  // patches: neighbouring patches, whose halos share input rows, share an L2.
-  const uint32_t wg = xcd_contiguous(blockIdx.x, gridDim.x);
+  // (Numbering the workgroups so that each XCD takes a contiguous range of
+  // patches, as the 16-bit kernel does, measured 1.3 % slower on the fp32
+  // stem in alternating runs, although it cut the input's re-reads from HBM
+  // from 2.0x to 1.2x: at this kernel's 0.3 TB/s they limit nothing.)
+  const uint32_t wg = blockIdx.x;
   uint32_t cb = 0, p_first, p_end;
   if (a.groups) {
     const uint32_t P = G.N * a.h_blocks * a.w_blocks;
