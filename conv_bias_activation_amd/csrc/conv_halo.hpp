@@ -5,15 +5,16 @@
 // features as the k x spatial operand).
 //
 // The reduction index is ordered (tap, channel): k = t * C + c with
-// t = r * kw + s.  For one tap and 8 consecutive channels, both operands are
-// 16 contiguous bytes in LDS:
+// t = r * kw + s.  For one tap and 8 consecutive channels the input operand
+// is 16 contiguous bytes of the LDS halo
 //   halo  [row][col][c] : input rows  ih = oh*sh - pt + r*dh of the patch,
 //                         columns iw = iw_lo + col (iw_lo even, <= ow0*sw - pl)
-//   wts   [t][co][c]
-// so every MFMA fragment is one ds_read_b128 whatever the stride, padding or
+// so every input fragment is one ds_read_b128 whatever the stride, padding or
 // dilation, and each input element is fetched from memory once per channel
-// chunk instead of once per tap.  Channels are staged in chunks of
-// BKC = 16 * KS (KS = 1, 2, 4 MFMA k-steps per tap; zero-filled past C).
+// chunk instead of once per tap.  The weight fragments (8 channels of one tap
+// per lane) are regrouped in registers from the chunk's raw OIHW rows in LDS
+// (below).  Channels are staged in chunks of BKC = 16 * KS (KS = 1, 2, 4 MFMA
+// k-steps per tap; zero-filled past C).
 //
 // Workgroup: NW = 4 or 8 waves as 2 (output-channel halves) x NW / 2
 // (position groups), BM output channels x a patch of PH output rows x PW
@@ -37,11 +38,12 @@
 // T * KS (tap, k-step) steps; a step's input fragments are read two steps
 // ahead.
 //
-// LDS rows (one halo position, or one (tap, co) weight row) hold NCH = 2 * KS
-// chunks of 16 bytes; chunk c of row p sits at slot c ^ ((p >> S) % NCH) with
-// 2^S = 16 / NCH rows per 256 bytes, so the 16 lanes of a read phase that
-// take 16 consecutive rows hit all 64 banks once.  The bias is fetched as raw
-// words after the first staging loads and added in the epilogue.
+// Halo rows (one position) hold NCH = 2 * KS chunks of 16 bytes; chunk c of
+// row p sits at slot c ^ ((p >> S) % NCH) with 2^S = 16 / NCH rows per 256
+// bytes, so the 16 lanes of a read phase that take 16 consecutive rows hit
+// all 64 banks once.  Raw weight rows carry one 16-byte pad piece each, so 16
+// consecutive rows start in 16 different bank groups.  The bias is fetched as
+// raw words after the first staging loads and added in the epilogue.
 #pragma once
 
 #include <utility>

@@ -1,13 +1,17 @@
 // mfma_core.hpp — the fused contraction + bias + activation main loop for
 // gfx950: LDS double-buffered operand tiles, 32x32 MFMA accumulation in fp32,
-// and a register epilogue (activation, output cast, one store per element).
+// and the epilogue's output staging (activation, output cast, one store per
+// element).
 //
 // Orientation.  The MFMA "row" index i runs over the output's contiguous
 // dimension (GEMM column n, conv spatial position p) and the MFMA "column"
 // index j over the other one (GEMM row m, conv output channel co).  With the
 // 32x32 accumulator layout (lane l, register r <-> i = 8*(r/4) + 4*(l/32) +
 // r%4, j = l%32) each lane then owns four consecutive output elements per
-// register group, which it writes with one 8- or 16-byte store.
+// register group.  Where output rows allow 4-wide accesses the kernels pass
+// them through the LDS tile first (StagedOut, at the end of this file), so
+// that a store covers 128-byte runs of 8 rows; otherwise each lane stores
+// its elements one by one.
 //
 // LDS layout.  Both operand tiles are stored k-contiguous: one 128-byte LDS
 // row per i (or j) index holding 8 chunks of 16 bytes (BK = 64 16-bit values
