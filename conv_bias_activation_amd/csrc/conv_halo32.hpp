@@ -82,17 +82,19 @@ __global__ __launch_bounds__(256, 2) void conv32_halo_kernel(HaloArgs a) {
     p_first = (uint32_t)((uint64_t)wg * P / a.groups);
     p_end = (uint32_t)((uint64_t)(wg + 1) * P / a.groups);
   } else {
-    cb = wg % a.co_blocks;
-    p_first = wg / a.co_blocks;
+    p_first = fdiv(wg, a.div_cob);
+    cb = wg - p_first * a.co_blocks;
     p_end = p_first + 1;
   }
   const uint32_t co0 = cb * BM;
   // patch pi -> image, first output row and column
+  // (divisions by the grid's invariant counts through FastDiv: a runtime
+  // integer division costs tens of instructions)
   auto patch = [&](uint32_t pi, uint32_t& img, uint32_t& oh0, uint32_t& ow0) {
-    ow0 = (pi % a.w_blocks) * a.PW;
-    pi /= a.w_blocks;
-    oh0 = (pi % a.h_blocks) * a.PH;
-    img = pi / a.h_blocks;
+    const uint32_t r = fdiv(pi, a.div_wb);
+    ow0 = (pi - r * a.w_blocks) * a.PW;
+    img = fdiv(r, a.div_hb);
+    oh0 = (r - img * a.h_blocks) * a.PH;
   };
 
   const int lane = threadIdx.x & 63;
@@ -166,7 +168,7 @@ __global__ __launch_bounds__(256, 2) void conv32_halo_kernel(HaloArgs a) {
 #pragma unroll
   for (int si = 0; si < SN; ++si) {
     const uint32_t q = wave_n * halo32::WTN + si * 32 + lrow;
-    const uint32_t qh = q / a.PW, qw = q - qh * a.PW;
+    const uint32_t qh = fdiv(q, a.div_pw), qw = q - qh * a.PW;
     // lanes past the patch read position 0 (in range); their results are never stored
     pb[si] = q < a.PH * a.PW ? qh * G.sh * HC + qw * G.sw : 0u;
   }
@@ -268,7 +270,7 @@ __global__ __launch_bounds__(256, 2) void conv32_halo_kernel(HaloArgs a) {
           for (int e = 0; e < 4; ++e) z[e] = acc[si][sj][4 * g + e] + bvv[sj];
           if (a.vec_y) {
             // PW % 4 == 0 and Wo % 4 == 0: positions q..q+3 share an output row
-            const uint32_t qh = q / a.PW, qw = q - qh * a.PW;
+            const uint32_t qh = fdiv(q, a.div_pw), qw = q - qh * a.PW;
             const uint32_t oh = oh0 + qh, ow = ow0 + qw;
             const bool ok = cok && q < npos && oh < G.Ho && ow < G.Wo;
             if constexpr (HAS_R) {
@@ -284,7 +286,7 @@ __global__ __launch_bounds__(256, 2) void conv32_halo_kernel(HaloArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const uint32_t qe = q + e;
-              const uint32_t qh = qe / a.PW, qw = qe - qh * a.PW;
+              const uint32_t qh = fdiv(qe, a.div_pw), qw = qe - qh * a.PW;
               const uint32_t oh = oh0 + qh, ow = ow0 + qw;
               const bool ok = cok && qe < npos && oh < G.Ho && ow < G.Wo;
               float ze = z[e];
