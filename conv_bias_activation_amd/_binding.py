@@ -3,6 +3,7 @@ contract of every entry point).  No arithmetic of the method happens here."""
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from typing import Optional, Sequence
 
@@ -128,6 +129,7 @@ def _check(status: int, what: str):
     raise BiasActError(status, msg)
 
 
+@functools.lru_cache(maxsize=None)
 def dtypes_code(a: str, b: str, bias: Optional[str], out: str) -> int:
     try:
         codes = [DTYPE_CODES[a], DTYPE_CODES[b], DTYPE_CODES[bias or "f32"], DTYPE_CODES[out]]
@@ -151,14 +153,20 @@ def _torch():
     return torch
 
 
+_TNAMES = None      # torch dtype -> element type name, built on first use
+
+
 def _tname(t) -> str:
-    torch = _torch()
-    m = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16", torch.int8: "i8",
-         torch.int32: "i32"}
-    if t.dtype not in m:
+    global _TNAMES
+    if _TNAMES is None:
+        torch = _torch()
+        _TNAMES = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16", torch.int8: "i8",
+                   torch.int32: "i32"}
+    name = _TNAMES.get(t.dtype)
+    if name is None:
         raise ValueError(f"unsupported tensor dtype {t.dtype}; supported: float32, float16, "
                          "bfloat16, int8 and int32 (int8 GEMMs)")
-    return m[t.dtype]
+    return name
 
 
 def _dev(t, name):
