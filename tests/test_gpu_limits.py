@@ -94,3 +94,63 @@ def test_conv_output_just_under_2gib(ba, ti, to, kh, N, C):
     ref, floor = conv_reference(case, inp, idx=idx)
     rep = check(yv, ref, floor, case)
     assert rep["ok"], rep
+
+
+def _tiled(words, reps):
+    # a seeded block repeated along the leading dimension: the operand's
+    # last rows are known without drawing 2 GiB of random numbers
+    return np.concatenate([words] * reps, axis=0)
+
+
+def test_gemm_operand_a_just_under_2gib(ba):
+    # A is 65536 x 16376 bf16 (2^31 - 1 MiB bytes): the rows that read its
+    # tail (the last 64 output rows) and its head, against the oracle
+    M, N, K = 65536, 64, 16376
+    assert LIMIT - (2 << 20) < M * K * 2 < LIMIT
+    blk = wl.GemmCase("lim_a_blk", 256, N, K, "bf16", "f32", "f32", "relu")
+    inp = wl.gen_gemm(blk, seed=45)
+    a_words = inp["A"].reshape(256, K)
+    A, _ = to_dev(_tiled(a_words, M // 256), "bf16")
+    B, _ = to_dev(inp["B"].reshape(K, N), "bf16")
+    bias, _ = to_dev(inp["bias"], "f32")
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    try:
+        ba.gemm_bias_act(A, B, bias, C, "relu", 0.0)
+        torch.cuda.synchronize()
+        head = values_of(C[:64], "f32")
+        tail = values_of(C[M - 64:], "f32")
+    finally:
+        del A, C
+        torch.cuda.empty_cache()
+    # rows 0..63 and M-64..M-1 of A are block rows 0..63 and 192..255
+    for rows, y in ((slice(0, 64), head), (slice(192, 256), tail)):
+        sub = wl.GemmCase("lim_a_rows", 64, N, K, "bf16", "f32", "f32", "relu")
+        ref, floor = gemm_reference(sub, dict(inp, A=a_words[rows]))
+        rep = check(y, ref, floor, sub)
+        assert rep["ok"], rep
+
+
+def test_conv_input_just_under_2gib(ba):
+    # x is 63 x 64 x 512 x 512 fp16 (2^31 - 32 MiB bytes) on the conv-halo
+    # kernel: the first and the last image (the tail of x) against the oracle
+    N, C, H, W, Co = 63, 64, 512, 512, 8
+    assert LIMIT - (64 << 20) < N * C * H * W * 2 < LIMIT
+    one = wl.ConvCase("lim_x_img", 1, C, H, W, Co, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1), "f16", "f16", "f16", "tanh")
+    inp = wl.gen_conv(one, seed=46)
+    x, _ = to_dev(_tiled(inp["x"].reshape(1, C, H, W), N), "f16")
+    w, _ = to_dev(inp["w"].reshape(Co, C, 3, 3), "f16")
+    bias, _ = to_dev(inp["bias"], "f16")
+    y = torch.empty((N, Co, H, W), dtype=torch.float16, device="cuda")
+    try:
+        ba.conv2d_bias_act(x, w, bias, y, (1, 1), (1, 1, 1, 1), (1, 1), "tanh")
+        torch.cuda.synchronize()
+        assert ba.last_tile_config().startswith("conv-halo 9"), ba.last_tile_config()
+        first = values_of(y[0], "f16")
+        last = values_of(y[N - 1], "f16")
+    finally:
+        del x, y
+        torch.cuda.empty_cache()
+    ref, floor = conv_reference(one, inp)
+    for yv in (first, last):
+        rep = check(yv, ref, floor, one)
+        assert rep["ok"], rep
