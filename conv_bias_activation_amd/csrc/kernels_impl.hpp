@@ -252,28 +252,38 @@ __global__ __launch_bounds__(TL::threads, 1) void conv_bias_act_kernel(ConvArgs 
 // ---------------------------------------------------------------------------
 // Second kernel of the two-kernel path: out[i] = cast(act(ws[i] (+ res[i])))
 // over a packed fp32 workspace that already holds A.B + bias (GEMM, [M,N]) or
-// conv + bias (conv, NCHW); res, if given, is the residual in out's type.  Each thread handles 16 consecutive elements per
-// pass with four 16-byte loads issued before any is used (64 bytes in flight
-// per lane); grid-stride over the array with a grid that fills every CU.
+// conv + bias (conv, NCHW); res, if given, is the residual in out's type.
+// Each thread handles 16 elements per pass, as four groups of 4 consecutive
+// ones, with four 16-byte loads issued before any is used (64 bytes in
+// flight per lane); grid-stride over the array with a grid that fills every
+// CU.
 // ---------------------------------------------------------------------------
 template <int DTO>
 __global__ __launch_bounds__(256) void act_cast_kernel(const float* ws, void* out, uint32_t n,
                                                        int act, float alpha, const void* res) {
-  constexpr uint32_t EPT = 16;
+  constexpr uint32_t EPT = 16, WT = 64 * EPT;       // elements per thread, per wave tile
   const __amdgpu_buffer_rsrc_t ri = make_rsrc(ws, n * 4u);
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(out, n * (uint32_t)Elem<DTO>::bytes);
   const __amdgpu_buffer_rsrc_t rr = make_rsrc(res, res ? n * (uint32_t)Elem<DTO>::bytes : 0u);
-  const uint32_t stride = gridDim.x * blockDim.x * EPT;
+  // A wave takes tiles of 1024 consecutive elements; its q-th access covers
+  // elements [q * 256, q * 256 + 256) of the tile, four per lane, so every
+  // load and store instruction moves one contiguous run across the wave.
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const uint32_t stride = ((gridDim.x * blockDim.x) >> 6) * WT;
   auto run = [&](auto act_c, auto res_c) __attribute__((always_inline)) {
     constexpr int ACT = decltype(act_c)::value;
     constexpr bool HAS_R = decltype(res_c)::value;
-    for (uint32_t base = (blockIdx.x * blockDim.x + threadIdx.x) * EPT; base < n; base += stride) {
-      const bool full = base + EPT <= n;
+    for (uint32_t tile = wave * WT; tile < n; tile += stride) {
+      const bool full = tile + WT <= n;
+      uint32_t first[EPT / 4];                       // this lane's first element of access q
+#pragma unroll
+      for (uint32_t q = 0; q < EPT / 4; ++q) first[q] = tile + q * 256 + lane * 4;
       float z[EPT];
       if (full) {
         u32x4 v[EPT / 4];
 #pragma unroll
-        for (uint32_t q = 0; q < EPT / 4; ++q) v[q] = ld_b128(ri, (base + 4 * q) * 4u);
+        for (uint32_t q = 0; q < EPT / 4; ++q) v[q] = ld_b128(ri, first[q] * 4u);
 #pragma unroll
         for (uint32_t q = 0; q < EPT / 4; ++q) {
           z[4 * q + 0] = __uint_as_float(v[q].x);
@@ -283,8 +293,12 @@ __global__ __launch_bounds__(256) void act_cast_kernel(const float* ws, void* ou
         }
       } else {
 #pragma unroll
-        for (uint32_t e = 0; e < EPT; ++e)
-          z[e] = __uint_as_float(ld_b32(ri, base + e < n ? (base + e) * 4u : kOOB));
+        for (uint32_t q = 0; q < EPT / 4; ++q)
+#pragma unroll
+          for (uint32_t e = 0; e < 4; ++e) {
+            const uint32_t i = first[q] + e;
+            z[4 * q + e] = __uint_as_float(ld_b32(ri, i < n ? i * 4u : kOOB));
+          }
       }
       if constexpr (HAS_R) {
         // the residual joins the pre-activation (A.B + bias) before act
@@ -292,13 +306,15 @@ __global__ __launch_bounds__(256) void act_cast_kernel(const float* ws, void* ou
 #pragma unroll
           for (uint32_t q = 0; q < EPT / 4; ++q) {
             float rv[4];
-            load4<DTO>(rr, base + 4 * q, true, rv);
+            load4<DTO>(rr, first[q], true, rv);
 #pragma unroll
             for (int e = 0; e < 4; ++e) z[4 * q + e] += rv[e];
           }
         } else {
 #pragma unroll
-          for (uint32_t e = 0; e < EPT; ++e) z[e] += load1<DTO>(rr, base + e, base + e < n);
+          for (uint32_t q = 0; q < EPT / 4; ++q)
+#pragma unroll
+            for (uint32_t e = 0; e < 4; ++e) z[4 * q + e] += load1<DTO>(rr, first[q] + e, first[q] + e < n);
         }
       }
       float y[EPT];
@@ -307,10 +323,12 @@ __global__ __launch_bounds__(256) void act_cast_kernel(const float* ws, void* ou
       if (full) {
 #pragma unroll
         for (uint32_t q = 0; q < EPT / 4; ++q)
-          store4<DTO>(ro, base + 4 * q, true, y[4 * q], y[4 * q + 1], y[4 * q + 2], y[4 * q + 3]);
+          store4<DTO>(ro, first[q], true, y[4 * q], y[4 * q + 1], y[4 * q + 2], y[4 * q + 3]);
       } else {
 #pragma unroll
-        for (uint32_t e = 0; e < EPT; ++e) store1<DTO>(ro, base + e, base + e < n, y[e]);
+        for (uint32_t q = 0; q < EPT / 4; ++q)
+#pragma unroll
+          for (uint32_t e = 0; e < 4; ++e) store1<DTO>(ro, first[q] + e, first[q] + e < n, y[4 * q + e]);
       }
     }
   };
