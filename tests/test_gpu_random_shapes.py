@@ -127,3 +127,29 @@ def test_random_conv_vs_oracle(ba, case):
     _compare(y, ref, floor, case)
     y2 = run_conv(case, inp, "2k")
     assert np.array_equal(words_of(y, case.out_dtype), words_of(y2, case.out_dtype))
+
+
+FORCED = [(c, i % 8, (i // 8) % 6 - 1) for i, c in enumerate(_gemm_cases(48, seed=2026) + _conv_cases(48, seed=2027))]
+
+
+@pytest.mark.parametrize("case,tile,variant", FORCED,
+                         ids=lambda v: v.name if hasattr(v, "name") else str(v))
+def test_random_forced_config_vs_oracle(ba, case, tile, variant):
+    # every tile configuration and conv-halo variant in turn (a forced choice
+    # that does not apply to a problem falls back to one that does)
+    ba.force_tile_config(tile)
+    ba.force_halo_variant(variant)
+    try:
+        if isinstance(case, wl.GemmCase):
+            inp = wl.gen_gemm(case, seed=9)
+            ref, floor = gemm_reference(case, inp)
+            y = run_gemm(case, inp)
+        else:
+            inp = wl.gen_conv(case, seed=10)
+            ref, floor = conv_reference(case, inp)
+            y = run_conv(case, inp)
+        print(f"[{case.name} tile {tile} variant {variant}] {ba.last_tile_config()}", flush=True)
+    finally:
+        ba.force_tile_config(-1)
+        ba.force_halo_variant(-1)
+    _compare(y, ref, floor, case)
